@@ -1,0 +1,377 @@
+"""Float64 CPU oracle of one DiT block forward on a packed audio-video sequence.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline of the benchmark, never by the product path.
+
+Page titles cited below (abbreviated):
+  [RT-H3]  "Why Real-Time MiniMax H3 Serving Requires More Than a Faster DiT"
+  [OMNI]   "vLLM-Omni pushes MiniMax H3 video generation below playback time"
+  [FH3-zh] "MiniMax H3 通过 vLLM-Omni 实现 FastH3 实时推理"
+
+What the pages fix: attention over the packed audio-video sequence runs on each
+segment's valid length with structural suffix padding removed, and each rank
+touches only its own embedding/RoPE rows ([RT-H3] Key takeaways; [FH3-zh]
+vLLM-Omni 中的系统级优化); the block's Q/K RMSNorm with RoPE, modulation with
+normalisation, residual updates and SwiGLU are the operations that get fused
+(same sections); the DiT is a joint audio-video transformer ([OMNI] Who it
+affects); the student runs four forwards over five sigma positions ([FH3-zh]
+FastH3：四步学生模型).  Everything else -- norm kinds, epsilons, RoPE pair
+convention and section split, modulation slot order, absence of biases, the
+timestep embedding -- is a reading of silent pages (one plain choice each,
+named at each function).  Every step is computed in float64 on the values it is
+given; there is no blocking, fusion or intermediate rounding.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+
+POS_VIDEO, POS_AUDIO, POS_PAD = 0, 1, 2
+
+# modulation slots along axis 1 of the [rows, 6, C] modulation tensor
+SHIFT1, SCALE1, GATE1, SHIFT2, SCALE2, GATE2 = range(6)
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ O1 modnorm
+
+def modulated_norm(x, shift, scale, eps: float = 1e-6, kind: str = "layer") -> np.ndarray:
+    """adaLN-style modulated normalisation of each row of x.
+
+    kind="layer": n = (x - mean) / sqrt(var + eps), var the biased variance,
+    no affine of its own; kind="rms": n = x / sqrt(mean(x^2) + eps).
+    Returns n * (1 + scale) + shift.  The pages name modulation and
+    normalisation as one fused piece of work ([RT-H3] Key takeaways); the norm
+    kind and the (1 + scale) form are the plain adaLN reading.
+    """
+    x = _f64(x)
+    if kind == "layer":
+        mu = x.mean(axis=-1, keepdims=True)
+        var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+        n = (x - mu) / np.sqrt(var + eps)
+    elif kind == "rms":
+        n = x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    else:
+        raise ValueError(kind)
+    return n * (1.0 + _f64(scale)) + _f64(shift)
+
+
+def gated_residual(x, gate, y) -> np.ndarray:
+    """x + gate * y: the gated residual update named among the fused operations
+    ([RT-H3] Key takeaways)."""
+    return _f64(x) + _f64(gate) * _f64(y)
+
+
+# --------------------------------------------------------------- O2 projections
+
+def linear(x, w) -> np.ndarray:
+    """x @ w^T with w stored [out, in] and no bias."""
+    return _f64(x) @ _f64(w).T
+
+
+# ---------------------------------------------------------- O3 Q/K RMSNorm
+
+def rms_norm_heads(t, gain, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm over the last axis (one head's D values), times a gain [D] shared
+    by all heads ([RT-H3] Key takeaways: Q/K RMSNorm)."""
+    t = _f64(t)
+    return t / np.sqrt((t * t).mean(axis=-1, keepdims=True) + eps) * _f64(gain)
+
+
+# ------------------------------------------------------------------ O4 RoPE
+
+def rope_angles(pos, head_dim: int, sections: Sequence[int], theta: float) -> np.ndarray:
+    """Rotation angle of every adjacent pair (2j, 2j+1) of a head row, per token.
+
+    Video tokens (kind 0): the head row is cut into contiguous sections of
+    widths (d_t, d_h, d_w); in a section of width d at position p, pair j
+    (j < d/2) turns by p * theta**(-2j/d).  Audio tokens (kind 1): one section
+    of width D at the audio index.  Pad tokens (kind 2): angle 0.
+    Returns float64 [n, D/2].  ([RT-H3] Key takeaways: RoPE rows.)
+    """
+    pos = np.asarray(pos)
+    n = pos.shape[0]
+    half = head_dim // 2
+    ang = np.zeros((n, half), dtype=np.float64)
+    kind = pos[:, 0]
+    vid = kind == POS_VIDEO
+    aud = kind == POS_AUDIO
+    pair = 0
+    for axis, d in enumerate(sections):
+        j = np.arange(d // 2, dtype=np.float64)
+        freq = theta ** (-2.0 * j / d)
+        p = pos[:, 1 + axis].astype(np.float64)
+        ang[vid, pair:pair + d // 2] = p[vid, None] * freq[None, :]
+        pair += d // 2
+    j = np.arange(half, dtype=np.float64)
+    freq = theta ** (-2.0 * j / head_dim)
+    ang[aud, :] = pos[aud, 1].astype(np.float64)[:, None] * freq[None, :]
+    return ang
+
+
+def apply_rope(t, ang) -> np.ndarray:
+    """Rotate each adjacent pair (a, b) of t[n, H, D] by ang[n, D/2]:
+    (a, b) -> (a cos - b sin, a sin + b cos)."""
+    t = _f64(t)
+    a = t[..., 0::2]
+    b = t[..., 1::2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    out = np.empty_like(t)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def qk_norm_rope(q, k, pos, g_q, g_k, sections, theta: float = 10000.0, eps: float = 1e-6):
+    """Q/K RMSNorm per head followed by RoPE, on q, k [n, H, D].
+
+    Pad rows (kind 2) are returned unchanged.  ([RT-H3] Key takeaways: Q/K
+    RMSNorm with RoPE fused; rank-local RoPE rows.)
+    """
+    q = _f64(q)
+    k = _f64(k)
+    pos = np.asarray(pos)
+    d = q.shape[-1]
+    ang = rope_angles(pos, d, sections, theta)
+    live = pos[:, 0] != POS_PAD
+    qo = q.copy()
+    ko = k.copy()
+    qo[live] = apply_rope(rms_norm_heads(q[live], g_q, eps), ang[live])
+    ko[live] = apply_rope(rms_norm_heads(k[live], g_k, eps), ang[live])
+    return qo, ko
+
+
+# ------------------------------------------------------------- O5 attention
+
+def attention_dense(q, k, v, scale: float) -> np.ndarray:
+    """softmax(q k^T * scale) v for one segment and head; q [m, D], k, v [n, D].
+
+    Written with the row maximum subtracted before exponentiation.
+    """
+    s = _f64(q) @ _f64(k).T * scale
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=-1, keepdims=True)
+    return p @ _f64(v)
+
+
+def varlen_attention(q, k, v, cu_slots, valid_len, scale: Optional[float] = None,
+                     q_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Attention over a packed buffer of segments, valid rows only.
+
+    Segment s owns slot rows [cu_slots[s], cu_slots[s+1]); its first
+    valid_len[s] rows are valid.  A valid row attends, bidirectionally, to the
+    valid rows of its own segment only; every other row's output is 0.
+    ([RT-H3] Key takeaways: valid sequence lengths, structural suffix padding
+    removed.)  q, k, v are [n_buf, H, D]; scale defaults to 1/sqrt(D).
+
+    q_rows: if given, q holds only those buffer rows (in that order) and the
+    result has q's shape; keys and values are always the whole buffer.
+    """
+    k = np.asarray(k)
+    v = np.asarray(v)
+    n_buf, h, d = k.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(n_buf) if q_rows is None else np.asarray(q_rows)
+    q = np.asarray(q)
+    out = np.zeros((len(rows), h, d), dtype=np.float64)
+    cu = np.asarray(cu_slots)
+    vl = np.asarray(valid_len) if valid_len is not None else np.diff(cu)
+    for s in range(len(cu) - 1):
+        lo = int(cu[s])
+        hi = lo + int(vl[s])
+        if hi <= lo:
+            continue
+        sel = np.nonzero((rows >= lo) & (rows < hi))[0]
+        if sel.size == 0:
+            continue
+        for head in range(h):
+            out[sel, head] = attention_dense(q[sel, head], k[lo:hi, head], v[lo:hi, head], scale)
+    return out
+
+
+# ---------------------------------------------------------------- O8 SwiGLU
+
+def silu(a) -> np.ndarray:
+    a = _f64(a)
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu_gate(a, b) -> np.ndarray:
+    """silu(a) * b, a from the W1 branch, b from the W3 branch."""
+    return silu(a) * _f64(b)
+
+
+def swiglu_mlp(h, w1, w3, w2) -> np.ndarray:
+    """(silu(h W1^T) * (h W3^T)) W2^T ([RT-H3] Key takeaways: SwiGLU)."""
+    return linear(swiglu_gate(linear(h, w1), linear(h, w3)), w2)
+
+
+# ----------------------------------------------------------- whole block
+
+@dataclasses.dataclass
+class BlockShape:
+    dim: int
+    n_heads: int
+    head_dim: int
+    ffn_dim: int
+    sections: tuple
+    theta: float = 10000.0
+    eps_qk: float = 1e-6
+    eps_mod: float = 1e-6
+    norm_kind: str = "layer"
+    # rank-share description (world 1: tok_begin 0, head_begin 0, head_count = n_heads)
+    tok_begin: int = 0
+    head_begin: int = 0
+    head_count: Optional[int] = None
+
+    @staticmethod
+    def of(wl) -> "BlockShape":
+        return BlockShape(dim=wl.dim, n_heads=wl.n_heads, head_dim=wl.head_dim, ffn_dim=wl.ffn_dim,
+                          sections=tuple(wl.sections), theta=wl.theta, eps_qk=wl.eps_qk,
+                          eps_mod=wl.eps_mod, tok_begin=wl.tok_begin if wl.share_mode else 0,
+                          head_begin=wl.head_begin if wl.share_mode else 0,
+                          head_count=wl.head_count if wl.share_mode else wl.n_heads)
+
+
+def _mod_rows(mod, rows):
+    mod = np.asarray(mod)
+    if mod.shape[0] == 1:
+        return _f64(mod[0])[None]            # broadcast [1, 6, C]
+    return _f64(mod[rows])
+
+
+def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
+              qkv_attn_fill=None, o_local_fill=None, rows: Optional[np.ndarray] = None,
+              intermediates: bool = False):
+    """One DiT block forward on this GPU's token rows x [n, C].
+
+    Steps: h1 = modnorm(x; shift1, scale1) -> qkv = h1 Wqkv^T -> Q/K RMSNorm +
+    RoPE -> varlen attention -> y1 = o Wo^T -> x1 = x + gate1 * y1 ->
+    h2 = modnorm(x1; shift2, scale2) -> x2 = x1 + gate2 * SwiGLU(h2).
+
+    World 1 (qkv_attn_fill is None): attention runs over the n local rows with
+    all heads, segments given by cu_slots/valid_len over those rows.
+    Rank share: the attention buffer is qkv_attn_fill [N, 3, hc, D] (rows of
+    other ranks, as the sequence-parallel exchange would deliver them) with
+    rows [tok_begin, tok_begin + n) replaced by this rank's own q, k, v of heads
+    [head_begin, head_begin + hc); the attention output for those rows fills
+    heads [head_begin, head_begin + hc) of o_local_fill [n, H, D], whose other
+    heads stand for what the reverse exchange would deliver.
+    ([RT-H3] Key takeaways: rank-local rows, all-to-all around attention;
+    [FH3-zh] FastH3 推理配置: sequence-parallel degree 8.)
+
+    rows: return only these local rows (keys/values still use every row).
+    Returns x2 [len(rows), C], or a dict of every intermediate if asked.
+    """
+    sh = shape
+    x = np.asarray(x)
+    n = x.shape[0]
+    H, D, C = sh.n_heads, sh.head_dim, sh.dim
+    hc = sh.head_count or H
+    hb, tb = sh.head_begin, sh.tok_begin
+    out_rows = np.arange(n) if rows is None else np.asarray(rows)
+
+    # keys and values need every local row; queries and everything after need only out_rows
+    all_rows = np.arange(n)
+    mod_all = _mod_rows(mod, all_rows)
+    h1 = modulated_norm(x, mod_all[:, SHIFT1], mod_all[:, SCALE1], sh.eps_mod, sh.norm_kind)
+    wq = _f64(w.w_qkv).reshape(3, H, D, C)
+    share = qkv_attn_fill is not None
+    heads = slice(hb, hb + hc) if share else slice(0, H)
+    wk = wq[1, heads].reshape(-1, C)
+    wv = wq[2, heads].reshape(-1, C)
+    k_loc = linear(h1, wk).reshape(n, -1, D)
+    v_loc = linear(h1, wv).reshape(n, -1, D)
+    h1r = h1[out_rows]
+    q_loc = linear(h1r, wq[0, heads].reshape(-1, C)).reshape(len(out_rows), -1, D)
+    pos = np.asarray(pos)
+    # norm + RoPE on the local rows (q only on out_rows)
+    kq_dummy = np.zeros_like(k_loc)
+    _, k_loc = qk_norm_rope(kq_dummy, k_loc, pos, w.g_q, w.g_k, sh.sections, sh.theta, sh.eps_qk)
+    q_loc, _ = qk_norm_rope(q_loc, np.zeros_like(q_loc), pos[out_rows], w.g_q, w.g_k,
+                            sh.sections, sh.theta, sh.eps_qk)
+    if share:
+        buf = _f64(qkv_attn_fill).copy()
+        buf[tb:tb + n, 1] = k_loc
+        buf[tb:tb + n, 2] = v_loc
+        kbuf, vbuf = buf[:, 1], buf[:, 2]
+        qrows = out_rows + tb
+    else:
+        kbuf, vbuf = k_loc, v_loc
+        qrows = out_rows
+    o_h = varlen_attention(q_loc, kbuf, vbuf, cu_slots, valid_len, q_rows=qrows)
+    if share:
+        o = _f64(o_local_fill)[out_rows].copy()
+        o[:, hb:hb + hc] = o_h
+    else:
+        o = o_h
+    y1 = linear(o.reshape(len(out_rows), H * D), w.w_o)
+    mod_r = _mod_rows(mod, out_rows)
+    xr = _f64(x[out_rows])
+    x1 = gated_residual(xr, mod_r[:, GATE1], y1)
+    h2 = modulated_norm(x1, mod_r[:, SHIFT2], mod_r[:, SCALE2], sh.eps_mod, sh.norm_kind)
+    a = linear(h2, w.w1)
+    b = linear(h2, w.w3)
+    g = swiglu_gate(a, b)
+    y2 = linear(g, w.w2)
+    x2 = gated_residual(x1, mod_r[:, GATE2], y2)
+    if not intermediates:
+        return x2
+    return dict(h1=h1r, q=q_loc, k=k_loc[out_rows], v=v_loc[out_rows], o=o.reshape(len(out_rows), H, D),
+                o_heads=o_h, y1=y1, x1=x1, h2=h2, g=g, y2=y2, x2=x2)
+
+
+# -------------------------------------------------- O9 four-forward student loop
+
+def timestep_embedding(sigma: float, dim: int = 256, max_period: float = 10000.0,
+                       sigma_scale: float = 1000.0) -> np.ndarray:
+    """Sinusoidal embedding [cos(s w_j) || sin(s w_j)], s = 1000 sigma,
+    w_j = max_period**(-j/(dim/2)), j < dim/2.  The pages give none; this is
+    the common diffusion-transformer form."""
+    half = dim // 2
+    j = np.arange(half, dtype=np.float64)
+    om = max_period ** (-j / half)
+    a = sigma_scale * float(sigma) * om
+    return np.concatenate([np.cos(a), np.sin(a)])
+
+
+def timestep_modulation(sigma: float, tw) -> np.ndarray:
+    """Per-block modulation [n_blocks, 6, C] at noise level sigma:
+    W_t2 silu(W_t1 e(sigma)) reshaped [6, C], plus each block's table."""
+    e = timestep_embedding(sigma, _f64(tw.w_t1).shape[1])
+    hid = silu(_f64(tw.w_t1) @ e)
+    tvec = (_f64(tw.w_t2) @ hid).reshape(6, -1)
+    return tvec[None] + _f64(tw.table)
+
+
+def euler_update(z, u, sigma_from: float, sigma_to: float) -> np.ndarray:
+    """z + (sigma_to - sigma_from) * u."""
+    return _f64(z) + (float(sigma_to) - float(sigma_from)) * _f64(u)
+
+
+def student_loop(z, blocks_w, tw, pos, cu_slots, valid_len, shape: BlockShape, sigmas,
+                 qkv_attn_fill=None, o_local_fill=None):
+    """Four forwards over five sigma positions ([FH3-zh] FastH3：四步学生模型).
+
+    For k = 0..len(sigmas)-2: every block b takes its modulation from
+    timestep_modulation(sigma_k)[b] (broadcast over rows); u is the stack's
+    output on z; then z <- z + (sigma_{k+1} - sigma_k) u.  In rank-share mode
+    every block sees the same fill buffers for the other ranks' rows.
+    """
+    z = _f64(z)
+    for k in range(len(sigmas) - 1):
+        mods = timestep_modulation(sigmas[k], tw)
+        u = z
+        for b, w in enumerate(blocks_w):
+            u = dit_block(u, mods[b][None], w, pos, cu_slots, valid_len, shape,
+                          qkv_attn_fill, o_local_fill)
+        z = euler_update(z, u, sigmas[k], sigmas[k + 1])
+    return z

@@ -1,0 +1,595 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+No test here re-types the oracle's own formula: each checks a closed form, an
+invariant, a special case that reduces to a library routine (torch CPU in
+float64), a hand-derived fixture, or brute force on tiny inputs.
+"""
+import hashlib
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def t64(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+# ----------------------------------------------------------------- inputs (O0)
+
+def test_bf16_rounding_ties_to_even():
+    a = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8) * 4,
+                  2 ** -133, np.inf, -np.inf], dtype=np.float32)
+    want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0, -4.0, 2 ** -133, np.inf, -np.inf], dtype=np.float32)
+    got = W.round_to_bf16(a)
+    assert np.array_equal(got, want)
+    assert np.isnan(W.round_to_bf16(np.array([np.nan], np.float32)))[0]
+    # agrees with torch's own float32 -> bfloat16 conversion (round to nearest even)
+    x = rng.standard_normal(100000).astype(np.float32) * 7
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(W.round_to_bf16(x), ref)
+
+
+def test_seeded_draws_are_byte_identical():
+    a = W.normal(0, "x", (3000, 5000), threads=1)
+    b = W.normal(0, "x", (3000, 5000), threads=8)
+    c = W.normal(1, "x", (3000, 5000))
+    assert hashlib.sha256(a.tobytes()).digest() == hashlib.sha256(b.tobytes()).digest()
+    assert not np.array_equal(a, c)
+    assert abs(a.mean()) < 1e-2 and abs(a.std() - 1) < 1e-2
+
+
+def test_positions_layout():
+    wl = W.TINY
+    pos = W.positions(wl)
+    assert pos.shape == (480, 4)
+    assert (pos[:384, 0] == 0).all() and (pos[384:, 0] == 1).all()
+    # t slowest, then h, then w
+    assert tuple(pos[0, 1:]) == (0, 0, 0) and tuple(pos[1, 1:]) == (0, 0, 1)
+    assert tuple(pos[12, 1:]) == (0, 1, 0) and tuple(pos[96, 1:]) == (1, 0, 0)
+    assert tuple(pos[383, 1:]) == (3, 7, 11)
+    assert (pos[384:, 1] == np.arange(96)).all()
+    w10 = W.SHARE_10S
+    assert w10.n_valid == 246206 and w10.n_pad_total == 246208 and w10.n_loc == 30776
+    p10 = W.positions(w10)
+    assert (p10[-2:, 0] == W.POS_PAD).all() and p10[245952, 0] == W.POS_AUDIO
+
+
+def test_varlen_case_layout():
+    c = W.varlen_case(seed=0, n_heads=2, head_dim=8)
+    assert c.cu_slots[0] == 0 and c.cu_slots[-1] == 8192
+    slots = np.diff(c.cu_slots)
+    assert (slots >= c.valid_len).all()
+    assert c.valid_len.tolist() == [4032, 1500, 17]
+
+
+# ------------------------------------------------------------------- O1 modnorm
+
+def test_modnorm_closed_form_moments():
+    x = rng.standard_normal((64, 256)) * 3 + 1.5
+    eps = 1e-6
+    z = np.zeros_like(x)
+    n = O.modulated_norm(x, z, z, eps)
+    var = x.var(axis=1)
+    assert np.allclose(n.mean(axis=1), 0, atol=1e-12)
+    assert np.allclose((n ** 2).mean(axis=1), var / (var + eps), rtol=1e-12)
+
+
+def test_modnorm_matches_library_layer_norm():
+    x = rng.standard_normal((32, 96))
+    z = np.zeros_like(x)
+    got = O.modulated_norm(x, z, z, 1e-6)
+    ref = F.layer_norm(t64(x), (96,), eps=1e-6).numpy()
+    assert np.allclose(got, ref, atol=1e-12)
+    got = O.modulated_norm(x, z, z, 1e-6, kind="rms")
+    ref = F.rms_norm(t64(x), (96,), eps=1e-6).numpy()
+    assert np.allclose(got, ref, atol=1e-12)
+
+
+def test_modnorm_modulation_special_cases():
+    x = rng.standard_normal((16, 40))
+    shift = rng.standard_normal((16, 40))
+    # scale = -1 removes the normalised term entirely: output is shift
+    assert np.allclose(O.modulated_norm(x, shift, -np.ones_like(x)), shift, atol=1e-14)
+    # scale = c with no shift scales the plain norm by (1 + c)
+    c = 0.37
+    base = F.layer_norm(t64(x), (40,), eps=1e-6).numpy()
+    assert np.allclose(O.modulated_norm(x, 0 * x, c + 0 * x), (1 + c) * base, atol=1e-12)
+    # shift adds after scaling
+    assert np.allclose(O.modulated_norm(x, shift, 0 * x) - base, shift, atol=1e-12)
+    # constant rows normalise to 0 (var 0, eps keeps it finite)
+    assert np.allclose(O.modulated_norm(np.full((2, 8), 5.0), np.zeros((2, 8)), np.zeros((2, 8))), 0)
+
+
+def test_gated_residual_zero_gate_is_identity():
+    x = rng.standard_normal((8, 16))
+    y = rng.standard_normal((8, 16))
+    assert np.array_equal(O.gated_residual(x, np.zeros_like(x), y), x)
+    g = rng.standard_normal((8, 16))
+    # linear in the gate
+    d1 = O.gated_residual(x, g, y) - x
+    d2 = O.gated_residual(x, 2 * g, y) - x
+    assert np.allclose(d2, 2 * d1)
+
+
+# ------------------------------------------------------------- O3 Q/K RMSNorm
+
+def test_qk_rmsnorm_unit_rms_before_gain():
+    q = rng.standard_normal((50, 4, 64)) * 2.5
+    g = 1 + 0.02 * rng.standard_normal(64)
+    eps = 1e-6
+    out = O.rms_norm_heads(q, g, eps)
+    ms = (q ** 2).mean(axis=-1)
+    assert np.allclose(((out / g) ** 2).mean(axis=-1), ms / (ms + eps), rtol=1e-12)
+    ref = F.rms_norm(t64(q), (64,), weight=t64(g), eps=eps).numpy()
+    assert np.allclose(out, ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------- O4 RoPE
+
+def _golden_rope():
+    with open(os.path.join(GOLDEN, "rope_closed_form.json")) as f:
+        return json.load(f)
+
+
+def test_rope_hand_derived_angles():
+    g = _golden_rope()
+    d, secs, theta = g["head_dim"], tuple(g["sections"]), g["theta"]
+    for case in g["cases"]:
+        pos = np.array([case["pos"]], dtype=np.int32)
+        ang = O.rope_angles(pos, d, secs, theta)[0]
+        if case["angles"] is None:
+            assert np.all(ang == 0)
+            continue
+        assert np.allclose(ang, case["angles"], rtol=1e-13, atol=1e-15), case["note"]
+        # rotating the unit vector e0 of each pair yields (cos, sin) of that angle,
+        # and e1 yields (-sin, cos)
+        for unit, want in (((1.0, 0.0), lambda a: (math.cos(a), math.sin(a))),
+                           ((0.0, 1.0), lambda a: (-math.sin(a), math.cos(a)))):
+            x = np.tile(np.array(unit), d // 2).reshape(1, 1, d)
+            y = O.apply_rope(x, ang[None])[0, 0]
+            for j, a in enumerate(case["angles"]):
+                assert np.allclose(y[2 * j:2 * j + 2], want(a), atol=1e-14)
+
+
+def test_rope_matches_complex_rotation():
+    # pairs as complex numbers a + ib, multiplied by e^{i phi}
+    pos = W.positions(W.TINY)
+    x = rng.standard_normal((480, 4, 64))
+    ang = O.rope_angles(pos, 64, (16, 24, 24), 1e4)
+    got = O.apply_rope(x, ang)
+    z = torch.complex(t64(x[..., 0::2]), t64(x[..., 1::2])) * torch.polar(
+        torch.ones_like(t64(ang)), t64(ang))[:, None, :]
+    ref = np.stack([z.real.numpy(), z.imag.numpy()], axis=-1).reshape(x.shape)
+    assert np.allclose(got, ref, atol=1e-12)
+
+
+def test_rope_preserves_norm_and_composes():
+    d, secs = 128, (32, 48, 48)
+    x = rng.standard_normal((20, 3, d))
+    p1 = np.zeros((20, 4), np.int32)
+    p1[:, 1:] = rng.integers(0, 300, (20, 3))
+    p1[10:, 0] = W.POS_AUDIO
+    p2 = p1.copy()
+    p2[:, 1:] = rng.integers(0, 300, (20, 3))
+    a1 = O.rope_angles(p1, d, secs, 1e4)
+    a2 = O.rope_angles(p2, d, secs, 1e4)
+    p12 = p1.copy()
+    p12[:, 1:] = p1[:, 1:] + p2[:, 1:]
+    a12 = O.rope_angles(p12, d, secs, 1e4)
+    y = O.apply_rope(x, a1)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    assert np.allclose(O.apply_rope(y, a2), O.apply_rope(x, a12), atol=1e-10)
+    zero = np.zeros((20, 4), np.int32)
+    zero[10:, 0] = W.POS_AUDIO
+    assert np.array_equal(O.apply_rope(x, O.rope_angles(zero, d, secs, 1e4)), x)
+
+
+@pytest.mark.parametrize("axis", [1, 2, 3])
+def test_rope_scores_depend_only_on_relative_position(axis):
+    d, secs = 128, (32, 48, 48)
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, 1, d))
+    kind = W.POS_VIDEO if axis else W.POS_AUDIO
+
+    def score(pq, pk):
+        a = np.zeros((1, 4), np.int32)
+        b = np.zeros((1, 4), np.int32)
+        a[0, 0] = b[0, 0] = kind
+        a[0, axis], b[0, axis] = pq, pk
+        rq = O.apply_rope(q, O.rope_angles(a, d, secs, 1e4))
+        rk = O.apply_rope(k, O.rope_angles(b, d, secs, 1e4))
+        return float((rq * rk).sum())
+
+    s0 = score(3, 10)
+    assert abs(score(3 + 57, 10 + 57) - s0) < 1e-10
+    assert abs(score(0, 7) - s0) < 1e-10
+    assert abs(score(10, 3) - s0) > 1e-6  # not symmetric: direction matters
+
+
+def test_rope_audio_uses_full_width_single_section():
+    d, secs = 128, (32, 48, 48)
+    pos = np.array([[W.POS_AUDIO, 37, 5, 9]], np.int32)
+    ang = O.rope_angles(pos, d, secs, 1e4)[0]
+    # the h and w columns are ignored for audio; pair j turns by 37 * 1e4^(-2j/128)
+    assert np.allclose(ang[0], 37) and np.allclose(ang[-1], 37 * 1e4 ** (-126 / 128))
+    assert np.allclose(np.diff(np.log(ang)), -2 / 128 * math.log(1e4))
+
+
+def test_qk_norm_rope_pad_rows_untouched():
+    pos = W.positions(W.TINY.replace(pad_to=512))
+    q = rng.standard_normal((512, 4, 64))
+    k = rng.standard_normal((512, 4, 64))
+    g = np.ones(64)
+    qo, ko = O.qk_norm_rope(q, k, pos, g, g, (16, 24, 24))
+    assert np.array_equal(qo[480:], q[480:]) and np.array_equal(ko[480:], k[480:])
+    assert np.allclose(np.sqrt((qo[:480] ** 2).mean(-1)), 1, atol=1e-5)
+
+
+# ------------------------------------------------------------ O5 attention
+
+def _brute_attention(q, k, v, cu, vl, scale):
+    n, h, d = q.shape
+    out = [[[0.0] * d for _ in range(h)] for _ in range(n)]
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s]) + int(vl[s])
+        for i in range(lo, hi):
+            for hh in range(h):
+                sc = []
+                for j in range(lo, hi):
+                    sc.append(sum(float(q[i, hh, c]) * float(k[j, hh, c]) for c in range(d)) * scale)
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                z = sum(e)
+                for c in range(d):
+                    out[i][hh][c] = sum(e[j - lo] / z * float(v[j, hh, c]) for j in range(lo, hi))
+    return np.array(out)
+
+
+def test_attention_brute_force_tiny():
+    cu = np.array([0, 7, 12, 13, 16], np.int32)
+    vl = np.array([5, 5, 0, 2], np.int32)
+    q, k, v = (rng.standard_normal((16, 2, 4)) for _ in range(3))
+    got = O.varlen_attention(q, k, v, cu, vl)
+    ref = _brute_attention(q, k, v, cu, vl, 0.5)
+    assert np.allclose(got, ref, atol=1e-13)
+
+
+def test_attention_matches_library_sdpa_per_segment():
+    c = W.varlen_case(seed=3, lengths=(300, 77, 1), n_buf=512, n_heads=3, head_dim=64, dtype="f32")
+    got = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    for s in range(3):
+        lo = c.cu_slots[s]
+        hi = lo + c.valid_len[s]
+        ref = F.scaled_dot_product_attention(t64(c.q[lo:hi]).transpose(0, 1), t64(c.k[lo:hi]).transpose(0, 1),
+                                             t64(c.v[lo:hi]).transpose(0, 1)).transpose(0, 1).numpy()
+        assert np.allclose(got[lo:hi], ref, atol=1e-12)
+        assert np.all(got[hi:c.cu_slots[s + 1]] == 0)
+
+
+def test_attention_special_cases():
+    d = 16
+    # single-row segment returns its own v
+    q, k, v = (rng.standard_normal((4, 1, d)) for _ in range(3))
+    o = O.varlen_attention(q, k, v, np.array([0, 1, 4]), np.array([1, 3]))
+    assert np.allclose(o[0], v[0])
+    # identical keys: uniform weights, output = mean of the valid values
+    kk = np.tile(rng.standard_normal((1, 1, d)), (10, 1, 1))
+    vv = rng.standard_normal((10, 1, d))
+    o = O.varlen_attention(rng.standard_normal((10, 1, d)), kk, vv, np.array([0, 10]), np.array([6]))
+    assert np.allclose(o[:6], vv[:6].mean(axis=0, keepdims=True))
+    assert np.all(o[6:] == 0)
+    # two keys, closed form: weights e^{a}/(e^a+e^b)
+    qq = np.array([[[1.0, 0.0]]])
+    k2 = np.array([[[2.0, 0.0]], [[0.0, 5.0]]])
+    v2 = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    o = O.varlen_attention(qq.repeat(2, 0), k2, v2, np.array([0, 2]), np.array([2]), scale=1.0)
+    w0 = math.exp(2) / (math.exp(2) + 1)
+    assert np.allclose(o[0, 0], [w0, 1 - w0], atol=1e-15)
+
+
+def test_attention_packed_equals_each_segment_alone_and_pads_poisoned():
+    c = W.varlen_case(seed=5, lengths=(200, 45, 1, 17), n_buf=400, n_heads=2, head_dim=32,
+                      dtype="f32", pad_fill="nan")
+    got = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    for s in range(4):
+        lo = c.cu_slots[s]
+        hi = lo + c.valid_len[s]
+        alone = O.varlen_attention(c.q[lo:hi], c.k[lo:hi], c.v[lo:hi], np.array([0, hi - lo]),
+                                   np.array([hi - lo]))
+        assert np.array_equal(got[lo:hi], alone)
+    assert np.isfinite(got).all()
+
+
+def test_attention_permutation_equivariance():
+    q, k, v = (rng.standard_normal((50, 2, 8)) for _ in range(3))
+    perm = rng.permutation(50)
+    cu, vl = np.array([0, 50]), np.array([50])
+    a = O.varlen_attention(q, k, v, cu, vl)
+    b = O.varlen_attention(q[perm], k[perm], v[perm], cu, vl)
+    assert np.allclose(a[perm], b, atol=1e-13)
+
+
+def test_attention_invariant_to_shifting_all_positions_of_a_segment():
+    wl = W.TINY
+    pos = W.positions(wl)
+    q, k, v = (rng.standard_normal((480, 4, 64)) for _ in range(3))
+    g = 1 + 0.02 * rng.standard_normal(64)
+    cu, vl = np.array([0, 480]), np.array([480])
+    q1, k1 = O.qk_norm_rope(q, k, pos, g, g, wl.sections)
+    shifted = pos.copy()
+    shifted[:, 1:] += np.array([5, 3, 11])            # video t/h/w shift, audio index shift by 5
+    q2, k2 = O.qk_norm_rope(q, k, shifted, g, g, wl.sections)
+    # video and audio tokens sit in one segment; a shift that is the same for
+    # every token of each kind keeps scores within each kind, not across kinds,
+    # so compare per-kind segments
+    segs = (np.array([0, 384]), np.array([384]))
+    a = O.varlen_attention(q1[:384], k1[:384], v[:384], *segs)
+    b = O.varlen_attention(q2[:384], k2[:384], v[:384], *segs)
+    assert np.allclose(a, b, atol=1e-10)
+    a = O.varlen_attention(q1[384:], k1[384:], v[384:], np.array([0, 96]), np.array([96]))
+    b = O.varlen_attention(q2[384:], k2[384:], v[384:], np.array([0, 96]), np.array([96]))
+    assert np.allclose(a, b, atol=1e-10)
+
+
+# ------------------------------------------------------- O2 / O6 / O8 GEMMs, SwiGLU
+
+def test_linear_brute_force_and_identity():
+    x = rng.standard_normal((3, 5))
+    w = rng.standard_normal((4, 5))
+    got = O.linear(x, w)
+    for i in range(3):
+        for o in range(4):
+            assert abs(got[i, o] - sum(x[i, c] * w[o, c] for c in range(5))) < 1e-13
+    assert np.array_equal(O.linear(x, np.eye(5)), x)
+
+
+def test_silu_and_swiglu():
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(40.0) - 40.0) < 1e-12 and abs(O.silu(-40.0)) < 1e-15
+    a = rng.standard_normal((6, 7)) * 3
+    assert np.allclose(O.silu(a), F.silu(t64(a)).numpy(), atol=1e-14)
+    h = rng.standard_normal((5, 16))
+    w1, w3 = rng.standard_normal((24, 16)), rng.standard_normal((24, 16))
+    w2 = rng.standard_normal((16, 24))
+    ref = (F.silu(t64(h) @ t64(w1).T) * (t64(h) @ t64(w3).T)) @ t64(w2).T
+    assert np.allclose(O.swiglu_mlp(h, w1, w3, w2), ref.numpy(), atol=1e-10)
+    # W3 = 0 turns the branch off
+    assert np.all(O.swiglu_mlp(h, w1, 0 * w3, w2) == 0)
+
+
+# ------------------------------------------------------------------ whole block
+
+def _tiny(dtype="f32", seed=0, wl=W.TINY):
+    w = W.block_weights(wl, seed, dtype)
+    bi = W.block_inputs(wl, seed, dtype)
+    return wl, w, bi
+
+
+def test_block_zero_gates_and_zero_outputs_are_identity():
+    wl, w, bi = _tiny()
+    sh = O.BlockShape.of(wl)
+    mod = bi.mod.copy()
+    mod[:, O.GATE1] = 0
+    mod[:, O.GATE2] = 0
+    out = O.dit_block(bi.x, mod, w, bi.pos, bi.cu_slots, bi.valid_len, sh)
+    assert np.array_equal(out, bi.x.astype(np.float64))
+    import dataclasses
+    w0 = dataclasses.replace(w, w_o=0 * w.w_o, w2=0 * w.w2)
+    out = O.dit_block(bi.x, bi.mod, w0, bi.pos, bi.cu_slots, bi.valid_len, sh)
+    assert np.array_equal(out, bi.x.astype(np.float64))
+
+
+def test_block_slot_roles():
+    import dataclasses
+    wl, w, bi = _tiny()
+    sh = O.BlockShape.of(wl)
+    w_mlp_off = dataclasses.replace(w, w2=0 * w.w2)
+    x = bi.x.astype(np.float64)
+    # with the MLP off, the update is gate1 * y1 and is linear in gate1 only
+    base = O.dit_block(bi.x, bi.mod, w_mlp_off, bi.pos, bi.cu_slots, bi.valid_len, sh) - x
+    m2 = bi.mod.copy()
+    m2[:, O.GATE1] *= 2
+    assert np.allclose(O.dit_block(bi.x, m2, w_mlp_off, bi.pos, bi.cu_slots, bi.valid_len, sh) - x, 2 * base)
+    m3 = bi.mod.copy()
+    m3[:, O.SHIFT2:] = rng.standard_normal(m3[:, O.SHIFT2:].shape)
+    assert np.allclose(O.dit_block(bi.x, m3, w_mlp_off, bi.pos, bi.cu_slots, bi.valid_len, sh) - x, base)
+    # scale1 = -1 makes the first norm output shift1: the attention branch no
+    # longer sees x, so the update is the same for two different x
+    m4 = bi.mod.copy()
+    m4[:, O.SCALE1] = -1
+    x_other = rng.standard_normal(x.shape)
+    d1 = O.dit_block(bi.x, m4, w_mlp_off, bi.pos, bi.cu_slots, bi.valid_len, sh) - x
+    d2 = O.dit_block(x_other, m4, w_mlp_off, bi.pos, bi.cu_slots, bi.valid_len, sh) - x_other
+    assert np.allclose(d1, d2, atol=1e-12)
+
+
+def test_block_padding_invariance_with_poisoned_pad_rows():
+    wl, w, bi = _tiny()
+    wlp = wl.replace(pad_to=512)
+    bip = W.block_inputs(wlp, 0, "f32")
+    x = np.full((512, wl.dim), np.nan, np.float32)
+    x[:480] = bi.x
+    x[480::2] = np.inf
+    mod = np.full((512, 6, wl.dim), np.nan, np.float32)
+    mod[:480] = bi.mod
+    sh = O.BlockShape.of(wl)
+    a = O.dit_block(bi.x, bi.mod, w, bi.pos, bi.cu_slots, bi.valid_len, sh)
+    b = O.dit_block(x, mod, w, bip.pos, bip.cu_slots, bip.valid_len, sh)
+    assert np.array_equal(a, b[:480])
+
+
+def test_block_rank_share_matches_world_one():
+    """A rank's share, fed what the other ranks would send, equals the world-1
+    block on those rows (sequence parallel over tokens, head-parallel attention)."""
+    wl, w, bi = _tiny()
+    sh1 = O.BlockShape.of(wl)
+    full = O.dit_block(bi.x, bi.mod, w, bi.pos, bi.cu_slots, bi.valid_len, sh1, intermediates=True)
+    P = 4
+    for rank in (1, 3):
+        wr = wl.replace(sp_degree=P, rank=rank)
+        n = wr.n_loc
+        tb, hb, hc = wr.tok_begin, wr.head_begin, wr.head_count
+        # what the exchange delivers: every rank's post-norm/RoPE q, k, v of heads [hb, hb+hc)
+        qkv_fill = np.stack([full["q"][:, hb:hb + hc], full["k"][:, hb:hb + hc], full["v"][:, hb:hb + hc]], 1)
+        o_fill = full["o"][tb:tb + n].copy()
+        qkv_fill[tb:tb + n] = 1e30   # local rows must be overwritten by the rank's own values
+        o_fill[:, hb:hb + hc] = 1e30
+        shr = O.BlockShape.of(wr)
+        got = O.dit_block(bi.x[tb:tb + n], bi.mod[tb:tb + n], w, bi.pos[tb:tb + n], bi.cu_slots,
+                          bi.valid_len, shr, qkv_attn_fill=qkv_fill, o_local_fill=o_fill)
+        assert np.allclose(got, full["x2"][tb:tb + n], atol=1e-12)
+
+
+def test_block_sampled_rows_equal_full():
+    wl, w, bi = _tiny()
+    sh = O.BlockShape.of(wl)
+    full = O.dit_block(bi.x, bi.mod, w, bi.pos, bi.cu_slots, bi.valid_len, sh)
+    rows = np.array([0, 5, 383, 384, 479])
+    part = O.dit_block(bi.x, bi.mod, w, bi.pos, bi.cu_slots, bi.valid_len, sh, rows=rows)
+    assert np.allclose(part, full[rows], atol=1e-13)
+
+
+# ------------------------------------------------------------- O9 student loop
+
+def test_timestep_embedding_closed_form():
+    e0 = O.timestep_embedding(0.0)
+    assert np.array_equal(e0, np.concatenate([np.ones(128), np.zeros(128)]))
+    e = O.timestep_embedding(0.75)
+    assert np.allclose(e[:128] ** 2 + e[128:] ** 2, 1)
+    assert math.isclose(e[0], math.cos(750.0)) and math.isclose(e[128], math.sin(750.0))
+    assert math.isclose(e[127], math.cos(750.0 * 1e4 ** (-127 / 128)))
+
+
+def test_student_loop_special_cases():
+    wl = W.TINY.replace(n_blocks=1)
+    w = W.block_weights(wl, 0, "f32")
+    tw = W.timestep_weights(wl, 0, "f32")
+    bi = W.block_inputs(wl, 0, "f32")
+    sh = O.BlockShape.of(wl)
+    # equal sigmas: no motion
+    z = O.student_loop(bi.x, [w], tw, bi.pos, bi.cu_slots, bi.valid_len, sh, (0.5, 0.5, 0.5))
+    assert np.array_equal(z, bi.x.astype(np.float64))
+    # one step from sigma 1 to 0 with one block: z - block(z)
+    z = O.student_loop(bi.x, [w], tw, bi.pos, bi.cu_slots, bi.valid_len, sh, (1.0, 0.0))
+    mod = O.timestep_modulation(1.0, tw)[0][None]
+    u = O.dit_block(bi.x, mod, w, bi.pos, bi.cu_slots, bi.valid_len, sh)
+    assert np.allclose(z, bi.x - u, atol=1e-12)
+
+
+def test_block_gated_branch_enters_linearly():
+    """Doubling W3 doubles the MLP update exactly (silu sits on the W1 branch)."""
+    import dataclasses
+    wl, w, bi = _tiny()
+    sh = O.BlockShape.of(wl)
+    w_att_off = dataclasses.replace(w, w_o=0 * w.w_o)
+    x = bi.x.astype(np.float64)
+    d1 = O.dit_block(bi.x, bi.mod, w_att_off, bi.pos, bi.cu_slots, bi.valid_len, sh) - x
+    w_twice = dataclasses.replace(w_att_off, w3=2 * w.w3)
+    d2 = O.dit_block(bi.x, bi.mod, w_twice, bi.pos, bi.cu_slots, bi.valid_len, sh) - x
+    assert np.allclose(d2, 2 * d1, atol=1e-12)
+    w_w1 = dataclasses.replace(w_att_off, w1=2 * w.w1)
+    d3 = O.dit_block(bi.x, bi.mod, w_w1, bi.pos, bi.cu_slots, bi.valid_len, sh) - x
+    assert not np.allclose(d3, 2 * d1, atol=1e-6)
+
+
+def test_block_value_rows_drive_the_attention_update():
+    """Zero value projection rows (the last third of Wqkv) silence attention."""
+    import dataclasses
+    wl, w, bi = _tiny()
+    sh = O.BlockShape.of(wl)
+    hd = wl.n_heads * wl.head_dim
+    wq = w.w_qkv.copy()
+    wq[2 * hd:] = 0
+    w_v0 = dataclasses.replace(w, w_qkv=wq, w2=0 * w.w2)
+    out = O.dit_block(bi.x, bi.mod, w_v0, bi.pos, bi.cu_slots, bi.valid_len, sh)
+    assert np.array_equal(out, bi.x.astype(np.float64))
+
+
+def _brute_block(x, mod, w, pos, n_valid, C, H, D, secs, theta, eps):
+    """Direct loops over tokens, heads and dims: one segment [0, n), first n_valid valid."""
+    n = len(x)
+    E = math.exp
+
+    def modnorm(row, sh, sc):
+        mu = sum(row) / C
+        var = sum((a - mu) ** 2 for a in row) / C
+        return [(a - mu) / math.sqrt(var + eps) * (1 + sc[c]) + sh[c] for c, a in enumerate(row)]
+
+    def mv(wm, vec):  # wm [out][in]
+        return [sum(wm[o][c] * vec[c] for c in range(len(vec))) for o in range(len(wm))]
+
+    def angle(p, i):  # pair i of a head row
+        if p[0] == 1:
+            return p[1] * theta ** (-2 * i / D)
+        off = 0
+        for ax, d in enumerate(secs):
+            if i < off + d // 2:
+                return p[1 + ax] * theta ** (-2 * (i - off) / d)
+            off += d // 2
+
+    h1 = [modnorm(list(x[t]), mod[t][0], mod[t][1]) for t in range(n)]
+    qkv = [mv(w.w_qkv.tolist(), h1[t]) for t in range(n)]
+    q = [[[qkv[t][hh * D + c] for c in range(D)] for hh in range(H)] for t in range(n)]
+    k = [[[qkv[t][H * D + hh * D + c] for c in range(D)] for hh in range(H)] for t in range(n)]
+    v = [[[qkv[t][2 * H * D + hh * D + c] for c in range(D)] for hh in range(H)] for t in range(n)]
+    for t in range(n):
+        if pos[t][0] == 2:
+            continue
+        for arr, g in ((q, w.g_q), (k, w.g_k)):
+            for hh in range(H):
+                r = arr[t][hh]
+                rms = math.sqrt(sum(a * a for a in r) / D + eps)
+                r = [r[c] / rms * g[c] for c in range(D)]
+                out = []
+                for i in range(D // 2):
+                    a, b = r[2 * i], r[2 * i + 1]
+                    phi = angle(pos[t], i)
+                    out += [a * math.cos(phi) - b * math.sin(phi), a * math.sin(phi) + b * math.cos(phi)]
+                arr[t][hh] = out
+    o = [[0.0] * (H * D) for _ in range(n)]
+    for t in range(n_valid):
+        for hh in range(H):
+            s = [sum(q[t][hh][c] * k[j][hh][c] for c in range(D)) / math.sqrt(D) for j in range(n_valid)]
+            m = max(s)
+            e = [E(a - m) for a in s]
+            z = sum(e)
+            for c in range(D):
+                o[t][hh * D + c] = sum(e[j] * v[j][hh][c] for j in range(n_valid)) / z
+    res = []
+    for t in range(n):
+        y1 = mv(w.w_o.tolist(), o[t])
+        x1 = [x[t][c] + mod[t][2][c] * y1[c] for c in range(C)]
+        h2 = modnorm(x1, mod[t][3], mod[t][4])
+        a = mv(w.w1.tolist(), h2)
+        b = mv(w.w3.tolist(), h2)
+        g = [a[i] / (1 + E(-a[i])) * b[i] for i in range(len(a))]
+        y2 = mv(w.w2.tolist(), g)
+        res.append([x1[c] + mod[t][5][c] * y2[c] for c in range(C)])
+    return np.array(res)
+
+
+def test_block_brute_force_tiny():
+    C, H, D, Fd, secs = 12, 2, 8, 10, (2, 2, 4)
+    r = np.random.default_rng(7)
+    w = W.BlockWeights(w_qkv=r.standard_normal((3 * H * D, C)) * 0.5, w_o=r.standard_normal((C, H * D)) * 0.5,
+                       w1=r.standard_normal((Fd, C)), w3=r.standard_normal((Fd, C)),
+                       w2=r.standard_normal((C, Fd)) * 0.5, g_q=1 + 0.3 * r.standard_normal(D),
+                       g_k=1 + 0.3 * r.standard_normal(D))
+    pos = np.array([[0, 0, 0, 0], [0, 0, 1, 2], [0, 1, 0, 3], [0, 2, 1, 1], [1, 4, 0, 0], [2, 0, 0, 0]], np.int32)
+    x = r.standard_normal((6, C))
+    mod = r.standard_normal((6, 6, C)) * 0.3
+    sh = O.BlockShape(dim=C, n_heads=H, head_dim=D, ffn_dim=Fd, sections=secs)
+    got = O.dit_block(x, mod, w, pos, np.array([0, 6]), np.array([5]), sh)
+    ref = _brute_block(x, mod, w, pos, 5, C, H, D, secs, 1e4, 1e-6)
+    assert np.allclose(got, ref, atol=1e-11)
