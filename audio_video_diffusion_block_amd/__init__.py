@@ -1,0 +1,277 @@
+"""Python binding of libh3dit.so: one DiT block forward on a packed
+audio-video token sequence, hand-written HIP for MI355X (gfx950).
+
+Argument marshalling only.  Every function takes torch tensors that already
+live in device memory (torch is the allocator and the stream provider) and
+passes raw pointers, strides and sizes to the C ABI declared in
+``include/h3dit.h``; all arithmetic happens in the library's kernels.  There
+is no CPU fallback: if the library is missing, importing the binding raises.
+
+Names mirror the C entry points (``h3_qk_norm_rope`` ...); tensors' row
+strides are taken from the tensors themselves.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libh3dit.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m audio_video_diffusion_block_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+H3_OK, H3_ERR_ARG, H3_ERR_UNSUPPORTED, H3_ERR_WORKSPACE, H3_ERR_HIP = range(5)
+H3_F32, H3_BF16 = 0, 1
+POS_VIDEO, POS_AUDIO, POS_PAD = 0, 1, 2
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class H3Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"h3dit status {status} ({_status_string(status)}): {detail}")
+        self.status = status
+
+
+class BlockConfig(ctypes.Structure):
+    _fields_ = [("dim", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn_dim", _i32),
+                ("sec_t", _i32), ("sec_h", _i32), ("sec_w", _i32), ("theta", _f),
+                ("eps_qk", _f), ("eps_mod", _f), ("norm_kind", _i32), ("dtype", _i32)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", _p), ("w_o", _p), ("w1", _p), ("w3", _p), ("w2", _p), ("g_q", _p),
+                ("g_k", _p)]
+
+
+class BlockIO(ctypes.Structure):
+    _fields_ = [("x", _p), ("ld_x", _i64), ("mod", _p), ("ld_mod", _i64), ("pos", _p),
+                ("cu_slots", _p), ("valid_len", _p), ("n_seg", _i32), ("max_valid_len", _i32),
+                ("n_tok_local", _i64), ("n_buf", _i64), ("tok_begin", _i64),
+                ("head_begin", _i32), ("head_count", _i32), ("qkv_attn", _p), ("o_attn", _p),
+                ("o_local", _p)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_lib.h3_abi_version.restype = ctypes.c_int
+_lib.h3_status_string.restype = ctypes.c_char_p
+_lib.h3_status_string.argtypes = [ctypes.c_int]
+_lib.h3_last_error.restype = ctypes.c_char_p
+
+_c_qk = _sig("h3_qk_norm_rope", ctypes.c_int,
+             [_p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _i32, _f, _f, _i32, _p])
+_c_attn_ws = _sig("h3_varlen_attn_workspace_size", _sz, [_i64, _i32, _i32, _i32, _i32])
+_c_attn = _sig("h3_varlen_attn", ctypes.c_int,
+               [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _f,
+                _p, _sz, _i32, _p])
+_c_modres = _sig("h3_modulate_residual", ctypes.c_int,
+                 [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _i32, _i32, _f, _i32, _p])
+_c_linear = _sig("h3_linear", ctypes.c_int,
+                 [_p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i32, _p])
+_c_swiglu_ws = _sig("h3_swiglu_workspace_size", _sz, [_i64, _i32, _i32])
+_c_swiglu = _sig("h3_swiglu", ctypes.c_int,
+                 [_p, _i64, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _sz, _i32, _p])
+_c_block_ws = _sig("h3_dit_block_workspace_size", _sz,
+                   [ctypes.POINTER(BlockConfig), _i64, _i64, _i32])
+_c_block = _sig("h3_dit_block_forward", ctypes.c_int,
+                [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), ctypes.POINTER(BlockIO),
+                 _p, _sz, _p])
+_c_temb_ws = _sig("h3_timestep_workspace_size", _sz, [_i32])
+_c_temb = _sig("h3_timestep_modulation", ctypes.c_int,
+               [_f, _p, _p, _p, _p, _i32, _i32, _i32, _p, _sz, _i32, _p])
+_c_euler = _sig("h3_euler_update", ctypes.c_int, [_p, _p, _p, _i64, _f, _f, _i32, _p])
+
+EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_rope",
+            "h3_varlen_attn_workspace_size", "h3_varlen_attn", "h3_modulate_residual",
+            "h3_linear", "h3_swiglu_workspace_size", "h3_swiglu", "h3_dit_block_workspace_size",
+            "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
+            "h3_euler_update")
+
+
+def _status_string(st: int) -> str:
+    return _lib.h3_status_string(st).decode()
+
+
+def last_error() -> str:
+    return _lib.h3_last_error().decode()
+
+
+def abi_version() -> int:
+    return _lib.h3_abi_version()
+
+
+def _check(st: int):
+    if st != H3_OK:
+        raise H3Error(st, last_error())
+
+
+# --------------------------------------------------------------- marshalling
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return H3_BF16
+    if t.dtype == torch.float32:
+        return H3_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live in device memory")
+    return t.data_ptr()
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row stride (elements) of a 2-D view whose rows may be strided, columns contiguous."""
+    if t.dim() == 1:
+        return t.shape[0]
+    if t.stride(-1) != 1:
+        raise ValueError("innermost dimension must be contiguous")
+    return t.stride(0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _bytes_ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entries
+
+def h3_qk_norm_rope(q: torch.Tensor, k: torch.Tensor, n_heads: int, head_dim: int,
+                    g_q: torch.Tensor, g_k: torch.Tensor, pos: torch.Tensor,
+                    sections: Sequence[int], theta: float = 1e4, eps: float = 1e-6, stream=None):
+    """In place on q, k (views [n_tok, >= H*D] with row strides)."""
+    _check(_c_qk(_ptr(q), _ld(q), _ptr(k), _ld(k), q.shape[0], n_heads, head_dim, _ptr(g_q),
+                 _ptr(g_k), _ptr(pos), sections[0], sections[1], sections[2], theta, eps, _dt(q),
+                 _stream(stream)))
+
+
+def varlen_attn_workspace_size(n_buf: int, n_heads: int, head_dim: int, n_seg: int, dtype) -> int:
+    return _c_attn_ws(n_buf, n_heads, head_dim, n_seg, H3_BF16 if dtype == torch.bfloat16 else H3_F32)
+
+
+def h3_varlen_attn(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tensor,
+                   valid_len: Optional[torch.Tensor], max_valid_len: int,
+                   softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None, stream=None):
+    n_buf = q.shape[0]
+    n_seg = cu_slots.shape[0] - 1
+    need = varlen_attn_workspace_size(n_buf, n_heads, head_dim, n_seg, q.dtype)
+    if ws is None:
+        ws = _bytes_ws(need, q.device)
+    _check(_c_attn(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
+                   n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
+                   softmax_scale, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
+                   _stream(stream)))
+
+
+def h3_modulate_residual(x, y=None, gate=None, shift=None, scale=None, h_out=None,
+                         ld_mod: Optional[int] = None, norm_kind: int = 0, eps: float = 1e-6,
+                         stream=None):
+    """x [n, C] in place; gate/shift/scale [n or 1, C] row views (ld_mod 0 = broadcast)."""
+    mod_ref = next((t for t in (gate, shift, scale) if t is not None), None)
+    if ld_mod is None:
+        ld_mod = 0 if mod_ref is None or mod_ref.shape[0] == 1 else _ld(mod_ref)
+    _check(_c_modres(_ptr(x), _ld(x), _ptr(y), _ld(y) if y is not None else 0, _ptr(gate),
+                     _ptr(shift), _ptr(scale), ld_mod, _ptr(h_out),
+                     _ld(h_out) if h_out is not None else 0, x.shape[0], x.shape[1], norm_kind, eps,
+                     _dt(x), _stream(stream)))
+
+
+def h3_linear(a, w, out, gate=None, ld_gate: Optional[int] = None, stream=None):
+    """out = a @ w^T, or out += gate * (a @ w^T) if gate is given."""
+    if gate is not None and ld_gate is None:
+        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    _check(_c_linear(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(out), _ld(out), a.shape[0],
+                     w.shape[0], a.shape[1], _ptr(gate), ld_gate or 0, _dt(a), _stream(stream)))
+
+
+def swiglu_workspace_size(n_tok: int, ffn_dim: int, dtype) -> int:
+    return _c_swiglu_ws(n_tok, ffn_dim, H3_BF16 if dtype == torch.bfloat16 else H3_F32)
+
+
+def h3_swiglu(h, w1, w3, w2, out, gate=None, ld_gate: Optional[int] = None,
+              ws: Optional[torch.Tensor] = None, stream=None):
+    n, c = h.shape
+    f = w1.shape[0]
+    if gate is not None and ld_gate is None:
+        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    if ws is None:
+        ws = _bytes_ws(swiglu_workspace_size(n, f, h.dtype), h.device)
+    _check(_c_swiglu(_ptr(h), _ld(h), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out), _ld(out),
+                     _ptr(gate), ld_gate or 0, n, c, f, _ptr(ws), ws.numel() * ws.element_size(),
+                     _dt(h), _stream(stream)))
+
+
+def block_config(dim, n_heads, head_dim, ffn_dim, sections, theta=1e4, eps_qk=1e-6,
+                 eps_mod=1e-6, norm_kind=0, dtype=torch.bfloat16) -> BlockConfig:
+    return BlockConfig(dim, n_heads, head_dim, ffn_dim, sections[0], sections[1], sections[2],
+                       theta, eps_qk, eps_mod, norm_kind,
+                       H3_BF16 if dtype == torch.bfloat16 else H3_F32)
+
+
+def block_workspace_size(cfg: BlockConfig, n_tok_local: int, n_buf: int, n_seg: int) -> int:
+    return _c_block_ws(ctypes.byref(cfg), n_tok_local, n_buf, n_seg)
+
+
+def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots, valid_len,
+                         max_valid_len: int, ws=None, n_buf: Optional[int] = None,
+                         tok_begin: int = 0, head_begin: int = 0, head_count: Optional[int] = None,
+                         qkv_attn=None, o_attn=None, o_local=None, stream=None):
+    """One block, x [n, C] updated in place.  mod is [n, 6, C] or [1, 6, C] (broadcast)."""
+    n = x.shape[0]
+    share = qkv_attn is not None
+    n_buf = n_buf if n_buf is not None else (qkv_attn.shape[0] if share else n)
+    n_seg = cu_slots.shape[0] - 1
+    w = BlockWeights(*(_ptr(weights[k]) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")))
+    ld_mod = 0 if mod.shape[0] == 1 else mod.stride(0)
+    io = BlockIO(_ptr(x), _ld(x), _ptr(mod), ld_mod, _ptr(pos), _ptr(cu_slots), _ptr(valid_len),
+                 n_seg, max_valid_len, n, n_buf, tok_begin, head_begin,
+                 head_count if head_count is not None else cfg.n_heads, _ptr(qkv_attn),
+                 _ptr(o_attn), _ptr(o_local))
+    need = block_workspace_size(cfg, n, n_buf, n_seg)
+    if ws is None:
+        ws = _bytes_ws(need, x.device)
+    _check(_c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), _ptr(ws),
+                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def timestep_workspace_size(dim: int) -> int:
+    return _c_temb_ws(dim)
+
+
+def h3_timestep_modulation(sigma: float, w_t1, w_t2, table, mod_out, ws=None, stream=None):
+    nb, six, c = table.shape
+    if ws is None:
+        ws = _bytes_ws(timestep_workspace_size(c), table.device)
+    _check(_c_temb(sigma, _ptr(w_t1), _ptr(w_t2), _ptr(table), _ptr(mod_out), nb, c,
+                   w_t1.shape[1], _ptr(ws), ws.numel() * ws.element_size(), _dt(table),
+                   _stream(stream)))
+
+
+def h3_euler_update(z, u, x_next=None, sigma_from: float = 0.0, sigma_to: float = 0.0,
+                    stream=None):
+    _check(_c_euler(_ptr(z), _ptr(u), _ptr(x_next), z.numel(), sigma_from, sigma_to, _dt(z),
+                    _stream(stream)))

@@ -1,0 +1,516 @@
+// C ABI of h3dit: argument validation, workspace carving and the launch
+// sequence of the DiT block.  Every check runs on the host before anything is
+// enqueued; a failed check returns a status and launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/h3dit.h"
+#include "h3_common.hpp"
+#include "h3_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+h3_status fail(h3_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+h3_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return H3_OK;
+  return fail(H3_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t esize(h3_dtype dt) { return dt == H3_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define CHECK(cond, ...)                              \
+  do {                                                \
+    if (!(cond)) return fail(H3_ERR_ARG, __VA_ARGS__); \
+  } while (0)
+
+h3_status check_dtype(h3_dtype dt) {
+  if (dt != H3_F32 && dt != H3_BF16) return fail(H3_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+  return H3_OK;
+}
+
+// tensor pointer p of rows with stride ld (elements) and width w (elements)
+h3_status check_rows(const char* name, const void* p, int64_t ld, int64_t width, int64_t rows,
+                     h3_dtype dt, bool required = true) {
+  if (!p) {
+    if (required && rows > 0) return fail(H3_ERR_ARG, "%s is NULL", name);
+    return H3_OK;
+  }
+  if (!aligned16(p)) return fail(H3_ERR_ARG, "%s is not 16-byte aligned", name);
+  if (ld < 0 || (ld != 0 && ld < width))
+    return fail(H3_ERR_ARG, "%s: row stride %lld below row width %lld", name, (long long)ld,
+                (long long)width);
+  if ((ld * (int64_t)esize(dt)) % 16 != 0)
+    return fail(H3_ERR_ARG, "%s: row stride %lld elements is not a multiple of 16 bytes", name,
+                (long long)ld);
+  return H3_OK;
+}
+
+// Device check, cached per device: gfx950 only.
+std::atomic<int> g_dev_ok[64];
+
+h3_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(H3_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(H3_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return H3_OK;
+}
+
+#define TRY(expr)                          \
+  do {                                     \
+    h3_status _st = (expr);                \
+    if (_st != H3_OK) return _st;          \
+  } while (0)
+
+h3_status check_head_dim(int32_t d) {
+  if (d != 64 && d != 128) return fail(H3_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d);
+  return H3_OK;
+}
+
+h3_status check_sections(int32_t d, int32_t st, int32_t sh, int32_t sw) {
+  CHECK(st >= 0 && sh >= 0 && sw >= 0, "negative RoPE section");
+  CHECK(st % 2 == 0 && sh % 2 == 0 && sw % 2 == 0, "RoPE sections must be even (%d,%d,%d)", st, sh, sw);
+  CHECK(st + sh + sw == d, "RoPE sections %d+%d+%d do not sum to head_dim %d", st, sh, sw, d);
+  return H3_OK;
+}
+
+h3_status validate_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t n_tok, int32_t H,
+                      int32_t D, const void* g_q, const void* g_k, const h3_pos* pos,
+                      int32_t st, int32_t sh, int32_t sw, float theta, float eps, h3_dtype dt) {
+  TRY(check_dtype(dt));
+  CHECK(n_tok >= 0, "n_tok < 0");
+  CHECK(H > 0, "n_heads must be positive");
+  TRY(check_head_dim(D));
+  TRY(check_sections(D, st, sh, sw));
+  CHECK(theta > 0.f && std::isfinite(theta), "theta must be positive");
+  CHECK(eps >= 0.f, "eps < 0");
+  if (n_tok == 0) return H3_OK;
+  TRY(check_rows("q", q, ld_q, (int64_t)H * D, n_tok, dt));
+  TRY(check_rows("k", k, ld_k, (int64_t)H * D, n_tok, dt));
+  CHECK(ld_q > 0 && ld_k > 0, "q/k row stride must be positive");
+  CHECK(g_q && g_k, "gains are NULL");
+  CHECK(aligned16(g_q) && aligned16(g_k), "gains are not 16-byte aligned");
+  CHECK(pos && aligned16(pos), "pos is NULL or not 16-byte aligned");
+  return H3_OK;
+}
+
+h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
+                        int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf, int32_t H,
+                        int32_t D, const int32_t* cu, int32_t n_seg, int32_t max_len,
+                        void* ws, size_t ws_bytes, h3_dtype dt) {
+  TRY(check_dtype(dt));
+  CHECK(n_buf >= 0 && n_buf < (int64_t)INT32_MAX, "n_buf out of range");
+  CHECK(H > 0, "n_heads must be positive");
+  TRY(check_head_dim(D));
+  CHECK(n_seg >= 1 && n_seg <= 65535, "n_seg must be in [1, 65535]");
+  CHECK(max_len >= 0 && max_len <= n_buf, "max_valid_len must be in [0, n_buf]");
+  CHECK(cu != nullptr, "cu_slots is NULL");
+  if (n_buf == 0) return H3_OK;
+  const int64_t w = (int64_t)H * D;
+  TRY(check_rows("q", q, ld_q, w, n_buf, dt));
+  TRY(check_rows("k", k, ld_k, w, n_buf, dt));
+  TRY(check_rows("v", v, ld_v, w, n_buf, dt));
+  TRY(check_rows("o", o, ld_o, w, n_buf, dt));
+  CHECK(ld_q > 0 && ld_k > 0 && ld_v > 0 && ld_o > 0, "row strides must be positive");
+  const size_t need = h3::attn_workspace_bytes(dt == H3_BF16, n_buf, H, D, n_seg);
+  if (ws_bytes < need)
+    return fail(H3_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu", ws_bytes, need);
+  CHECK(need == 0 || (ws && aligned16(ws)), "workspace is NULL or not 16-byte aligned");
+  return H3_OK;
+}
+
+h3_status validate_modres(void* x, int64_t ld_x, const void* y, int64_t ld_y, const void* gate,
+                          const void* shift, const void* scale, int64_t ld_mod, void* h,
+                          int64_t ld_h, int64_t n_tok, int32_t dim, int32_t norm_kind, float eps,
+                          h3_dtype dt) {
+  TRY(check_dtype(dt));
+  CHECK(n_tok >= 0 && n_tok <= (int64_t)INT32_MAX, "n_tok out of range");
+  CHECK(dim > 0 && dim % 8 == 0 && dim <= 16384, "dim must be a positive multiple of 8, <= 16384");
+  CHECK(norm_kind == 0 || norm_kind == 1, "norm_kind must be 0 or 1");
+  CHECK(eps >= 0.f, "eps < 0");
+  if (n_tok == 0) return H3_OK;
+  TRY(check_rows("x", x, ld_x, dim, n_tok, dt));
+  CHECK(ld_x > 0, "x row stride must be positive");
+  CHECK(y || h, "nothing to do: y and h_out are both NULL");
+  if (y) {
+    TRY(check_rows("y", y, ld_y, dim, n_tok, dt));
+    CHECK(ld_y > 0, "y row stride must be positive");
+    TRY(check_rows("gate", gate, ld_mod, dim, n_tok, dt));
+  }
+  if (h) {
+    TRY(check_rows("h_out", h, ld_h, dim, n_tok, dt));
+    CHECK(ld_h > 0, "h_out row stride must be positive");
+    TRY(check_rows("shift", shift, ld_mod, dim, n_tok, dt));
+    TRY(check_rows("scale", scale, ld_mod, dim, n_tok, dt));
+  }
+  return H3_OK;
+}
+
+h3_status validate_linear(const void* a, int64_t lda, const void* w, int64_t ldw, void* out,
+                          int64_t ld_out, int64_t m, int32_t n_out, int32_t k_in,
+                          const void* gate, int64_t ld_gate, h3_dtype dt) {
+  TRY(check_dtype(dt));
+  CHECK(m >= 0 && m <= (int64_t)INT32_MAX, "m out of range");
+  CHECK(n_out > 0 && k_in > 0 && k_in % 8 == 0, "n_out > 0 and k_in a positive multiple of 8 required");
+  if (m == 0) return H3_OK;
+  TRY(check_rows("a", a, lda, k_in, m, dt));
+  TRY(check_rows("w", w, ldw, k_in, n_out, dt));
+  TRY(check_rows("out", out, ld_out, n_out, m, dt));
+  CHECK(lda > 0 && ldw > 0 && ld_out > 0, "row strides must be positive");
+  if (gate) TRY(check_rows("gate", gate, ld_gate, n_out, m, dt));
+  return H3_OK;
+}
+
+}  // namespace
+
+using namespace h3;
+
+extern "C" {
+
+int h3_abi_version(void) { return H3_ABI_VERSION; }
+
+const char* h3_status_string(h3_status st) {
+  switch (st) {
+    case H3_OK: return "ok";
+    case H3_ERR_ARG: return "invalid argument";
+    case H3_ERR_UNSUPPORTED: return "unsupported";
+    case H3_ERR_WORKSPACE: return "workspace too small";
+    case H3_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* h3_last_error(void) { return g_err; }
+
+h3_status h3_qk_norm_rope(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t n_tok,
+                          int32_t n_heads, int32_t head_dim, const void* g_q, const void* g_k,
+                          const h3_pos* pos, int32_t sec_t, int32_t sec_h, int32_t sec_w,
+                          float theta, float eps, h3_dtype dtype, void* stream) {
+  g_err[0] = 0;
+  TRY(validate_qk(q, ld_q, k, ld_k, n_tok, n_heads, head_dim, g_q, g_k, pos, sec_t, sec_h, sec_w,
+                  theta, eps, dtype));
+  if (n_tok == 0) return H3_OK;
+  TRY(check_device());
+  return hip_status(launch_qk_norm_rope(dtype == H3_BF16, head_dim, q, ld_q, k, ld_k, n_tok,
+                                        n_heads, g_q, g_k, pos, sec_t, sec_h, theta, eps,
+                                        (hipStream_t)stream),
+                    "qk_norm_rope launch");
+}
+
+size_t h3_varlen_attn_workspace_size(int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                     int32_t n_seg, h3_dtype dtype) {
+  if (n_buf <= 0 || n_heads <= 0 || head_dim <= 0 || n_seg <= 0) return 0;
+  return attn_workspace_bytes(dtype == H3_BF16, n_buf, n_heads, head_dim, n_seg);
+}
+
+h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                         const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
+                         int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
+                         const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
+                         float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
+                         void* stream) {
+  g_err[0] = 0;
+  TRY(validate_attn(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, head_dim, cu_slots, n_seg,
+                    max_valid_len, ws, ws_bytes, dtype));
+  if (n_buf == 0) return H3_OK;
+  TRY(check_device());
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  return hip_status(launch_varlen_attn(dtype == H3_BF16, head_dim, q, ld_q, k, ld_k, v, ld_v, o,
+                                       ld_o, n_buf, n_heads, cu_slots, valid_len, n_seg,
+                                       max_valid_len, scale, ws, (hipStream_t)stream),
+                    "varlen_attn launch");
+}
+
+h3_status h3_modulate_residual(void* x, int64_t ld_x, const void* y, int64_t ld_y,
+                               const void* gate, const void* shift, const void* scale,
+                               int64_t ld_mod, void* h_out, int64_t ld_h, int64_t n_tok,
+                               int32_t dim, int32_t norm_kind, float eps, h3_dtype dtype,
+                               void* stream) {
+  g_err[0] = 0;
+  TRY(validate_modres(x, ld_x, y, ld_y, gate, shift, scale, ld_mod, h_out, ld_h, n_tok, dim,
+                      norm_kind, eps, dtype));
+  if (n_tok == 0) return H3_OK;
+  TRY(check_device());
+  return hip_status(launch_modulate_residual(dtype == H3_BF16, x, ld_x, y, ld_y, gate, shift,
+                                             scale, ld_mod, h_out, ld_h, n_tok, dim, norm_kind,
+                                             eps, (hipStream_t)stream),
+                    "modulate_residual launch");
+}
+
+h3_status h3_linear(const void* a, int64_t lda, const void* w, int64_t ldw, void* out,
+                    int64_t ld_out, int64_t m, int32_t n_out, int32_t k_in, const void* gate,
+                    int64_t ld_gate, h3_dtype dtype, void* stream) {
+  g_err[0] = 0;
+  TRY(validate_linear(a, lda, w, ldw, out, ld_out, m, n_out, k_in, gate, ld_gate, dtype));
+  if (m == 0) return H3_OK;
+  TRY(check_device());
+  return hip_status(launch_gemm(dtype == H3_BF16, gate ? EPI_RESIDUAL : EPI_STORE, a, lda, w,
+                                nullptr, ldw, out, ld_out, gate, ld_gate, m, n_out, k_in,
+                                (hipStream_t)stream),
+                    "linear launch");
+}
+
+size_t h3_swiglu_workspace_size(int64_t n_tok, int32_t ffn_dim, h3_dtype dtype) {
+  if (n_tok <= 0 || ffn_dim <= 0) return 0;
+  return (size_t)round_up((int64_t)n_tok * ffn_dim * (int64_t)esize(dtype), 256);
+}
+
+h3_status h3_swiglu(const void* h, int64_t ld_h, const void* w1, const void* w3,
+                    const void* w2, void* out, int64_t ld_out, const void* gate,
+                    int64_t ld_gate, int64_t n_tok, int32_t dim, int32_t ffn_dim, void* ws,
+                    size_t ws_bytes, h3_dtype dtype, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dtype(dtype));
+  CHECK(n_tok >= 0 && n_tok <= (int64_t)INT32_MAX, "n_tok out of range");
+  CHECK(dim > 0 && dim % 8 == 0 && ffn_dim > 0 && ffn_dim % 8 == 0,
+        "dim and ffn_dim must be positive multiples of 8");
+  if (n_tok == 0) return H3_OK;
+  TRY(check_rows("h", h, ld_h, dim, n_tok, dtype));
+  TRY(check_rows("w1", w1, dim, dim, ffn_dim, dtype));
+  TRY(check_rows("w3", w3, dim, dim, ffn_dim, dtype));
+  TRY(check_rows("w2", w2, ffn_dim, ffn_dim, dim, dtype));
+  TRY(check_rows("out", out, ld_out, dim, n_tok, dtype));
+  CHECK(ld_h > 0 && ld_out > 0, "row strides must be positive");
+  if (gate) TRY(check_rows("gate", gate, ld_gate, dim, n_tok, dtype));
+  const size_t need = h3_swiglu_workspace_size(n_tok, ffn_dim, dtype);
+  if (ws_bytes < need) return fail(H3_ERR_WORKSPACE, "swiglu workspace %zu bytes, need %zu", ws_bytes, need);
+  CHECK(ws && aligned16(ws), "workspace is NULL or not 16-byte aligned");
+  TRY(check_device());
+  const bool bf = dtype == H3_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  TRY(hip_status(launch_gemm(bf, EPI_SWIGLU, h, ld_h, w1, w3, dim, ws, ffn_dim, nullptr, 0, n_tok,
+                             ffn_dim, dim, s),
+                 "swiglu up-projection launch"));
+  return hip_status(launch_gemm(bf, gate ? EPI_RESIDUAL : EPI_STORE, ws, ffn_dim, w2, nullptr,
+                                ffn_dim, out, ld_out, gate, ld_gate, n_tok, dim, ffn_dim, s),
+                    "swiglu down-projection launch");
+}
+
+// ------------------------------------------------------------------- block
+
+namespace {
+struct BlockWs {
+  size_t h1, qkv, attn, o, g, total;
+};
+
+BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int32_t n_seg,
+                        bool share, int32_t head_count) {
+  const int64_t es = (int64_t)esize(c->dtype);
+  const int64_t hd = (int64_t)c->n_heads * c->head_dim;
+  BlockWs w{};
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t at = off;
+    off += (size_t)round_up(bytes, 256);
+    return at;
+  };
+  w.h1 = take(n * c->dim * es);
+  w.qkv = take(n * 3 * hd * es);
+  w.attn = take((int64_t)attn_workspace_bytes(c->dtype == H3_BF16, share ? n_buf : n,
+                                              share ? head_count : c->n_heads, c->head_dim, n_seg));
+  w.o = take(share ? 0 : n * hd * es);
+  w.g = take(n * (int64_t)c->ffn_dim * es);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t h3_dit_block_workspace_size(const h3_block_config* cfg, int64_t n_tok_local,
+                                   int64_t n_buf, int32_t n_seg) {
+  if (!cfg || n_tok_local < 0 || n_buf < 0 || n_seg <= 0) return 0;
+  // the query does not know the mode: cover world 1 and a rank share of any head count
+  const size_t w1 = block_ws_layout(cfg, n_tok_local, n_tok_local, n_seg, false, cfg->n_heads).total;
+  const size_t sh = block_ws_layout(cfg, n_tok_local, n_buf, n_seg, true, cfg->n_heads).total;
+  return w1 > sh ? w1 : sh;
+}
+
+h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weights* w,
+                               const h3_block_io* io, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(cfg && w && io, "cfg, weights and io must be non-NULL");
+  const h3_dtype dt = cfg->dtype;
+  TRY(check_dtype(dt));
+  const int32_t C = cfg->dim, H = cfg->n_heads, D = cfg->head_dim, F = cfg->ffn_dim;
+  CHECK(C > 0 && C % 8 == 0 && C <= 16384, "dim must be a positive multiple of 8, <= 16384");
+  CHECK(H > 0 && F > 0 && F % 8 == 0, "n_heads > 0 and ffn_dim a positive multiple of 8 required");
+  TRY(check_head_dim(D));
+  TRY(check_sections(D, cfg->sec_t, cfg->sec_h, cfg->sec_w));
+  CHECK(cfg->norm_kind == 0 || cfg->norm_kind == 1, "norm_kind must be 0 or 1");
+  CHECK(cfg->theta > 0.f && cfg->eps_qk >= 0.f && cfg->eps_mod >= 0.f, "theta/eps out of range");
+  const int64_t n = io->n_tok_local;
+  CHECK(n >= 0 && n <= (int64_t)INT32_MAX, "n_tok_local out of range");
+  const bool share = io->qkv_attn != nullptr;
+  const int32_t hb = share ? io->head_begin : 0;
+  const int32_t hc = share ? io->head_count : H;
+  if (share) {
+    CHECK(io->o_attn && io->o_local, "rank-share mode needs qkv_attn, o_attn and o_local");
+    CHECK(hc > 0 && hb >= 0 && hb + hc <= H, "head slice [%d, %d) outside [0, %d)", hb, hb + hc, H);
+    CHECK(io->tok_begin >= 0 && io->tok_begin + n <= io->n_buf, "local rows outside the buffer");
+    CHECK(aligned16(io->qkv_attn) && aligned16(io->o_attn) && aligned16(io->o_local),
+          "exchange buffers must be 16-byte aligned");
+  } else {
+    CHECK(io->tok_begin == 0 && io->n_buf == n && (io->head_count == H || io->head_count == 0) &&
+              io->head_begin == 0,
+          "world-1 mode needs tok_begin 0, n_buf == n_tok_local, full head range");
+  }
+  if (n == 0) return H3_OK;
+  CHECK(io->n_seg >= 1 && io->n_seg <= 65535, "n_seg must be in [1, 65535]");
+  CHECK(io->max_valid_len >= 0 && io->max_valid_len <= io->n_buf, "max_valid_len out of range");
+  CHECK(io->cu_slots, "cu_slots is NULL");
+  CHECK(io->pos && aligned16(io->pos), "pos is NULL or not 16-byte aligned");
+  TRY(check_rows("x", io->x, io->ld_x, C, n, dt));
+  CHECK(io->ld_x > 0, "x row stride must be positive");
+  TRY(check_rows("mod", io->mod, io->ld_mod, 6 * (int64_t)C, n, dt));
+  const void* wp[] = {w->w_qkv, w->w_o, w->w1, w->w3, w->w2, w->g_q, w->g_k};
+  for (const void* p : wp) CHECK(p && aligned16(p), "a weight pointer is NULL or misaligned");
+  const BlockWs L = block_ws_layout(cfg, n, io->n_buf, io->n_seg, share, hc);
+  if (ws_bytes < L.total)
+    return fail(H3_ERR_WORKSPACE, "block workspace %zu bytes, need %zu", ws_bytes, L.total);
+  CHECK(ws && aligned16(ws), "workspace is NULL or not 16-byte aligned");
+  TRY(check_device());
+
+  const bool bf = dt == H3_BF16;
+  const int64_t es = (int64_t)esize(dt);
+  const int64_t hd = (int64_t)H * D;
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  void* h1 = wsb + L.h1;
+  char* qkv = wsb + L.qkv;
+  void* attn_ws = wsb + L.attn;
+  char* mod = (char*)io->mod;
+  const int64_t ldm = io->ld_mod;
+  auto mslot = [&](int i) { return (const void*)(mod + (int64_t)i * C * es); };
+
+  // A1 h1 = norm(x)(1 + scale1) + shift1
+  TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(0),
+                                          mslot(1), ldm, h1, C, n, C, cfg->norm_kind,
+                                          cfg->eps_mod, s),
+                 "modulate-1"));
+  // A2 qkv = h1 w_qkv^T
+  TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, qkv, 3 * hd, nullptr, 0,
+                             n, (int)(3 * hd), C, s),
+                 "qkv projection"));
+  // A3 Q/K RMSNorm + RoPE on the local rows
+  TRY(hip_status(launch_qk_norm_rope(bf, D, qkv, 3 * hd, qkv + hd * es, 3 * hd, n, H, w->g_q,
+                                     w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
+                                     cfg->eps_qk, s),
+                 "qk_norm_rope"));
+  const float scale = 1.0f / std::sqrt((float)D);
+  const void* o_for_proj;
+  if (!share) {
+    // A5 attention straight from the QKV buffer
+    void* o = wsb + L.o;
+    TRY(hip_status(launch_varlen_attn(bf, D, qkv, 3 * hd, qkv + hd * es, 3 * hd,
+                                      qkv + 2 * hd * es, 3 * hd, o, hd, n, H, io->cu_slots,
+                                      io->valid_len, io->n_seg, io->max_valid_len, scale,
+                                      attn_ws, s),
+                   "attention"));
+    o_for_proj = o;
+  } else {
+    const int64_t sd = (int64_t)hc * D;  // slice width
+    char* qa = (char*)io->qkv_attn;
+    // A4 this rank's q, k, v of heads [hb, hb+hc) into its rows of the attention buffer
+    TRY(hip_status(launch_copy_rows(qkv + hb * D * es, 3 * hd * es, hd * es,
+                                    qa + io->tok_begin * 3 * sd * es, 3 * sd * es, sd * es, n, 3,
+                                    sd * es, s),
+                   "exchange-in copy"));
+    // A5 attention over the whole buffer for the head slice
+    TRY(hip_status(launch_varlen_attn(bf, D, qa, 3 * sd, qa + sd * es, 3 * sd, qa + 2 * sd * es,
+                                      3 * sd, io->o_attn, sd, io->n_buf, hc, io->cu_slots,
+                                      io->valid_len, io->n_seg, io->max_valid_len, scale,
+                                      attn_ws, s),
+                   "attention"));
+    // A6 this rank's rows of the output into its head slice of o_local
+    TRY(hip_status(launch_copy_rows((char*)io->o_attn + io->tok_begin * sd * es, sd * es, 0,
+                                    (char*)io->o_local + hb * D * es, hd * es, 0, n, 1, sd * es,
+                                    s),
+                   "exchange-out copy"));
+    o_for_proj = io->o_local;
+  }
+  // A7 x <- x + gate1 * (o w_o^T)
+  TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, o_for_proj, hd, w->w_o, nullptr, hd, io->x,
+                             io->ld_x, mslot(2), ldm, n, C, (int)hd, s),
+                 "output projection"));
+  // A8 h2 = norm(x)(1 + scale2) + shift2   (h2 reuses h1's scratch)
+  TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(3),
+                                          mslot(4), ldm, h1, C, n, C, cfg->norm_kind,
+                                          cfg->eps_mod, s),
+                 "modulate-2"));
+  // A9 g = silu(h2 w1^T) * (h2 w3^T)
+  void* g = wsb + L.g;
+  TRY(hip_status(launch_gemm(bf, EPI_SWIGLU, h1, C, w->w1, w->w3, C, g, F, nullptr, 0, n, F, C, s),
+                 "swiglu up-projection"));
+  // A10 x <- x + gate2 * (g w2^T)
+  return hip_status(launch_gemm(bf, EPI_RESIDUAL, g, F, w->w2, nullptr, F, io->x, io->ld_x,
+                                mslot(5), ldm, n, C, F, s),
+                    "swiglu down-projection");
+}
+
+// ------------------------------------------------------------ loop glue
+
+size_t h3_timestep_workspace_size(int32_t dim) {
+  return dim > 0 ? (size_t)round_up((int64_t)dim * 4, 256) : 0;
+}
+
+h3_status h3_timestep_modulation(float sigma, const void* w_t1, const void* w_t2,
+                                 const void* table, void* mod_out, int32_t n_blocks,
+                                 int32_t dim, int32_t emb_dim, void* ws, size_t ws_bytes,
+                                 h3_dtype dtype, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dtype(dtype));
+  CHECK(std::isfinite(sigma), "sigma must be finite");
+  CHECK(dim > 0 && dim % 8 == 0, "dim must be a positive multiple of 8");
+  CHECK(emb_dim > 0 && emb_dim % 16 == 0 && emb_dim <= 1024, "emb_dim must be a multiple of 16, <= 1024");
+  CHECK(n_blocks > 0, "n_blocks must be positive");
+  CHECK(w_t1 && w_t2 && table && mod_out, "NULL tensor");
+  CHECK(aligned16(w_t1) && aligned16(w_t2), "weights must be 16-byte aligned");
+  if (ws_bytes < h3_timestep_workspace_size(dim))
+    return fail(H3_ERR_WORKSPACE, "timestep workspace too small");
+  CHECK(ws && aligned16(ws), "workspace is NULL or not 16-byte aligned");
+  TRY(check_device());
+  return hip_status(launch_timestep(dtype == H3_BF16, sigma, w_t1, w_t2, table, mod_out, n_blocks,
+                                    dim, emb_dim, ws, (hipStream_t)stream),
+                    "timestep launch");
+}
+
+h3_status h3_euler_update(void* z, const void* u, void* x_next, int64_t n, float sigma_from,
+                          float sigma_to, h3_dtype dtype, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dtype(dtype));
+  CHECK(n >= 0 && n % 8 == 0, "n must be a non-negative multiple of 8");
+  if (n == 0) return H3_OK;
+  CHECK(z && u && aligned16(z) && aligned16(u), "z and u must be non-NULL, 16-byte aligned");
+  CHECK(!x_next || aligned16(x_next), "x_next must be 16-byte aligned");
+  CHECK(std::isfinite(sigma_from) && std::isfinite(sigma_to), "sigmas must be finite");
+  TRY(check_device());
+  return hip_status(launch_euler(dtype == H3_BF16, z, u, x_next, n, sigma_to - sigma_from,
+                                 (hipStream_t)stream),
+                    "euler launch");
+}
+
+}  // extern "C"

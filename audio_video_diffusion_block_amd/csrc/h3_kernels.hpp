@@ -1,0 +1,48 @@
+// Internal launcher API between the C ABI (h3_api.cpp) and the kernel files.
+// Every launcher enqueues on `s` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace h3 {
+
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2 };
+
+hipError_t launch_qk_norm_rope(bool bf16, int head_dim, void* q, int64_t ld_q, void* k,
+                               int64_t ld_k, int64_t n_tok, int n_heads, const void* g_q,
+                               const void* g_k, const void* pos, int sec_t, int sec_h,
+                               float theta, float eps, hipStream_t s);
+
+hipError_t launch_modulate_residual(bool bf16, void* x, int64_t ld_x, const void* y,
+                                    int64_t ld_y, const void* gate, const void* shift,
+                                    const void* scale, int64_t ld_mod, void* h, int64_t ld_h,
+                                    int64_t n_tok, int dim, int norm_kind, float eps,
+                                    hipStream_t s);
+
+// out = A @ B^T with epilogue; for EPI_SWIGLU, B = W1, B3 = W3 and N = features
+hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B,
+                       const void* B3, int64_t ldb, void* C, int64_t ldc, const void* gate,
+                       int64_t ld_gate, int64_t M, int N, int K, hipStream_t s);
+
+size_t attn_workspace_bytes(bool bf16, int64_t n_buf, int n_heads, int head_dim, int n_seg);
+hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld_q,
+                              const void* k, int64_t ld_k, const void* v, int64_t ld_v, void* o,
+                              int64_t ld_o, int64_t n_buf, int n_heads, const int* cu,
+                              const int* valid, int n_seg, int max_len, float scale, void* ws,
+                              hipStream_t s);
+
+// strides and group sizes in BYTES (multiples of 16)
+hipError_t launch_copy_rows(const void* src, int64_t ld_src, int64_t gs_src, void* dst,
+                            int64_t ld_dst, int64_t gs_dst, int64_t rows, int groups,
+                            int64_t bytes_per_group, hipStream_t s);
+
+hipError_t launch_euler(bool bf16, void* z, const void* u, void* x_next, int64_t n, float dsig,
+                        hipStream_t s);
+
+hipError_t launch_timestep(bool bf16, float sigma, const void* w1, const void* w2,
+                           const void* table, void* mod_out, int n_blocks, int dim, int emb,
+                           void* ws, hipStream_t s);
+
+}  // namespace h3

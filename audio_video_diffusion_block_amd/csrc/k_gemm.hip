@@ -1,0 +1,280 @@
+// GEMMs of the block: out = A @ B^T with A [M, K] activations and B [N, K]
+// weights (torch Linear layout, both operands K-contiguous), fp32 accumulation,
+// and three epilogues:
+//   EPI_STORE     out = acc
+//   EPI_SWIGLU    out = silu(acc_w1) * acc_w3   (W1 and W3 columns of the same
+//                 output feature computed by the same wave)
+//   EPI_RESIDUAL  out = out + gate * acc        (gated residual, in place)
+//
+// Why Real-Time MiniMax H3 Serving Requires More Than a Faster DiT, "Key
+// takeaways": SwiGLU and residual updates are fused into neighbouring work.
+//
+// bf16 path (MFMA, gfx950): 256x256 output tile (256x128 for SwiGLU), K step
+// 64, 512 threads = 8 waves as 2 (M) x 4 (N), each wave 128x64 built from
+// 4x2 v_mfma_f32_32x32x16_bf16 tiles.  A and B tiles are staged through LDS,
+// double buffered (128 KiB), with the 16-byte chunk index XOR-swizzled by the
+// row so that MFMA operand reads of 32 rows at one k offset spread over banks.
+// The next K tile is fetched into registers while the current one is
+// multiplied.  Work-group ids are remapped so that the tiles one XCD runs at
+// a time form a compact 4 (M) x 8 (N) patch: their A and B panels are then
+// shared in that XCD's L2.
+//
+// fp32 path: a plain LDS-tiled FMA kernel (small problems, parity runs).
+#include "h3_common.hpp"
+#include "h3_kernels.hpp"
+
+namespace h3 {
+
+namespace {
+
+constexpr int BM = 256;
+constexpr int BN = 256;  // rows of the B tile
+constexpr int BK = 64;
+constexpr int NTHREADS = 512;
+constexpr int GROUP_M = 4;
+
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 7)) << 3);
+}
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+
+// XCD-aware mapping of a linear work-group id to (tile_m, tile_n).
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int total8 = total / 8 * 8;
+  // consecutive ids go to different XCDs; give each XCD a contiguous run of tiles
+  const int logical = bid < total8 ? (bid % 8) * (total8 / 8) + bid / 8 : bid;
+  const int per_group = GROUP_M * tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in_group = logical - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+    const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
+    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BK];
+
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;   // 2 waves along M
+  const int wn = wave >> 1;  // 4 waves along N
+
+  // ---- global load assignment: 4 chunks of A and 4 of B per thread ----
+  const int lchunk = tid & 7;
+  const int lrow = tid >> 3;  // 0..63, +64*i
+  const bf16_t* a_src[4];
+  const bf16_t* b_src[4];
+  bool a_ok[4], b_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 64 * i;
+    const int gm = m0 + r;
+    a_ok[i] = gm < M;
+    a_src[i] = A + (int64_t)(a_ok[i] ? gm : 0) * lda + lchunk * 8;
+    int gn;
+    const bf16_t* base;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // B tile rows [w*64, w*64+32) = W1 features, [w*64+32, w*64+64) = W3 features
+      const int w = r >> 6, within = r & 63;
+      gn = tn * 128 + w * 32 + (within & 31);
+      base = within < 32 ? B : B3;
+    } else {
+      gn = tn * BN + r;
+      base = B;
+    }
+    b_ok[i] = gn < N;
+    b_src[i] = base + (int64_t)(b_ok[i] ? gn : 0) * ldb + lchunk * 8;
+  }
+
+  uint4 ra[4], rb[4];
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BK + lchunk * 8;
+    const bool kin = k0 < K;  // K % 8 == 0: a chunk is wholly in or out
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = (a_ok[i] && kin) ? *reinterpret_cast<const uint4*>(a_src[i] + kt * BK)
+                               : make_uint4(0, 0, 0, 0);
+      rb[i] = (b_ok[i] && kin) ? *reinterpret_cast<const uint4*>(b_src[i] + kt * BK)
+                               : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 64 * i;
+      *reinterpret_cast<uint4*>(&As[buf][lds_off(r, lchunk)]) = ra[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][lds_off(r, lchunk)]) = rb[i];
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int nk = (K + BK - 1) / BK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  const int frag_row = lane & 31;
+  const int frag_half = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int chunk = kk * 2 + frag_half;
+      bf16x8_t af[4], bfr[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(
+            &As[buf][lds_off(wm * 128 + mi * 32 + frag_row, chunk)]);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(
+            &Bs[buf][lds_off(wn * 64 + ni * 32 + frag_row, chunk)]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds column (lane & 31), rows (r/4)*8 + (lane/32)*4 + r%4 ----
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + mi * 32 + (r >> 2) * 8 + frag_half * 4 + (r & 3);
+      if (row >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int col = tn * 128 + wn * 32 + frag_row;
+        if (col < N) {
+          const float a = acc[mi][0][r], b = acc[mi][1][r];
+          C[(int64_t)row * ldc + col] = f2bf(silu_f(a) * b);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = tn * BN + wn * 64 + ni * 32 + frag_row;
+          if (col < N) {
+            bf16_t* p = C + (int64_t)row * ldc + col;
+            if constexpr (EPI == EPI_RESIDUAL) {
+              const float g = bf2f(gate[(int64_t)row * ld_gate + col]);
+              *p = f2bf(bf2f(*p) + g * acc[mi][ni][r]);
+            } else {
+              *p = f2bf(acc[mi][ni][r]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(
+    const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
+    const float* __restrict__ B3, int64_t ldb, float* C, int64_t ldc,
+    const float* __restrict__ gate, int64_t ld_gate, int M, int N, int K) {
+  constexpr int T = 64, TK = 16;
+  __shared__ float as[TK][T + 1];
+  __shared__ float bs[TK][T + 1];
+  __shared__ float b3s[TK][T + 1];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
+  float acc[4][4] = {}, acc3[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += TK) {
+    for (int i = threadIdx.x; i < T * TK; i += 256) {
+      const int r = i / TK, c = i % TK;
+      const int gm = m0 + r, gn = n0 + r, gk = k0 + c;
+      as[c][r] = (gm < M && gk < K) ? A[(int64_t)gm * lda + gk] : 0.f;
+      bs[c][r] = (gn < N && gk < K) ? B[(int64_t)gn * ldb + gk] : 0.f;
+      if constexpr (EPI == EPI_SWIGLU) b3s[c][r] = (gn < N && gk < K) ? B3[(int64_t)gn * ldb + gk] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < TK; ++c) {
+      float av[4], bv[4], b3v[4];
+      for (int i = 0; i < 4; ++i) {
+        av[i] = as[c][ty * 4 + i];
+        bv[i] = bs[c][tx * 4 + i];
+        if constexpr (EPI == EPI_SWIGLU) b3v[i] = b3s[c][tx * 4 + i];
+      }
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] += av[i] * bv[j];
+          if constexpr (EPI == EPI_SWIGLU) acc3[i][j] += av[i] * b3v[j];
+        }
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + ty * 4 + i, col = n0 + tx * 4 + j;
+      if (row >= M || col >= N) continue;
+      float* p = C + (int64_t)row * ldc + col;
+      if constexpr (EPI == EPI_SWIGLU) {
+        *p = silu_f(acc[i][j]) * acc3[i][j];
+      } else if constexpr (EPI == EPI_RESIDUAL) {
+        *p = *p + gate[(int64_t)row * ld_gate + col] * acc[i][j];
+      } else {
+        *p = acc[i][j];
+      }
+    }
+}
+
+hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B,
+                       const void* B3, int64_t ldb, void* C, int64_t ldc, const void* gate,
+                       int64_t ld_gate, int64_t M, int N, int K, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (bf16) {
+    const int tiles_m = (int)ceil_div(M, BM);
+    const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : BN);
+    const dim3 grid((unsigned)(tiles_m * tiles_n));
+#define H3_G(E)                                                                               \
+  hipLaunchKernelGGL((gemm_bf16_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, lda, \
+                     (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,                \
+                     (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n)
+    if (epi == EPI_SWIGLU) H3_G(EPI_SWIGLU);
+    else if (epi == EPI_RESIDUAL) H3_G(EPI_RESIDUAL);
+    else H3_G(EPI_STORE);
+#undef H3_G
+  } else {
+    const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(M, 64));
+#define H3_G(E)                                                                         \
+  hipLaunchKernelGGL((gemm_f32_kernel<E>), grid, dim3(256), 0, s, (const float*)A, lda, \
+                     (const float*)B, (const float*)B3, ldb, (float*)C, ldc,            \
+                     (const float*)gate, ld_gate, (int)M, N, K)
+    if (epi == EPI_SWIGLU) H3_G(EPI_SWIGLU);
+    else if (epi == EPI_RESIDUAL) H3_G(EPI_RESIDUAL);
+    else H3_G(EPI_STORE);
+#undef H3_G
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h3

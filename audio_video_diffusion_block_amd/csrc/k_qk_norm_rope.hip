@@ -1,0 +1,132 @@
+// Fused Q/K RMSNorm + RoPE, in place on the q and k regions of a QKV buffer.
+//
+// Why Real-Time MiniMax H3 Serving Requires More Than a Faster DiT, "Key
+// takeaways": Q/K RMSNorm and RoPE are one fused operation, and a rank computes
+// RoPE only for its own rows.
+//
+// HBM-bound pass.  A head row (D values) is owned by D/8 adjacent lanes, 8
+// values (16 bytes of bf16) per lane, so four consecutive head rows of a token
+// are one contiguous 1 KiB wave access.  The sum of squares is reduced across
+// the D/8 lanes with DPP.  A lane always owns the same 4 RoPE pairs; it derives
+// their inverse frequencies once and recomputes cos/sin only when its token
+// changes (each work-group walks a contiguous run of rows, so that happens
+// every 2H/(256/(D/8)) rows).
+#include "h3_common.hpp"
+#include "h3_kernels.hpp"
+
+namespace h3 {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(
+    T* __restrict__ q, int64_t ld_q, T* __restrict__ k, int64_t ld_k, int64_t n_tok, int n_heads,
+    const T* __restrict__ g_q, const T* __restrict__ g_k, const int4* __restrict__ pos, int sec_t,
+    int sec_h, double log2_theta, float eps, int64_t rows_per_block) {
+  constexpr int L = D / 8;          // lanes per head row
+  constexpr int SLOTS = 256 / L;    // head rows in flight per work-group
+  const int lane = threadIdx.x % L;
+  const int slot = threadIdx.x / L;
+
+  // this lane's 4 pairs are pair indices 4*lane .. 4*lane+3 (dims 8*lane .. 8*lane+7)
+  float f_vid[4], f_aud[4];
+  int axis[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 4 * lane + j;
+    int a, jj, width;
+    if (p < sec_t / 2) {
+      a = 0; jj = p; width = sec_t;
+    } else if (p < (sec_t + sec_h) / 2) {
+      a = 1; jj = p - sec_t / 2; width = sec_h;
+    } else {
+      a = 2; jj = p - (sec_t + sec_h) / 2; width = D - sec_t - sec_h;
+    }
+    axis[j] = a;
+    // frequencies in double, rounded once to float
+    f_vid[j] = (float)exp2(-2.0 * jj / width * log2_theta);
+    f_aud[j] = (float)exp2(-2.0 * p / D * log2_theta);
+  }
+  float gq[8], gk[8];
+  Vec8<T>::load(g_q + 8 * lane, gq);
+  Vec8<T>::load(g_k + 8 * lane, gk);
+
+  const int64_t rows_per_tok = 2 * (int64_t)n_heads;
+  const int64_t total = n_tok * rows_per_tok;
+  const int64_t begin = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t end = min(total, begin + rows_per_block);
+
+  int64_t cur_tok = -1;
+  int kind = 2;
+  float cs[4], sn[4];
+  for (int64_t r = begin + slot; r < end; r += SLOTS) {
+    const int64_t tok = r / rows_per_tok;
+    const int rr = (int)(r - tok * rows_per_tok);
+    const bool is_k = rr >= n_heads;
+    const int head = is_k ? rr - n_heads : rr;
+    if (tok != cur_tok) {
+      cur_tok = tok;
+      const int4 p = pos[tok];
+      kind = p.x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pv = axis[j] == 0 ? p.y : (axis[j] == 1 ? p.z : p.w);
+        const float ang = kind == 1 ? (float)p.y * f_aud[j] : (float)pv * f_vid[j];
+        sincosf(ang, &sn[j], &cs[j]);
+      }
+    }
+    if (kind != 0 && kind != 1) continue;  // pad row: untouched
+    T* ptr = (is_k ? k + tok * ld_k : q + tok * ld_q) + (int64_t)head * D + 8 * lane;
+    float v[8];
+    Vec8<T>::load(ptr, v);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+    ss = group_sum<L>(ss);
+    const float rinv = rsqrtf(ss * (1.0f / D) + eps);
+    const float* g = is_k ? gk : gq;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * rinv * g[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = v[2 * j], b = v[2 * j + 1];
+      v[2 * j] = a * cs[j] - b * sn[j];
+      v[2 * j + 1] = a * sn[j] + b * cs[j];
+    }
+    Vec8<T>::store(ptr, v);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t n_tok,
+                            int n_heads, const void* g_q, const void* g_k, const void* pos,
+                            int sec_t, int sec_h, float theta, float eps, hipStream_t s) {
+  constexpr int L = D / 8;
+  constexpr int SLOTS = 256 / L;
+  const int64_t total = n_tok * 2 * (int64_t)n_heads;
+  const int64_t rows_per_block = (int64_t)SLOTS * 16;
+  const int64_t blocks = ceil_div(total, rows_per_block);
+  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (T*)q, ld_q, (T*)k, ld_k, n_tok, n_heads, (const T*)g_q, (const T*)g_k,
+                     (const int4*)pos, sec_t, sec_h, log2((double)theta), eps, rows_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm_rope(bool bf16, int head_dim, void* q, int64_t ld_q, void* k,
+                               int64_t ld_k, int64_t n_tok, int n_heads, const void* g_q,
+                               const void* g_k, const void* pos, int sec_t, int sec_h,
+                               float theta, float eps, hipStream_t s) {
+  if (n_tok == 0) return hipSuccess;
+  if (bf16) {
+    if (head_dim == 128)
+      return launch_qk<bf16_t, 128>(q, ld_q, k, ld_k, n_tok, n_heads, g_q, g_k, pos, sec_t, sec_h,
+                                    theta, eps, s);
+    return launch_qk<bf16_t, 64>(q, ld_q, k, ld_k, n_tok, n_heads, g_q, g_k, pos, sec_t, sec_h,
+                                 theta, eps, s);
+  }
+  if (head_dim == 128)
+    return launch_qk<float, 128>(q, ld_q, k, ld_k, n_tok, n_heads, g_q, g_k, pos, sec_t, sec_h,
+                                 theta, eps, s);
+  return launch_qk<float, 64>(q, ld_q, k, ld_k, n_tok, n_heads, g_q, g_k, pos, sec_t, sec_h,
+                              theta, eps, s);
+}
+
+}  // namespace h3

@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark: one DiT block forward on one GPU's share of a packed audio-video
+sequence (default: the 10 s request at 1344x768, 24 FPS), bf16, on MI355X.
+
+A "step" is one h3_dit_block_forward call (all steps of the block: modulated
+norm, QKV projection, Q/K RMSNorm+RoPE, head-slice exchange copies, varlen
+attention over the full sequence, output projection with gated residual,
+modulated norm, SwiGLU with gated residual) over inputs already resident in
+HBM.  Prints ONE JSON line.
+
+Per-kernel figures (attention TFLOP/s, fused-op GB/s) come from HIP events
+around each C entry point on the stream it is launched on.  The CPU baseline
+is the float64 oracle, timed on this host on a bounded row sample and
+extrapolated by row count.
+
+  python bench.py [--steps K] [--warmup W] [--config share10s|share5s|tiny]
+                  [--no-cpu-baseline] [--only attn|copy|block]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "varlen attn TFLOP/s + fused-op HBM GB/s; DiT-block ms, 10 s shape, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "audio_video_diffusion_block_amd", "csrc", "k_attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="share10s")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", choices=["", "attn", "copy", "block"])
+    ap.add_argument("--op-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workload
+
+def algorithmic_work(wl):
+    """Per-launch algorithmic FLOPs and bytes of every step (each input read once,
+    each output written once; bf16 = 2 bytes)."""
+    n, c, h, d, f = wl.n_loc, wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim
+    hc = wl.head_count if wl.share_mode else h
+    nv = wl.n_valid
+    es = 2
+    mod_rows = n if wl.mod_per_token else 1
+    return {
+        "attn_flop": 4.0 * d * hc * nv * nv,
+        "qkv_flop": 2.0 * n * c * 3 * h * d,
+        "out_flop": 2.0 * n * h * d * c,
+        "w13_flop": 2.0 * n * c * 2 * f,
+        "w2_flop": 2.0 * n * f * c,
+        # modulated norm: read x, shift, scale; write h
+        "modnorm_bytes": es * (2 * n * c + 2 * mod_rows * c),
+        # Q/K RMSNorm + RoPE: read and write q and k (positions: 16 B/token)
+        "qknorm_bytes": es * 2 * 2 * n * h * d + 16 * n,
+    }
+
+
+def make_inputs(wl, seed):
+    import numpy as np
+    import workloads as W
+    t0 = time.time()
+    w = W.block_weights(wl, seed, "bf16")
+    bi = W.block_inputs(wl, seed, "bf16")
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    return w, bi
+
+
+def to_dev(a, dtype=None):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        return t.to("cuda").to(dtype)
+    return t.to("cuda")
+
+
+# ----------------------------------------------------------------- timing
+
+class EventTimer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, stream):
+        import torch
+        self.torch = torch
+        self.stream = stream
+
+    def time(self, fn, reps):
+        torch = self.torch
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(self.stream)
+        for _ in range(reps):
+            fn()
+        e.record(self.stream)
+        e.synchronize()
+        return s.elapsed_time(e) / reps  # ms per call
+
+
+def traffic_record():
+    """HBM bytes per attention launch from committed rocprof counters, if they were
+    taken on the current attention source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("k_attn_sha256") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------- cpu baseline
+
+def cpu_baseline(wl, w, bi, work, attn_rows=2048, local_rows=4096):
+    """The float64 oracle on this host, on a bounded sample of the same workload:
+    attention for `attn_rows` query rows of the head slice against every key
+    (scaled by N / attn_rows), and the row-local steps (modulated norms, QKV
+    projection, Q/K RMSNorm+RoPE, output projection, residuals, SwiGLU) for
+    `local_rows` token rows (scaled by n_loc / local_rows).  Both scalings are
+    exact in work."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    import oracle as O
+    rng = np.random.default_rng(0)
+    hc = wl.head_count if wl.share_mode else wl.n_heads
+    D = wl.head_dim
+    # attention sample
+    if wl.share_mode:
+        qkv = bi.qkv_attn
+        q_all, k_all, v_all = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    else:
+        g = np.random.default_rng(1)
+        q_all, k_all, v_all = (g.standard_normal((wl.n_loc, hc, D)).astype(np.float32) for _ in range(3))
+    qrows = np.sort(rng.choice(wl.n_valid, size=attn_rows, replace=False))
+    t0 = time.perf_counter()
+    O.varlen_attention(q_all[qrows], k_all, v_all, bi.cu_slots, bi.valid_len, q_rows=qrows)
+    t_attn = time.perf_counter() - t0
+    # row-local sample
+    rows = np.sort(rng.choice(wl.n_loc, size=local_rows, replace=False))
+    mod = bi.mod[rows] if bi.mod.shape[0] > 1 else bi.mod
+    H = wl.n_heads
+    t0 = time.perf_counter()
+    h1 = O.modulated_norm(bi.x[rows], mod[:, 0], mod[:, 1], wl.eps_mod)
+    qkv_r = O.linear(h1, w.w_qkv).reshape(len(rows), 3, H, D)
+    O.qk_norm_rope(qkv_r[:, 0], qkv_r[:, 1], bi.pos[rows], w.g_q, w.g_k, wl.sections, wl.theta, wl.eps_qk)
+    o = bi.o_local[rows].reshape(len(rows), -1) if bi.o_local is not None else qkv_r[:, 2].reshape(len(rows), -1)
+    x1 = O.gated_residual(bi.x[rows], mod[:, 2], O.linear(o, w.w_o))
+    h2 = O.modulated_norm(x1, mod[:, 3], mod[:, 4], wl.eps_mod)
+    O.gated_residual(x1, mod[:, 5], O.swiglu_mlp(h2, w.w1, w.w3, w.w2))
+    t_local = time.perf_counter() - t0
+    full_s = t_attn * wl.n_valid / attn_rows + t_local * wl.n_loc / local_rows
+    flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
+    log(f"oracle: attention {attn_rows} rows {t_attn:.1f}s, row-local {local_rows} rows {t_local:.1f}s, "
+        f"full block extrapolated {full_s:.0f}s")
+    return {"value": flop / full_s / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 numpy oracle: attention for {attn_rows} query rows x {hc} heads against "
+                       f"all {wl.n_valid} keys ({t_attn:.1f}s, scaled by N/{attn_rows}) + row-local steps "
+                       f"for {local_rows} of {wl.n_loc} token rows ({t_local:.1f}s, scaled by "
+                       f"n_loc/{local_rows}); extrapolated full block {full_s:.0f}s")}
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the "
+                                   "sequence-parallel sharding across GPUs is a design, not built)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import audio_video_diffusion_block_amd as h3
+    import workloads as W
+
+    wl = W.PRESETS[args.config]
+    bf = torch.bfloat16
+    stream = torch.cuda.current_stream()
+    timer = EventTimer(stream)
+
+    if args.only == "copy":
+        # plain copy of known size: calibration of the HBM byte counters
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 2, dtype=bf, device="cuda").normal_()
+        b = torch.empty_like(a)
+        for _ in range(2):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        ms = timer.time(lambda: b.copy_(a), 3)
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": ms,
+                          "GB/s": 2 * nbytes / ms / 1e6}))
+        return
+
+    work = algorithmic_work(wl)
+    w, bi = make_inputs(wl, args.seed)
+    t0 = time.time()
+    wd = {k: to_dev(getattr(w, k), bf) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")}
+    x0 = to_dev(bi.x, bf)
+    x = x0.clone()
+    mod = to_dev(bi.mod, bf)
+    pos = to_dev(bi.pos)
+    cu = to_dev(bi.cu_slots)
+    vl = to_dev(bi.valid_len)
+    max_len = int(bi.valid_len.max())
+    cfg = h3.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
+                          wl.eps_qk, wl.eps_mod, 0, bf)
+    share = {}
+    H, D, C = wl.n_heads, wl.head_dim, wl.dim
+    hc = wl.head_count if wl.share_mode else H
+    if wl.share_mode:
+        share = dict(qkv_attn=to_dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), bf),
+                     o_attn=torch.zeros((wl.n_pad_total, hc * D), dtype=bf, device="cuda"),
+                     o_local=to_dev(bi.o_local.reshape(wl.n_loc, -1), bf),
+                     tok_begin=wl.tok_begin, head_begin=wl.head_begin, head_count=hc)
+    n_buf = wl.n_pad_total if wl.share_mode else wl.n_loc
+    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, n_buf, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"uploaded in {time.time() - t0:.1f}s; workspace {ws.numel() / 2**30:.2f} GiB")
+
+    def block():
+        h3.h3_dit_block_forward(cfg, wd, x, mod, pos, cu, vl, max_len, ws=ws, **share)
+
+    # attention alone, as the block launches it (head slice over the whole buffer)
+    if wl.share_mode:
+        qa = share["qkv_attn"]
+        q_v, k_v, v_v = qa[:, :hc * D], qa[:, hc * D:2 * hc * D], qa[:, 2 * hc * D:]
+        o_v = share["o_attn"]
+    else:
+        qkv_t = torch.randn((wl.n_loc, 3 * H * D), dtype=bf, device="cuda")
+        q_v, k_v, v_v = qkv_t[:, :H * D], qkv_t[:, H * D:2 * H * D], qkv_t[:, 2 * H * D:]
+        o_v = torch.empty((wl.n_loc, H * D), dtype=bf, device="cuda")
+    attn_ws = torch.empty(max(h3.varlen_attn_workspace_size(n_buf, hc, D, 1, bf), 16), dtype=torch.uint8,
+                          device="cuda")
+
+    def attn():
+        h3.h3_varlen_attn(q_v, k_v, v_v, o_v, hc, D, cu, vl, max_len, ws=attn_ws)
+
+    if args.only == "attn":
+        for _ in range(args.warmup):
+            attn()
+        torch.cuda.synchronize()
+        ms = timer.time(attn, max(args.steps, 1))
+        print(json.dumps({"attn_ms": ms, "attn_tflops": work["attn_flop"] / ms / 1e9}))
+        return
+
+    # ---- timed block steps
+    log(f"warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        block()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    step_ms = timer.time(block, args.steps)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    log(f"block {step_ms:.2f} ms/step (wall {wall_ms:.2f})")
+
+    # ---- per-step breakdown: each C entry alone, HIP events on the launch stream
+    reps = args.op_reps
+    h1 = torch.empty((wl.n_loc, C), dtype=bf, device="cuda")
+    qkv = torch.empty((wl.n_loc, 3 * H * D), dtype=bf, device="cuda")
+    xs = x0.clone()
+    ops = {}
+    ops["modnorm"] = timer.time(lambda: h3.h3_modulate_residual(
+        xs, shift=mod[:, 0], scale=mod[:, 1], h_out=h1), reps)
+    ops["qkv_gemm"] = timer.time(lambda: h3.h3_linear(h1, wd["w_qkv"], qkv), reps)
+    ops["qk_norm_rope"] = timer.time(lambda: h3.h3_qk_norm_rope(
+        qkv[:, :H * D], qkv[:, H * D:2 * H * D], H, D, wd["g_q"], wd["g_k"], pos, wl.sections,
+        wl.theta, wl.eps_qk), reps)
+    ops["attention"] = timer.time(attn, reps)
+    o_in = share["o_local"] if wl.share_mode else o_v
+    ops["out_gemm_residual"] = timer.time(lambda: h3.h3_linear(o_in, wd["w_o"], xs, gate=mod[:, 2]), reps)
+    sw_ws = torch.empty(h3.swiglu_workspace_size(wl.n_loc, wl.ffn_dim, bf), dtype=torch.uint8, device="cuda")
+    ops["swiglu_residual"] = timer.time(lambda: h3.h3_swiglu(
+        h1, wd["w1"], wd["w3"], wd["w2"], xs, gate=mod[:, 5], ws=sw_ws), reps)
+    torch.cuda.synchronize()
+    attn_ms = ops["attention"]
+    attn_tflops = work["attn_flop"] / attn_ms / 1e9
+    breakdown = {
+        "attention": {"ms": attn_ms, "TFLOP/s": attn_tflops, "frac_peak": attn_tflops / BF16_PEAK_TFLOPS},
+        "qkv_gemm": {"ms": ops["qkv_gemm"], "TFLOP/s": work["qkv_flop"] / ops["qkv_gemm"] / 1e9},
+        "out_gemm_residual": {"ms": ops["out_gemm_residual"],
+                              "TFLOP/s": work["out_flop"] / ops["out_gemm_residual"] / 1e9},
+        "swiglu_residual": {"ms": ops["swiglu_residual"],
+                            "TFLOP/s": (work["w13_flop"] + work["w2_flop"]) / ops["swiglu_residual"] / 1e9},
+        "modnorm": {"ms": ops["modnorm"], "GB/s": work["modnorm_bytes"] / ops["modnorm"] / 1e6,
+                    "frac_hbm": work["modnorm_bytes"] / ops["modnorm"] / 1e6 / HBM_PEAK_GBS},
+        "qk_norm_rope": {"ms": ops["qk_norm_rope"], "GB/s": work["qknorm_bytes"] / ops["qk_norm_rope"] / 1e6,
+                         "frac_hbm": work["qknorm_bytes"] / ops["qk_norm_rope"] / 1e6 / HBM_PEAK_GBS},
+    }
+    total_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
+    value = total_flop / step_ms / 1e9  # TFLOP/s of the whole block
+
+    traffic = traffic_record()
+    roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
+                "kernel": "attn_fwd_bf16_kernel<128,4> (+ V transpose pass)",
+                "algorithmic_flop_per_launch": work["attn_flop"]}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: one DiT block, rank {wl.rank} of {wl.sp_degree} share "
+                               f"(n_loc={wl.n_loc} tokens x C={C}; attention over N={wl.n_valid} "
+                               f"valid tokens, heads {wl.head_begin}-{wl.head_begin + hc - 1} of {H} x {D})",
+                   "n_valid": wl.n_valid, "n_loc": wl.n_loc, "dim": C, "heads": H, "head_dim": D,
+                   "ffn_dim": wl.ffn_dim, "head_slice": hc, "parallelism": "1 GPU (rank-share stand-in)"},
+        "block_ms": step_ms, "attn_tflops": attn_tflops,
+        "fused_op_gbps": {k: breakdown[k]["GB/s"] for k in ("modnorm", "qk_norm_rope")},
+        "breakdown": breakdown, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, w, bi, work)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,274 @@
+/*
+ * h3dit -- one DiT block forward on a packed audio-video token sequence, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Page titles cited (abbreviated):
+ *   [RT-H3]  "Why Real-Time MiniMax H3 Serving Requires More Than a Faster DiT"
+ *   [FH3-zh] "MiniMax H3 通过 vLLM-Omni 实现 FastH3 实时推理"
+ *
+ * The block: modulated norm -> QKV projection -> Q/K RMSNorm + RoPE ->
+ * attention over each segment's valid rows -> output projection -> gated
+ * residual -> modulated norm -> SwiGLU MLP -> gated residual.  The pages name
+ * the packed sequence with valid lengths and no structural suffix padding,
+ * rank-local RoPE rows, and the fused Q/K RMSNorm+RoPE, modulation/norm,
+ * residual and SwiGLU operations ([RT-H3] Key takeaways; [FH3-zh]
+ * vLLM-Omni 中的系统级优化).  Widths, norm kinds and layouts below are the
+ * plain readings of pages that give no model code.
+ *
+ * Conventions for every entry point
+ *  - Memory: every tensor argument is a DEVICE pointer unless marked "host".
+ *    The caller allocates and owns all buffers and the stream; the library
+ *    never allocates, frees or synchronises, and keeps no pointer after the
+ *    call returns.  Scratch memory comes from the caller as `ws`/`ws_bytes`,
+ *    sized by the matching *_workspace_size() query.
+ *  - Layout: row-major.  `ld_*` arguments are row strides in ELEMENTS.  Every
+ *    tensor pointer must be 16-byte aligned and every row stride times the
+ *    element size a multiple of 16 bytes.
+ *  - Types: storage is H3_F32 or H3_BF16 (all tensors of one call share it);
+ *    accumulation is always fp32; outputs are rounded to nearest even.
+ *    Position and offset tables are int32.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  All work
+ *    is enqueued asynchronously on it, in order.
+ *  - Errors: arguments are checked on the host before anything is enqueued; on
+ *    any error nothing is launched and a status != H3_OK is returned, with a
+ *    description in h3_last_error() (thread-local).  Faults inside kernels
+ *    surface, as HIP reports them, at the caller's next synchronisation.
+ *  - Determinism: no atomics and a fixed reduction order; identical inputs give
+ *    byte-identical outputs run after run (the pages observe byte-identical
+ *    output for a fixed seed, [FH3-zh] 质量与兼容性说明).
+ */
+#ifndef H3DIT_H
+#define H3DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3_ABI_VERSION 1
+
+typedef enum {
+  H3_OK = 0,
+  H3_ERR_ARG = 1,          /* bad pointer, size, stride, alignment or layout */
+  H3_ERR_UNSUPPORTED = 2,  /* dtype, head_dim or device not supported (gfx950 only) */
+  H3_ERR_WORKSPACE = 3,    /* ws_bytes below the size the query returns */
+  H3_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} h3_status;
+
+typedef enum { H3_F32 = 0, H3_BF16 = 1 } h3_dtype;
+
+/* Token kinds of the position table. */
+enum { H3_POS_VIDEO = 0, H3_POS_AUDIO = 1, H3_POS_PAD = 2 };
+
+/* One token's RoPE position: video tokens use (t, h, w); audio tokens use t as
+ * their audio index; pad tokens are left untouched by h3_qk_norm_rope. */
+typedef struct {
+  int32_t kind;
+  int32_t t;
+  int32_t h;
+  int32_t w;
+} h3_pos;
+
+/* Library ABI version (H3_ABI_VERSION of the build). */
+int h3_abi_version(void);
+/* Static text for a status code. */
+const char* h3_status_string(h3_status st);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* h3_last_error(void);
+
+/*
+ * h3_qk_norm_rope -- in place, per (token, head): q <- RoPE(RMSNorm(q) * g_q),
+ * k <- RoPE(RMSNorm(k) * g_k).  ([RT-H3] Key takeaways: fused Q/K RMSNorm
+ * with RoPE; rank-local RoPE rows.)
+ *   q, k      [n_tok rows] x [n_heads * head_dim], row strides ld_q, ld_k; heads
+ *             contiguous at stride head_dim inside a row (e.g. the q and k
+ *             thirds of a [n_tok, 3, H, D] QKV buffer, ld = 3*H*D).
+ *   g_q, g_k  [head_dim] gains shared by all heads.
+ *   pos       [n_tok] positions of exactly these rows (rank-local rows only).
+ *   RMSNorm:  x / sqrt(mean(x^2) + eps) over one head's head_dim values.
+ *   RoPE:     adjacent pairs (2j, 2j+1) turn by angle phi:
+ *             (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi).
+ *             Video: the head row is cut into sections [sec_t | sec_h | sec_w];
+ *             pair j of a section of width d at position p turns by
+ *             p * theta^(-2j/d).  Audio: one section of width head_dim at
+ *             position t.  Pad rows: untouched (no norm either).
+ *   Requires head_dim in {64, 128}; sec_* even, >= 0, summing to head_dim.
+ *   n_tok == 0 is a no-op.
+ */
+h3_status h3_qk_norm_rope(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t n_tok,
+                          int32_t n_heads, int32_t head_dim, const void* g_q, const void* g_k,
+                          const h3_pos* pos, int32_t sec_t, int32_t sec_h, int32_t sec_w,
+                          float theta, float eps, h3_dtype dtype, void* stream);
+
+/*
+ * h3_varlen_attn -- softmax attention over a packed buffer of segments, valid
+ * rows only ([RT-H3] Key takeaways: valid sequence lengths, structural suffix
+ * padding removed).
+ *   q, k, v, o  [n_buf rows] x [n_heads * head_dim], row strides ld_*.
+ *   cu_slots    device int32 [n_seg + 1]: segment s owns rows
+ *               [cu_slots[s], cu_slots[s+1]), non-decreasing, 0 <= .. <= n_buf.
+ *   valid_len   device int32 [n_seg]: the first valid_len[s] rows of slot s are
+ *               valid (0 <= valid_len[s] <= slot length); NULL = whole slots.
+ *   max_valid_len  host: an upper bound of max(valid_len) (sizes the grid).
+ *   For each valid row i of segment s and each head:
+ *     o_i = sum_j softmax_j(q_i . k_j * softmax_scale) v_j over valid rows j of s.
+ *   Every other row of o (suffix pad, rows outside all slots) is written as 0.
+ *   Pad rows of q, k, v are never read into the result (they may hold NaN/Inf).
+ *   softmax_scale <= 0 means 1/sqrt(head_dim).  Bidirectional, no cross-segment
+ *   attention.  head_dim in {64, 128}.
+ *   ws: scratch of h3_varlen_attn_workspace_size(n_buf, n_heads, head_dim,
+ *   n_seg, dtype) bytes (a transposed copy of v).
+ */
+size_t h3_varlen_attn_workspace_size(int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                     int32_t n_seg, h3_dtype dtype);
+h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                         const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
+                         int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
+                         const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
+                         float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
+                         void* stream);
+
+/*
+ * h3_modulate_residual -- one pass over rows of width dim:
+ *   if y != NULL:     x <- x + gate * y                       (gated residual)
+ *   if h_out != NULL: h_out <- norm(x) * (1 + scale) + shift  (modulated norm)
+ * ([RT-H3] Key takeaways: modulation, normalisation and residual updates fused.)
+ *   x       [n_tok, dim] in/out, stride ld_x.   y [n_tok, dim], stride ld_y.
+ *   gate, shift, scale  rows of stride ld_mod; ld_mod == 0 broadcasts row 0 to
+ *           every token.  gate is required iff y != NULL; shift and scale iff
+ *           h_out != NULL.
+ *   norm_kind 0: LayerNorm without affine, biased variance, eps inside the
+ *           square root; 1: RMSNorm.
+ *   The norm sees the updated x in fp32 (before its rounding to storage).
+ *   dim must be a multiple of 8 and at most 16384.
+ */
+h3_status h3_modulate_residual(void* x, int64_t ld_x, const void* y, int64_t ld_y,
+                               const void* gate, const void* shift, const void* scale,
+                               int64_t ld_mod, void* h_out, int64_t ld_h, int64_t n_tok,
+                               int32_t dim, int32_t norm_kind, float eps, h3_dtype dtype,
+                               void* stream);
+
+/*
+ * h3_linear -- out = a @ w^T (w stored [n_out, k_in], no bias); if gate != NULL
+ * the result is instead added as a gated residual: out <- out + gate * (a @ w^T).
+ * The QKV and output projections of the block.
+ *   a [m, k_in] stride lda; w [n_out, k_in] stride ldw; out [m, n_out] stride
+ *   ld_out; gate rows of stride ld_gate (0 = broadcast).  k_in % 8 == 0.
+ */
+h3_status h3_linear(const void* a, int64_t lda, const void* w, int64_t ldw, void* out,
+                    int64_t ld_out, int64_t m, int32_t n_out, int32_t k_in, const void* gate,
+                    int64_t ld_gate, h3_dtype dtype, void* stream);
+
+/*
+ * h3_swiglu -- SwiGLU MLP ([RT-H3] Key takeaways: SwiGLU fused):
+ *   g = silu(h @ w1^T) * (h @ w3^T)    (silu(a) = a / (1 + e^-a); one GEMM
+ *                                        pass with the gate in its epilogue)
+ *   y = g @ w2^T
+ *   gate == NULL: out <- y;  else out <- out + gate * y (gated residual, in place).
+ *   h [n_tok, dim] stride ld_h; w1, w3 [ffn_dim, dim]; w2 [dim, ffn_dim];
+ *   out [n_tok, dim] stride ld_out; gate rows of stride ld_gate (0 = broadcast).
+ *   ws: h3_swiglu_workspace_size(n_tok, ffn_dim, dtype) bytes (holds g).
+ *   dim % 8 == 0, ffn_dim % 8 == 0.
+ */
+size_t h3_swiglu_workspace_size(int64_t n_tok, int32_t ffn_dim, h3_dtype dtype);
+h3_status h3_swiglu(const void* h, int64_t ld_h, const void* w1, const void* w3,
+                    const void* w2, void* out, int64_t ld_out, const void* gate,
+                    int64_t ld_gate, int64_t n_tok, int32_t dim, int32_t ffn_dim, void* ws,
+                    size_t ws_bytes, h3_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------ whole block */
+
+typedef struct {
+  int32_t dim;        /* C */
+  int32_t n_heads;    /* H */
+  int32_t head_dim;   /* D, 64 or 128 */
+  int32_t ffn_dim;    /* F */
+  int32_t sec_t, sec_h, sec_w;  /* RoPE sections of a head row (video) */
+  float theta;        /* RoPE base */
+  float eps_qk;       /* Q/K RMSNorm epsilon */
+  float eps_mod;      /* modulated-norm epsilon */
+  int32_t norm_kind;  /* 0 LayerNorm, 1 RMSNorm (modulated norms) */
+  h3_dtype dtype;
+} h3_block_config;
+
+typedef struct {
+  const void* w_qkv;  /* [3*H*D, C]: rows q heads 0..H-1, then k heads, then v heads */
+  const void* w_o;    /* [C, H*D] */
+  const void* w1;     /* [F, C] (silu branch) */
+  const void* w3;     /* [F, C] (linear branch) */
+  const void* w2;     /* [C, F] */
+  const void* g_q;    /* [D] */
+  const void* g_k;    /* [D] */
+} h3_block_weights;
+
+typedef struct {
+  void* x;              /* [n_tok_local, C] residual stream, updated in place */
+  int64_t ld_x;
+  const void* mod;      /* [rows, 6, C]: shift1, scale1, gate1, shift2, scale2, gate2 */
+  int64_t ld_mod;       /* elements between token rows (6*C), or 0 = one row for all */
+  const h3_pos* pos;    /* [n_tok_local] positions of the local rows */
+  const int32_t* cu_slots;   /* device [n_seg+1] over the attention buffer rows */
+  const int32_t* valid_len;  /* device [n_seg] (NULL = whole slots) */
+  int32_t n_seg;
+  int32_t max_valid_len;     /* host bound of max(valid_len) */
+  int64_t n_tok_local;  /* this GPU's token rows */
+  int64_t n_buf;        /* attention buffer rows (world 1: n_tok_local) */
+  int64_t tok_begin;    /* attention-buffer row of local token 0 (world 1: 0) */
+  int32_t head_begin;   /* first head of this GPU's attention slice (world 1: 0) */
+  int32_t head_count;   /* heads in the slice (world 1: H) */
+  /* Rank-share mode only (all NULL in world 1).  The sequence-parallel
+   * exchange around attention ([RT-H3] Key takeaways: all-to-all around
+   * attention) is outside this library: the caller provides its buffers with
+   * the other ranks' rows and heads already in place. */
+  void* qkv_attn;       /* [n_buf, 3, head_count, D]; rows [tok_begin, +n_tok_local) are written */
+  void* o_attn;         /* [n_buf, head_count, D]; written by attention */
+  void* o_local;        /* [n_tok_local, H, D]; heads [head_begin, +head_count) are written */
+} h3_block_io;
+
+/*
+ * h3_dit_block_forward -- one block on one GPU, all steps enqueued on `stream`:
+ *   h1 = norm(x)(1+scale1)+shift1;  qkv = h1 w_qkv^T;  Q/K RMSNorm+RoPE (local rows);
+ *   attention over cu_slots/valid_len (world 1: reads qkv in place; rank share:
+ *   the local head slice is copied into qkv_attn rows first, attention runs on
+ *   qkv_attn and its local rows are copied into o_local);
+ *   x <- x + gate1 * (o w_o^T);  h2 = norm(x)(1+scale2)+shift2;
+ *   x <- x + gate2 * (silu(h2 w1^T) * (h2 w3^T)) w2^T.
+ * World 1: qkv_attn == NULL, tok_begin == 0, n_buf == n_tok_local, head_count == H.
+ */
+size_t h3_dit_block_workspace_size(const h3_block_config* cfg, int64_t n_tok_local,
+                                   int64_t n_buf, int32_t n_seg);
+h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weights* w,
+                               const h3_block_io* io, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------ student loop glue */
+
+/*
+ * h3_timestep_modulation -- per-block modulation at noise level sigma for the
+ * four-forward student ([FH3-zh] FastH3：四步学生模型: four forwards over five
+ * sigma positions).  The pages give no embedding; this is the common
+ * sinusoidal one:
+ *   e = [cos(1000 sigma w_j) || sin(1000 sigma w_j)], w_j = 10000^(-j/(E/2)), j < E/2
+ *   t = w_t2 @ silu(w_t1 @ e)                  (w_t1 [C, E], w_t2 [6C, C])
+ *   mod_out[b] = t (as [6, C]) + table[b]      (table, mod_out [n_blocks, 6, C])
+ * emb_dim E even, <= 1024.  ws: h3_timestep_workspace_size(dim) bytes.
+ */
+size_t h3_timestep_workspace_size(int32_t dim);
+h3_status h3_timestep_modulation(float sigma, const void* w_t1, const void* w_t2,
+                                 const void* table, void* mod_out, int32_t n_blocks,
+                                 int32_t dim, int32_t emb_dim, void* ws, size_t ws_bytes,
+                                 h3_dtype dtype, void* stream);
+
+/*
+ * h3_euler_update -- z <- z + (sigma_to - sigma_from) * u over n elements, then,
+ * if x_next != NULL, x_next <- z (the next forward's input).  u may alias x_next.
+ */
+h3_status h3_euler_update(void* z, const void* u, void* x_next, int64_t n, float sigma_from,
+                          float sigma_to, h3_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3DIT_H */

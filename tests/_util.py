@@ -1,0 +1,43 @@
+"""Helpers shared by the GPU parity tests (no arithmetic of the method here)."""
+import numpy as np
+import torch
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+# bf16 outputs: the stated bound (max-abs 2e-2, mean-abs 2e-3) plus a relative
+# L2 bound; fp32 outputs: max-abs 1e-4, mean-abs 1e-5.
+TOL = {"bf16": dict(max_abs=2e-2, mean_abs=2e-3, rel_l2=1e-2),
+       "f32": dict(max_abs=1e-4, mean_abs=1e-5, rel_l2=1e-5)}
+
+
+def dev(a, dtype: str, device="cuda"):
+    """float32 numpy values (already representable in `dtype`) -> device tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device=device, dtype=TORCH_DT[dtype])
+
+
+def dev_i32(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = np.abs(got - ref)
+    return dict(max_abs=float(d.max()) if d.size else 0.0, mean_abs=float(d.mean()) if d.size else 0.0,
+                rel_l2=float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)))
+
+
+def assert_close(got, ref, dtype: str, what: str = "", **override):
+    tol = dict(TOL[dtype])
+    tol.update(override)
+    e = errors(got, ref)
+    assert np.isfinite(np.asarray(got)).all(), f"{what}: non-finite output"
+    bad = {k: (e[k], tol[k]) for k in tol if e[k] > tol[k]}
+    print(f"[{what}] {dtype} " + " ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+    assert not bad, f"{what}: {bad}"
+    return e

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects
+bad arguments on the host before touching the GPU (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3dit.h")
+LIB = os.path.join(ROOT, "audio_video_diffusion_block_amd", "libh3dit.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libh3dit.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_block_boundary():
+    syms = declared_symbols()
+    for s in ("h3_qk_norm_rope", "h3_varlen_attn", "h3_modulate_residual", "h3_swiglu",
+              "h3_dit_block_forward", "h3_abi_version", "h3_status_string", "h3_last_error"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+    import audio_video_diffusion_block_amd as h3
+    assert set(declared_symbols()) == set(h3.EXPORTED)
+    assert h3.abi_version() == 1
+
+
+def test_status_strings():
+    import audio_video_diffusion_block_amd as h3
+    assert h3._status_string(0) == "ok"
+    assert "workspace" in h3._status_string(3)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails before any launch
+
+
+def _qk(h3, **kw):
+    a = dict(q=FAKE, ld_q=3 * 512, k=FAKE, ld_k=3 * 512, n=10, H=4, D=128, gq=FAKE, gk=FAKE,
+             pos=FAKE, st=32, sh=48, sw=48, theta=1e4, eps=1e-6, dt=1)
+    a.update(kw)
+    return h3._c_qk(a["q"], a["ld_q"], a["k"], a["ld_k"], a["n"], a["H"], a["D"], a["gq"], a["gk"],
+                    a["pos"], a["st"], a["sh"], a["sw"], a["theta"], a["eps"], a["dt"], None)
+
+
+def test_qk_norm_rope_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    assert _qk(h3, q=None) == h3.H3_ERR_ARG and "q is NULL" in h3.last_error()
+    assert _qk(h3, D=96) == h3.H3_ERR_UNSUPPORTED
+    assert _qk(h3, st=30) == h3.H3_ERR_ARG and "sum" in h3.last_error()
+    assert _qk(h3, st=31, sh=49) == h3.H3_ERR_ARG and "even" in h3.last_error()
+    assert _qk(h3, q=FAKE + 8) == h3.H3_ERR_ARG and "aligned" in h3.last_error()
+    assert _qk(h3, ld_q=100) == h3.H3_ERR_ARG
+    assert _qk(h3, ld_q=512 + 4) == h3.H3_ERR_ARG and "16 bytes" in h3.last_error()
+    assert _qk(h3, dt=7) == h3.H3_ERR_UNSUPPORTED
+    assert _qk(h3, n=0, q=None, k=None) == h3.H3_OK  # empty call: nothing to do
+
+
+def test_attention_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    ws_need = h3._c_attn_ws(8192, 8, 128, 3, 1)
+    assert ws_need >= 8 * 128 * 8192 * 2
+
+    def call(**kw):
+        a = dict(n_buf=8192, H=8, D=128, cu=FAKE, n_seg=3, max_len=4032, ws=FAKE, ws_bytes=ws_need)
+        a.update(kw)
+        return h3._c_attn(FAKE, 1024, FAKE, 1024, FAKE, 1024, FAKE, 1024, a["n_buf"], a["H"], a["D"],
+                          a["cu"], None, a["n_seg"], a["max_len"], 0.0, a["ws"], a["ws_bytes"], 1, None)
+
+    assert call(ws_bytes=ws_need - 1) == h3.H3_ERR_WORKSPACE
+    assert call(cu=None) == h3.H3_ERR_ARG
+    assert call(n_seg=0) == h3.H3_ERR_ARG
+    assert call(max_len=9000) == h3.H3_ERR_ARG
+    assert call(D=80) == h3.H3_ERR_UNSUPPORTED
+    assert call(ws=None) == h3.H3_ERR_ARG
+
+
+def test_modres_and_linear_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    st = h3._c_modres(FAKE, 5120, None, 0, None, None, None, 0, None, 0, 4, 5120, 0, 1e-6, 1, None)
+    assert st == h3.H3_ERR_ARG and "nothing to do" in h3.last_error()
+    st = h3._c_modres(FAKE, 5120, None, 0, None, FAKE, FAKE, 6 * 5120, FAKE, 5120, 4, 5124, 0, 1e-6, 1, None)
+    assert st == h3.H3_ERR_ARG
+    st = h3._c_modres(FAKE, 5120, FAKE, 5120, None, None, None, 0, None, 0, 4, 5120, 0, 1e-6, 1, None)
+    assert st == h3.H3_ERR_ARG and "gate" in h3.last_error()
+    st = h3._c_linear(FAKE, 100, FAKE, 100, FAKE, 64, 10, 64, 100, None, 0, 1, None)
+    assert st == h3.H3_ERR_ARG  # k_in not a multiple of 8
+    st = h3._c_swiglu(FAKE, 256, FAKE, FAKE, FAKE, FAKE, 256, None, 0, 10, 256, 704, FAKE, 16, 1, None)
+    assert st == h3.H3_ERR_WORKSPACE
+
+
+def test_block_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    cfg = h3.block_config(256, 4, 64, 704, (16, 24, 24))
+    need = h3.block_workspace_size(cfg, 480, 480, 1)
+    assert need > 480 * (256 + 768 + 704) * 2
+    w = h3.BlockWeights(*([FAKE] * 7))
+    io = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 480, 0, 0, 4, None, None, None)
+    st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), FAKE, need - 256, None)
+    assert st == h3.H3_ERR_WORKSPACE
+    bad = h3.block_config(256, 4, 64, 704, (16, 24, 26))
+    st = h3._c_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(io), FAKE, need, None)
+    assert st == h3.H3_ERR_ARG
+    io2 = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 512, 0, 0, 4, None, None, None)
+    st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io2), FAKE, need, None)
+    assert st == h3.H3_ERR_ARG and "world-1" in h3.last_error()
+    io3 = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 120, 480, 400, 3, 1, FAKE, FAKE, FAKE)
+    st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io3), FAKE, need, None)
+    assert st == h3.H3_ERR_ARG and "local rows" in h3.last_error()

@@ -1,0 +1,203 @@
+"""Per-kernel parity of the HIP path against the float64 oracle (GPU).
+
+Inputs come from the seeded generators in ``workloads``; expected values come
+from ``oracle`` only.  Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from _util import assert_close, dev, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------- qk_norm_rope
+
+def _qk_case(wl, dtype, seed, n_rows=None):
+    pos = W.positions(wl)
+    if n_rows is not None:  # a contiguous window that holds video, audio and pad rows
+        lo = max(0, len(pos) - n_rows)
+        pos = pos[lo:]
+    n = len(pos)
+    hd = wl.n_heads * wl.head_dim
+    qkv = W.as_dtype_values(W.normal(seed, "qkv_rows", (n, 3 * hd)) * 1.7, dtype)
+    gq = W.as_dtype_values(W.normal(seed, "gq", (wl.head_dim,), std=0.02, mean=1.0), dtype)
+    gk = W.as_dtype_values(W.normal(seed, "gk", (wl.head_dim,), std=0.02, mean=1.0), dtype)
+    return pos, qkv, gq, gk
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", ["tiny", "tiny_pad", "h40d128"])
+def test_qk_norm_rope_parity(lib, dtype, shape):
+    if shape == "tiny":
+        wl, rows = W.TINY, None
+    elif shape == "tiny_pad":
+        wl, rows = W.TINY.replace(pad_to=520), None
+    else:  # the 10 s share's head layout on the tail of the sequence (video, audio, pad rows)
+        wl, rows = W.SHARE_10S, 3000
+    pos, qkv, gq, gk = _qk_case(wl, dtype, seed=11, n_rows=rows)
+    H, D = wl.n_heads, wl.head_dim
+    hd = H * D
+    t = dev(qkv, dtype)
+    lib.h3_qk_norm_rope(t[:, :hd], t[:, hd:2 * hd], H, D, dev(gq, dtype), dev(gk, dtype),
+                        dev_i32(pos), wl.sections, wl.theta, wl.eps_qk)
+    torch.cuda.synchronize()
+    got = host(t)
+    n = len(pos)
+    q = qkv[:, :hd].reshape(n, H, D)
+    k = qkv[:, hd:2 * hd].reshape(n, H, D)
+    rq, rk = O.qk_norm_rope(q, k, pos, gq, gk, wl.sections, wl.theta, wl.eps_qk)
+    assert_close(got[:, :hd], rq.reshape(n, hd), dtype, "q")
+    assert_close(got[:, hd:2 * hd], rk.reshape(n, hd), dtype, "k")
+    # v untouched bit for bit; pad rows untouched bit for bit
+    assert np.array_equal(got[:, 2 * hd:], qkv[:, 2 * hd:].astype(np.float64))
+    pad = pos[:, 0] == W.POS_PAD
+    assert np.array_equal(got[pad], qkv[pad].astype(np.float64))
+
+
+# ----------------------------------------------------------- modulate/residual
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dim,n,mode", [(256, 480, "per_token"), (5120, 777, "per_token"),
+                                        (5120, 300, "broadcast"), (1024, 65, "rms")])
+def test_modulate_residual_parity(lib, dtype, dim, n, mode):
+    seed = 3
+    x = W.as_dtype_values(W.normal(seed, "x", (n, dim)) * 1.3 + 0.2, dtype)
+    y = W.as_dtype_values(W.normal(seed, "y", (n, dim)), dtype)
+    rows = 1 if mode == "broadcast" else n
+    mod = W.as_dtype_values(W.normal(seed, "mod", (rows, 6, dim), std=0.1), dtype)
+    kind = 1 if mode == "rms" else 0
+    xt, yt, mt = dev(x, dtype), dev(y, dtype), dev(mod, dtype)
+    ht = torch.empty_like(xt)
+    # residual + norm in one pass (slots: gate 2, shift 3, scale 4)
+    lib.h3_modulate_residual(xt, y=yt, gate=mt[:, 2], shift=mt[:, 3], scale=mt[:, 4], h_out=ht,
+                             norm_kind=kind)
+    torch.cuda.synchronize()
+    x1 = O.gated_residual(x, mod[:, 2], y)
+    h = O.modulated_norm(x1, mod[:, 3], mod[:, 4], 1e-6, "rms" if kind else "layer")
+    assert_close(host(xt), x1, dtype, "x+gate*y")
+    assert_close(host(ht), h, dtype, "modnorm")
+    # norm only (residual off): x must stay bit-identical
+    x0 = host(xt).copy()
+    lib.h3_modulate_residual(xt, shift=mt[:, 0], scale=mt[:, 1], h_out=ht, norm_kind=kind)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(xt), x0)
+    h = O.modulated_norm(x0, mod[:, 0], mod[:, 1], 1e-6, "rms" if kind else "layer")
+    assert_close(host(ht), h, dtype, "modnorm-only")
+
+
+# -------------------------------------------------------------------- GEMMs
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m,n,k", [(480, 768, 256), (1000, 1408, 704), (257, 304, 136),
+                                   (513, 5120, 1024)])
+def test_linear_parity(lib, dtype, m, n, k):
+    """Unit-scale operands (weights std 1/sqrt(k)) so outputs are O(1), like the block's;
+    ragged M, N and K tiles."""
+    seed = 5
+    a = W.as_dtype_values(W.normal(seed, "a", (m, k)), dtype)
+    w = W.as_dtype_values(W.normal(seed, "w", (n, k), std=k ** -0.5), dtype)
+    out = torch.empty((m, n), dtype=dev(a[:1], dtype).dtype, device="cuda")
+    lib.h3_linear(dev(a, dtype), dev(w, dtype), out)
+    torch.cuda.synchronize()
+    ref = O.linear(a, w)
+    assert_close(host(out), ref, dtype, f"linear {m}x{n}x{k}")
+    # gated residual epilogue, per-row gate and broadcast gate
+    x = W.as_dtype_values(W.normal(seed, "x", (m, n)), dtype)
+    g = W.as_dtype_values(W.normal(seed, "g", (m, n), std=0.1), dtype)
+    xt = dev(x, dtype)
+    lib.h3_linear(dev(a, dtype), dev(w, dtype), xt, gate=dev(g, dtype))
+    torch.cuda.synchronize()
+    assert_close(host(xt), O.gated_residual(x, g, ref), dtype, "linear+residual")
+    xt = dev(x, dtype)
+    lib.h3_linear(dev(a, dtype), dev(w, dtype), xt, gate=dev(g[:1], dtype))
+    torch.cuda.synchronize()
+    assert_close(host(xt), O.gated_residual(x, g[:1], ref), dtype, "linear+residual(bcast)")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816)])
+def test_swiglu_parity(lib, dtype, n, c, f):
+    seed = 9
+    h = W.as_dtype_values(W.normal(seed, "h", (n, c)), dtype)
+    # unit-scale weights (std 1/sqrt(fan_in)): pre-activations and outputs are O(1)
+    w1 = W.as_dtype_values(W.normal(seed, "w1", (f, c), std=c ** -0.5), dtype)
+    w3 = W.as_dtype_values(W.normal(seed, "w3", (f, c), std=c ** -0.5), dtype)
+    w2 = W.as_dtype_values(W.normal(seed, "w2", (c, f), std=f ** -0.5), dtype)
+    out = dev(np.zeros((n, c), np.float32), dtype)
+    lib.h3_swiglu(dev(h, dtype), dev(w1, dtype), dev(w3, dtype), dev(w2, dtype), out)
+    torch.cuda.synchronize()
+    ref = O.swiglu_mlp(h, w1, w3, w2)
+    assert_close(host(out), ref, dtype, "swiglu")
+    x = W.as_dtype_values(W.normal(seed, "x", (n, c)), dtype)
+    g = W.as_dtype_values(W.normal(seed, "g", (n, c), std=0.1), dtype)
+    xt = dev(x, dtype)
+    lib.h3_swiglu(dev(h, dtype), dev(w1, dtype), dev(w3, dtype), dev(w2, dtype), xt, gate=dev(g, dtype))
+    torch.cuda.synchronize()
+    assert_close(host(xt), O.gated_residual(x, g, ref), dtype, "swiglu+residual")
+
+
+# ------------------------------------------------------------- attention
+
+def _attn_gpu(lib, c, dtype, max_len=None):
+    q, k, v = (dev(t.reshape(c.n_buf, -1), dtype) for t in (c.q, c.k, c.v))
+    o = torch.full_like(q, float("nan"))
+    lib.h3_varlen_attn(q, k, v, o, c.n_heads, c.head_dim, dev_i32(c.cu_slots), dev_i32(c.valid_len),
+                       int(max_len if max_len is not None else c.valid_len.max()))
+    torch.cuda.synchronize()
+    return host(o).reshape(c.n_buf, c.n_heads, c.head_dim)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lengths,n_buf,H,D", [((480,), 480, 4, 64), ((300, 77, 1, 64), 512, 3, 64),
+                                              ((1000, 129, 17), 1300, 2, 128)])
+def test_varlen_attention_parity_small(lib, dtype, lengths, n_buf, H, D):
+    c = W.varlen_case(seed=21, lengths=lengths, n_buf=n_buf, n_heads=H, head_dim=D, dtype=dtype)
+    got = _attn_gpu(lib, c, dtype)
+    ref = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    assert_close(got, ref, dtype, f"attn {lengths}")
+
+
+def test_varlen_attention_8k_three_segments(lib):
+    """Packed 4032/1500/17 in an 8192 buffer, 8 heads x 128, bf16: parity, pad rows
+    exactly 0, NaN/Inf pads change nothing bit for bit, each segment alone equals
+    the packed run bit for bit, reruns are byte-identical."""
+    c = W.varlen_case(seed=0, dtype="bf16")
+    got = _attn_gpu(lib, c, "bf16")
+    ref = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    assert_close(got, ref, "bf16", "attn 8k")
+    valid = np.zeros(c.n_buf, bool)
+    for s in range(3):
+        valid[c.cu_slots[s]:c.cu_slots[s] + c.valid_len[s]] = True
+    assert np.all(got[~valid] == 0)
+    poisoned = W.varlen_case(seed=0, dtype="bf16", pad_fill="nan")
+    got_p = _attn_gpu(lib, poisoned, "bf16")
+    assert np.array_equal(got_p, got)
+    again = _attn_gpu(lib, c, "bf16")
+    assert np.array_equal(again, got)
+    for s in range(3):
+        lo, n = int(c.cu_slots[s]), int(c.valid_len[s])
+        one = W.VarlenCase(n, 8, 128, np.array([0, n], np.int32), np.array([n], np.int32),
+                           c.q[lo:lo + n], c.k[lo:lo + n], c.v[lo:lo + n])
+        alone = _attn_gpu(lib, one, "bf16")
+        assert np.array_equal(alone, got[lo:lo + n])
+
+
+def test_varlen_attention_edge_segments(lib):
+    """Zero-length and one-row segments, a segment ending exactly at the buffer end,
+    a grid bound above the true maximum."""
+    H, D = 2, 128
+    n_buf = 200
+    r = np.random.default_rng(0)
+    q, k, v = (W.round_to_bf16(r.standard_normal((n_buf, H, D)).astype(np.float32)) for _ in range(3))
+    cu = np.array([0, 10, 10, 11, 75, 200], np.int32)
+    vl = np.array([0, 0, 1, 64, 125], np.int32)
+    c = W.VarlenCase(n_buf, H, D, cu, vl, q, k, v)
+    got = _attn_gpu(lib, c, "bf16", max_len=190)
+    ref = O.varlen_attention(q, k, v, cu, vl)
+    assert_close(got, ref, "bf16", "attn edges")
+    assert np.all(got[0:10] == 0)
+    assert np.allclose(got[10], v[10], atol=0)  # one-row segment: o = v exactly (p = 1)
