@@ -137,6 +137,8 @@ h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k
   TRY(check_rows("v", v, ld_v, w, n_buf, dt));
   TRY(check_rows("o", o, ld_o, w, n_buf, dt));
   CHECK(ld_q > 0 && ld_k > 0 && ld_v > 0 && ld_o > 0, "row strides must be positive");
+  // the bf16 kernel addresses a 64-row key tile and the transposed-V scratch with 32-bit byte offsets
+  CHECK(ld_k <= (1 << 23) && n_buf <= (1 << 22), "row stride above 2^23 or n_buf above 2^22");
   const size_t need = h3::attn_workspace_bytes(dt == H3_BF16, n_buf, H, D, n_seg);
   if (ws_bytes < need)
     return fail(H3_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu", ws_bytes, need);

@@ -109,16 +109,6 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restri
 namespace {
 constexpr int KT = 64;  // keys per tile
 
-// K tile in LDS: [64 keys][D], the D/8 16-byte chunks of a row swizzled by the row
-template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk) {
-  return row * D + ((chunk ^ (row & (D / 8 - 1))) << 3);
-}
-// V^T tile in LDS: [D][64 keys], 8 chunks per row swizzled by (row & 7)
-__device__ __forceinline__ int vt_off(int row, int chunk) {
-  return row * KT + ((chunk ^ (row & 7)) << 3);
-}
-
 // Accumulator row i of a 32x32 MFMA tile (lane half h, register r) is
 // i = (r/4)*8 + h*4 + r%4.  Reading K row sigma(i) into A-operand row i makes
 // register r of lane half h hold key (r/8)*16 + h*8 + r%8, i.e. registers
@@ -128,8 +118,30 @@ __device__ __forceinline__ int sigma_row(int i) {
   const int a = i >> 3;
   return (a >> 1) * 16 + ((i >> 2) & 1) * 8 + (a & 1) * 4 + (i & 3);
 }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16x2 (one v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// raw buffer resource over [base, base + bytes); loads past the end return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
 }  // namespace
 
+// LDS layout of one stage: K tile [64 keys][D + 8] then V^T tile [D][64 + 8]
+// (bf16).  The 16-byte row padding puts the 16 rows that one 16-lane group of
+// a ds_read_b128 touches on 16 distinct 4-bank groups, and keeps every
+// fragment read a compile-time offset from one per-lane base address.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ q, int64_t ld_q, const bf16_t* __restrict__ k, int64_t ld_k,
@@ -137,9 +149,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     const int* __restrict__ cu, const int* __restrict__ valid, float scale_log2) {
   constexpr int BMQ = NW * 32;
   constexpr int NTH = NW * 64;
-  constexpr int KCH = D / 8;  // 16-byte chunks per K row
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * KT];
+  constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  constexpr int KS = D + 8;            // padded K row, elements
+  constexpr int VS = KT + 8;           // padded V^T row, elements
+  constexpr int K_ELEMS = KT * KS;
+  constexpr int STAGE = K_ELEMS + D * VS;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
 
   const int s = blockIdx.y;
   const int head = blockIdx.z;
@@ -167,42 +182,45 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     }
   }
 
-  // ---- tile loaders: K 64 x D and V^T D x 64, 16-byte chunks
-  constexpr int K_CHUNKS = KT * KCH;   // 1024 for D=128
-  constexpr int V_CHUNKS = D * 8;      // 1024 for D=128
-  constexpr int KPT = K_CHUNKS / NTH;  // per thread
-  constexpr int VPT = V_CHUNKS / NTH;
-  static_assert(K_CHUNKS % NTH == 0 && V_CHUNKS % NTH == 0, "tile split");
-  const bf16_t* kbase = k + (int64_t)seg_lo * ld_k + head * D;
-  const bf16_t* vbase = vt + (int64_t)head * D * vt_cols + vt_segment_base(seg_lo, s);
+  // ---- tile loaders (buffer loads: per-thread byte offsets fixed, per-tile base in SGPRs)
+  constexpr int KPT = KT * KCH / NTH;  // 16-byte K chunks per thread per tile
+  constexpr int VPT = D * 8 / NTH;     // 16-byte V^T chunks per thread per tile
+  static_assert((KT * KCH) % NTH == 0 && (D * 8) % NTH == 0, "tile split");
+  const char* kbase = reinterpret_cast<const char*>(k + (int64_t)seg_lo * ld_k + head * D);
+  const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)head * D * vt_cols +
+                                                    vt_segment_base(seg_lo, s));
+  const int k_row_bytes = (int)(ld_k * 2);
+  int k_voff[KPT], k_lds[KPT], v_voff[VPT], v_lds[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = tid + i * NTH, r = c / KCH, ch = c % KCH;
+    k_voff[i] = r * k_row_bytes + ch * 16;
+    k_lds[i] = r * KS + ch * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = tid + i * NTH, r = c / 8, ch = c % 8;
+    v_voff[i] = r * (int)(vt_cols * 2) + ch * 16;
+    v_lds[i] = K_ELEMS + r * VS + ch * 8;
+  }
+  const int v_bytes = (int)(D * vt_cols * 2);
   uint4 rk[KPT], rv[VPT];
   auto load_tile = [&](int jt) {
     const int j0 = jt * KT;
+    const __amdgpu_buffer_rsrc_t rs_k =
+        make_rsrc(kbase + (int64_t)j0 * k_row_bytes, min(len - j0, KT) * k_row_bytes);
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(vbase + (int64_t)j0 * 2, v_bytes);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NTH;
-      const int r = c / KCH, ch = c % KCH;
-      rk[i] = (j0 + r < len) ? *reinterpret_cast<const uint4*>(kbase + (int64_t)(j0 + r) * ld_k + ch * 8)
-                             : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < KPT; ++i) rk[i] = buf_load16(rs_k, k_voff[i]);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * NTH;
-      const int r = c / 8, ch = c % 8;
-      rv[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)r * vt_cols + j0 + ch * 8);
-    }
+    for (int i = 0; i < VPT; ++i) rv[i] = buf_load16(rs_v, v_voff[i]);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int stage) {
+    bf16_t* st = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NTH;
-      *reinterpret_cast<uint4*>(&Ks[buf][k_off<D>(c / KCH, c % KCH)]) = rk[i];
-    }
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[i];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * NTH;
-      *reinterpret_cast<uint4*>(&Vs[buf][vt_off(c / 8, c % 8)]) = rv[i];
-    }
+    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[i];
   };
 
   f32x16_t oacc[D / 32];
@@ -214,27 +232,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
   float l_run = 0.f;        // this lane's partial row sum
 
   const int n_tiles = (len + KT - 1) / KT;
-  const int krow = sigma_row(qi);  // permuted K row read by this lane
+  const int k_frag = sigma_row(qi) * KS + hf * 8;  // per-lane K fragment base (elements)
+  const int v_frag = K_ELEMS + qi * VS + hf * 8;   // per-lane V^T fragment base
   load_tile(0);
   store_tile(0);
   __syncthreads();
 
   for (int jt = 0; jt < n_tiles; ++jt) {
-    const int buf = jt & 1;
+    const bf16_t* st = smem + (jt & 1) * STAGE;
     if (jt + 1 < n_tiles) load_tile(jt + 1);
 
-    // S^T for keys [0,32) and [32,64) of the tile
+    // S^T for keys [0,32) and [32,64) of the tile, the two chains interleaved
     f32x16_t sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            &Ks[buf][k_off<D>(kb * 32 + krow, kk * 2 + hf)]);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sc[kb], 0, 0, 0);
-      }
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(st + k_frag + kk * 16);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(st + k_frag + 32 * KS + kk * 16);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], sc[1], 0, 0, 0);
     }
     // mask keys >= len (only the last tile can hold them)
     if ((jt + 1) * KT > len) {
@@ -253,7 +270,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    }
     const float mx_s = mx * scale_log2;
     // raise the running max only when it is exceeded by more than 8 (log2 units)
     const bool raise = mx_s > m_run + 8.0f;
@@ -279,25 +300,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + 2 * t], scale_log2, -m_run));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + 2 * t + 1], scale_log2, -m_run));
           l_run += p0 + p1;
-          w[t] = pack_bf16x2(p0, p1);
+          w[t] = cvt_pk_bf16(p0, p1);
         }
         pb[kb][half] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
     }
     // O^T += V^T P^T : d blocks of 32, keys in 4 blocks of 16
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int chunk = kb * 4 + half * 2 + hf;  // keys kb*32 + half*16 + hf*8 .. +8
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Vs[buf][vt_off(db * 32 + qi, chunk)]);
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+              st + v_frag + db * 32 * VS + kb * 32 + half * 16);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][half], oacc[db], 0, 0, 0);
         }
       }
     }
-    if (jt + 1 < n_tiles) store_tile(buf ^ 1);
+    if (jt + 1 < n_tiles) store_tile((jt + 1) & 1);
     __syncthreads();
   }
 
@@ -312,8 +333,275 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
     for (int g = 0; g < 4; ++g) {
       const int d = db * 32 + g * 8 + hf * 4;
       uint2 val;
-      val.x = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
-      val.y = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+      val.x = cvt_pk_bf16(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+      val.y = cvt_pk_bf16(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = val;
+    }
+  }
+}
+
+// ---------------------------------------------- software-pipelined MFMA kernel
+//
+// Same operand layouts as above, restructured so the MFMA and VALU pipes
+// overlap within a wave: in iteration j a wave issues S(j+1) = K(j+1) Q^T
+// (MFMA, independent) while it runs the softmax of S(j) (VALU), then P(j).V(j).
+// Keys go through a 3-stage LDS ring: iteration j reads K(j+1) and V(j) and
+// writes tile j+2 into the third stage, so one barrier per tile suffices.
+// 8 waves (256 query rows) share each K/V tile; the row sums use
+// v_dot2_f32_bf16 on the packed bf16 P (the values the MFMA multiplies).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
+    const bf16_t* __restrict__ q, int64_t ld_q, const bf16_t* __restrict__ k, int64_t ld_k,
+    const bf16_t* __restrict__ vt, int64_t vt_cols, bf16_t* __restrict__ o, int64_t ld_o,
+    const int* __restrict__ cu, const int* __restrict__ valid, float scale_log2) {
+  constexpr int BMQ = NW * 32;
+  constexpr int NTH = NW * 64;
+  constexpr int KCH = D / 8;
+  constexpr int KS = D + 8;
+  constexpr int VS = KT + 8;
+  constexpr int K_ELEMS = KT * KS;
+  constexpr int STAGE = K_ELEMS + D * VS;
+  constexpr int NSTAGE = 3;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[NSTAGE * STAGE];
+
+  const int s = blockIdx.y;
+  const int head = blockIdx.z;
+  const int seg_lo = cu[s];
+  const int len = seg_valid(cu, valid, s);
+  const int q0 = blockIdx.x * BMQ;
+  if (q0 >= len) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qi = lane & 31;
+  const int hf = lane >> 5;
+  const int qrow = q0 + wave * 32 + qi;
+  const bool q_ok = qrow < len;
+  const int n_tiles = (len + KT - 1) / KT;
+
+  bf16x8_t qf[D / 16];
+  {
+    const bf16_t* qp = q + (int64_t)(seg_lo + (q_ok ? qrow : 0)) * ld_q + head * D + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      uint4 val = q_ok ? *reinterpret_cast<const uint4*>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, val);
+    }
+  }
+
+  constexpr int KPT = KT * KCH / NTH;
+  constexpr int VPT = D * 8 / NTH;
+  static_assert((KT * KCH) % NTH == 0 && (D * 8) % NTH == 0, "tile split");
+  const char* kbase = reinterpret_cast<const char*>(k + (int64_t)seg_lo * ld_k + head * D);
+  const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)head * D * vt_cols +
+                                                    vt_segment_base(seg_lo, s));
+  const int k_row_bytes = (int)(ld_k * 2);
+  int k_voff[KPT], k_lds[KPT], v_voff[VPT], v_lds[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = tid + i * NTH, r = c / KCH, ch = c % KCH;
+    k_voff[i] = r * k_row_bytes + ch * 16;
+    k_lds[i] = r * KS + ch * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = tid + i * NTH, r = c / 8, ch = c % 8;
+    v_voff[i] = r * (int)(vt_cols * 2) + ch * 16;
+    v_lds[i] = K_ELEMS + r * VS + ch * 8;
+  }
+  const int v_bytes = (int)(D * vt_cols * 2);
+  uint4 rk[KPT], rv[VPT];
+  auto load_tile = [&](int jt) {
+    const int j0 = jt * KT;
+    const __amdgpu_buffer_rsrc_t rs_k =
+        make_rsrc(kbase + (int64_t)j0 * k_row_bytes, min(len - j0, KT) * k_row_bytes);
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(vbase + (int64_t)j0 * 2, v_bytes);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) rk[i] = buf_load16(rs_k, k_voff[i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) rv[i] = buf_load16(rs_v, v_voff[i]);
+  };
+  auto store_tile = [&](int stage) {
+    bf16_t* st = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[i];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[i];
+  };
+
+  const int k_frag = sigma_row(qi) * KS + hf * 8;
+  const int v_frag = K_ELEMS + qi * VS + hf * 8;
+  auto compute_s = [&](int stage, f32x16_t (&sc)[2]) {
+    const bf16_t* st = smem + stage * STAGE;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(st + k_frag + kk * 16);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(st + k_frag + 32 * KS + kk * 16);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], sc[1], 0, 0, 0);
+    }
+  };
+
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_a = 0.f, l_b = 0.f;
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  auto kfrag = [&](const bf16_t* sk, int kk, int ch) {
+    return *reinterpret_cast<const bf16x8_t*>(sk + k_frag + ch * 32 * KS + kk * 16);
+  };
+  // V^T fragment of P.V group g (keys g*16 .. g*16+15 of the tile) and d block db
+  auto vfrag = [&](const bf16_t* sv, int g, int db) {
+    return *reinterpret_cast<const bf16x8_t*>(sv + v_frag + db * 32 * VS + g * 16);
+  };
+  auto mask_tile = [&](f32x16_t (&sc)[2], int jt) {
+    const int base = jt * KT;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = base + kb * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
+        if (key >= len) sc[kb][r] = -INFINITY;
+      }
+  };
+  // raise the running max to the tile max if it exceeds it by more than 8
+  // (log2 units) and rescale O and l; skipped on most tiles
+  auto update_max = [&](float mx) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    const float mx_s = mx * scale_log2;
+    const bool raise = mx_s > m_run + 8.0f;
+    if (__any(raise)) {
+      const float m_new = raise ? mx_s : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_a *= alpha;
+      l_b *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+  };
+
+  // One tile step, hand-ordered so that each wave keeps both pipes busy:
+  //  phase A: S(next) = K(next) Q^T (16 MFMAs), each followed by 1/16 of the
+  //           softmax of S(cur): 2 fma + 2 exp + 1 pack + 1 dot2 (VALU);
+  //  phase B: O^T += V(cur)^T P^T (16 MFMAs), each followed by one v_max3 of
+  //           the row max of S(next).
+  // LDS fragments are read 4 MFMAs ahead.  sched_barrier(0) keeps the order.
+  auto step_core = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2],
+                       int jt) {
+    const bf16_t* sk = smem + stage_k * STAGE;
+    const bf16_t* sv = smem + stage_v * STAGE;
+    constexpr int NA = 2 * (D / 16);  // phase A MFMAs: 2 key blocks x D/16 k-steps
+    constexpr int NB = 4 * (D / 32);  // phase B MFMAs: 4 key groups x D/32 d blocks
+    constexpr int SL = 16 / NA;       // softmax slices (2 exps each) per phase-A MFMA
+    constexpr int MX = 32 / NB;       // scores folded into the max per phase-B MFMA
+    bf16x8_t kf[4], vf[4];
+    uint32_t w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[i] = kfrag(sk, i >> 1, i & 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nxt[0][r] = nxt[1][r] = 0.f;
+    // ---- phase A
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+      if (i + 4 < NA) kf[i & 3] = kfrag(sk, (i + 4) >> 1, (i + 4) & 1);
+      else {
+        const int pidx = i + 4 - NA;  // first P.V fragments of phase B
+        vf[pidx & 3] = vfrag(sv, pidx / (D / 32), pidx % (D / 32));
+      }
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) {
+        const int slice = i * SL + sl;
+        const int g = slice >> 2, t = slice & 3, kb = g >> 1, half = g & 1;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t], scale_log2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t + 1], scale_log2, -m_run));
+        w[g][t] = cvt_pk_bf16(p0, p1);
+        // keep this slice of the softmax here, next to its MFMA (no sinking past the mask branch)
+        asm volatile("" ::"v"(w[g][t]));
+        if (t & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_b, false);
+        else l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_a, false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const bool more = jt + 1 < n_tiles;
+    if (more && (jt + 2) * KT > len) mask_tile(nxt, jt + 1);
+    // ---- phase B
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int g = i / (D / 32), db = i % (D / 32);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[g][0], w[g][1], w[g][2], w[g][3]));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, oacc[db], 0, 0, 0);
+      if (i + 4 < NB) vf[i & 3] = vfrag(sv, (i + 4) / (D / 32), (i + 4) % (D / 32));
+#pragma unroll
+      for (int e = 0; e < MX; ++e) {
+        const int idx = i * MX + e;
+        mx = fmaxf(mx, nxt[idx >> 4][idx & 15]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) update_max(mx);
+  };
+
+  load_tile(0);
+  store_tile(0);
+  if (n_tiles > 1) {
+    load_tile(1);
+    store_tile(1);
+  }
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+  compute_s(0, sa);
+  if (n_tiles == 1) mask_tile(sa, 0);
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
+    update_max(mx);
+  }
+  if (n_tiles > 2) load_tile(2);
+
+  // after the last tile, S(next) reads a stale stage and is discarded
+  auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    step_core((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt);
+    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
+    __syncthreads();
+    if (jt + 3 < n_tiles) load_tile(jt + 3);
+  };
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    step(jt, sa, sb);
+    if (jt + 1 >= n_tiles) break;
+    step(jt + 1, sb, sa);
+  }
+
+  float l_run = l_a + l_b;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_ok) return;
+  const float inv = 1.0f / l_tot;
+  bf16_t* op = o + (int64_t)(seg_lo + qrow) * ld_o + head * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + hf * 4;
+      uint2 val;
+      val.x = cvt_pk_bf16(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+      val.y = cvt_pk_bf16(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
       *reinterpret_cast<uint2*>(op + d) = val;
     }
   }
@@ -375,9 +663,9 @@ static hipError_t launch_attn_d(bool bf16, const void* q, int64_t ld_q, const vo
     const int64_t cols = vt_columns(n_buf, n_seg);
     hipLaunchKernelGGL((transpose_v_kernel<D>), dim3((unsigned)ceil_div(max_len, 64), n_seg, n_heads),
                        dim3(256), 0, s, (const bf16_t*)v, ld_v, (bf16_t*)ws, cols, cu, valid);
-    constexpr int NW = 4;
+    constexpr int NW = 8;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>),
+    hipLaunchKernelGGL((attn_fwd_bf16_pipe_kernel<D, NW>),
                        dim3((unsigned)ceil_div(max_len, NW * 32), n_seg, n_heads), dim3(NW * 64), 0,
                        s, (const bf16_t*)q, ld_q, (const bf16_t*)k, ld_k, (const bf16_t*)ws, cols,
                        (bf16_t*)o, ld_o, cu, valid, scale_log2);
