@@ -182,6 +182,85 @@ def cpu_baseline(wl, w, bi, work, attn_rows=2048, local_rows=4096):
                        f"n_loc/{local_rows}); extrapolated full block {full_s:.0f}s")}
 
 
+
+# ------------------------------------------------------------ student loop
+
+def run_loop_bench(args, h3, torch, W):
+    """Four-forward student loop on the 15 s share: 8 blocks with their own weights,
+    modulation regenerated per sigma from the timestep embedding, Euler update."""
+    import numpy as np
+    wl = W.PRESETS[args.config]
+    bf = torch.bfloat16
+    timer = EventTimer(torch.cuda.current_stream())
+    t0 = time.time()
+    blocks = []
+    for b in range(wl.n_blocks):
+        w = W.block_weights(wl, args.seed, "bf16", block=b)
+        blocks.append({k: to_dev(getattr(w, k), bf) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")})
+        del w
+    tw = W.timestep_weights(wl, args.seed, "bf16")
+    bi = W.block_inputs(wl, args.seed, "bf16")
+    log(f"generated and uploaded loop inputs in {time.time() - t0:.1f}s")
+    H, D, C = wl.n_heads, wl.head_dim, wl.dim
+    hc = wl.head_count
+    z0 = to_dev(bi.x, bf)
+    z = z0.clone()
+    x = z0.clone()
+    t1, t2, tab = to_dev(tw.w_t1, bf), to_dev(tw.w_t2, bf), to_dev(tw.table, bf)
+    mods = torch.empty((wl.n_blocks, 6, C), dtype=bf, device="cuda")
+    pos, cu, vl = to_dev(bi.pos), to_dev(bi.cu_slots), to_dev(bi.valid_len)
+    max_len = int(bi.valid_len.max())
+    cfg = h3.block_config(C, H, D, wl.ffn_dim, wl.sections, wl.theta, wl.eps_qk, wl.eps_mod, 0, bf)
+    share = dict(qkv_attn=to_dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), bf),
+                 o_attn=torch.zeros((wl.n_pad_total, hc * D), dtype=bf, device="cuda"),
+                 o_local=to_dev(bi.o_local.reshape(wl.n_loc, -1), bf), tok_begin=wl.tok_begin,
+                 head_begin=wl.head_begin, head_count=hc)
+    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, wl.n_pad_total, 1), dtype=torch.uint8, device="cuda")
+    tws = torch.empty(max(h3.timestep_workspace_size(C), 16), dtype=torch.uint8, device="cuda")
+    sig = W.STUDENT_SIGMAS
+    fwd_ms = []
+
+    def loop(record=False):
+        z.copy_(z0)
+        x.copy_(z0)
+        for k in range(len(sig) - 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            h3.h3_timestep_modulation(sig[k], t1, t2, tab, mods, ws=tws)
+            for b in range(wl.n_blocks):
+                h3.h3_dit_block_forward(cfg, blocks[b], x, mods[b:b + 1], pos, cu, vl, max_len, ws=ws, **share)
+            h3.h3_euler_update(z, x, x, sig[k], sig[k + 1])
+            e1.record()
+            if record:
+                fwd_ms.append((e0, e1))
+
+    for _ in range(args.warmup):
+        loop()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    t_start = time.perf_counter()
+    loop_ms = timer.time(lambda: loop(record=True), steps)
+    wall = (time.perf_counter() - t_start) * 1e3 / steps
+    per_fwd = [a.elapsed_time(b) for a, b in fwd_ms]
+    work = algorithmic_work(wl)
+    blk_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
+    total_flop = blk_flop * wl.n_blocks * (len(sig) - 1)
+    value = total_flop / loop_ms / 1e9
+    out = {
+        "metric": "four-forward student loop, 15 s share: loop ms and ms per forward", "value": value,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": loop_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.n_blocks} DiT blocks x {len(sig) - 1} forwards, rank {wl.rank} "
+                               f"of {wl.sp_degree} share (n_loc={wl.n_loc}; attention over N={wl.n_valid}, "
+                               f"{hc} of {H} heads x {D})", "n_valid": wl.n_valid, "n_loc": wl.n_loc,
+                   "blocks": wl.n_blocks, "forwards": len(sig) - 1, "parallelism": "1 GPU (rank-share stand-in)"},
+        "loop_ms": loop_ms, "wall_ms": wall, "ms_per_forward": per_fwd[-(len(sig) - 1):],
+        "ms_per_block": loop_ms / (wl.n_blocks * (len(sig) - 1)),
+    }
+    print(json.dumps(out))
+
 # ------------------------------------------------------------------- main
 
 def main():
@@ -196,6 +275,9 @@ def main():
     import workloads as W
 
     wl = W.PRESETS[args.config]
+    if wl.n_blocks > 1:
+        run_loop_bench(args, h3, torch, W)
+        return
     bf = torch.bfloat16
     stream = torch.cuda.current_stream()
     timer = EventTimer(stream)
