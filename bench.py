@@ -397,7 +397,7 @@ def main():
     traffic = traffic_record()
     roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
-                "kernel": "attn_fwd_bf16_kernel<128,4> (+ V transpose pass)",
+                "kernel": "attn_fwd_bf16_pipe_kernel<128,8> (+ V transpose pass)",
                 "algorithmic_flop_per_launch": work["attn_flop"]}
 
     out = {
