@@ -11,9 +11,10 @@
 //
 // bf16 path (MFMA, gfx950): 256x256 output tile (256x128 for SwiGLU), K step
 // 64, 512 threads = 8 waves as 2 (M) x 4 (N), each wave 128x64 built from
-// 4x2 v_mfma_f32_32x32x16_bf16 tiles.  A and B tiles are staged through LDS,
-// double buffered (128 KiB), with the 16-byte chunk index XOR-swizzled by the
-// row so that MFMA operand reads of 32 rows at one k offset spread over banks.
+// 4x2 v_mfma_f32_32x32x16_bf16 tiles.  Two variants: the general one (any K
+// multiple of 8) stages A and B through LDS with the 16-byte chunk index
+// XOR-swizzled by the row; the K % 64 == 0 one (every shape of the block) is
+// described where it is defined.
 // The next K tile is fetched into registers while the current one is
 // multiplied.  Work-group ids are remapped so that the tiles one XCD runs at
 // a time form a compact 4 (M) x 8 (N) patch: their A and B panels are then
@@ -194,6 +195,184 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------- bf16 path, K % 64 == 0
+//
+// Same tiling and epilogues as above, with the K loop rebuilt around what
+// the hardware does cheaply:
+//  * A and B tiles sit in LDS as [256][64 + 8]: the 16-byte row padding puts
+//    the 16 rows read by one 16-lane group on distinct bank groups and keeps
+//    every fragment read an immediate offset from one per-lane base;
+//  * tiles are fetched with buffer loads whose base advances in SGPRs each K
+//    step; rows past M (or N) read as zero through the range check, so there
+//    is no per-load predicate;
+//  * the fragments of k-slice kk+1 are read while the 8 MFMAs of slice kk run.
+namespace {
+constexpr int BKP = BK + 8;  // padded LDS row (elements)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t g_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 g_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_fast_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+    const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
+    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BKP];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BKP];
+
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+
+  // global -> LDS assignment: chunk lchunk of rows lrow + 64 i
+  const int lchunk = tid & 7;
+  const int lrow = tid >> 3;
+  const int a_row_bytes = (int)(lda * 2), b_row_bytes = (int)(ldb * 2);
+  int a_voff[4], b_voff[4], lds_off_[4];
+  const char* a_base = reinterpret_cast<const char*>(A + (int64_t)m0 * lda);
+  const int64_t a_bytes = (int64_t)(M - m0) * a_row_bytes;
+  // B: for SwiGLU the tile's rows come from W1 (first 32 of every 64) and W3
+  const char* b_base;
+  const char* b3_base = nullptr;
+  int64_t b_bytes;
+  if constexpr (EPI == EPI_SWIGLU) {
+    b_base = reinterpret_cast<const char*>(B + (int64_t)tn * 128 * ldb);
+    b3_base = reinterpret_cast<const char*>(B3 + (int64_t)tn * 128 * ldb);
+    b_bytes = (int64_t)(N - tn * 128) * b_row_bytes;
+  } else {
+    b_base = reinterpret_cast<const char*>(B + (int64_t)tn * BN * ldb);
+    b_bytes = (int64_t)(N - tn * BN) * b_row_bytes;
+  }
+  bool b_from3[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 64 * i;
+    a_voff[i] = r * a_row_bytes + lchunk * 16;
+    int br = r;
+    b_from3[i] = false;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int w = r >> 6, within = r & 63;
+      br = w * 32 + (within & 31);
+      b_from3[i] = within >= 32;
+    }
+    b_voff[i] = br * b_row_bytes + lchunk * 16;
+    lds_off_[i] = r * BKP + lchunk * 8;
+  }
+
+  uint4 ra[4], rb[4];
+  auto load_tile = [&](int kt) {
+    const int64_t koff = (int64_t)kt * BK * 2;
+    const __amdgpu_buffer_rsrc_t rs_a = g_rsrc(a_base + koff, a_bytes - koff);
+    const __amdgpu_buffer_rsrc_t rs_b = g_rsrc(b_base + koff, b_bytes - koff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = g_load16(rs_a, a_voff[i]);
+    if constexpr (EPI == EPI_SWIGLU) {
+      const __amdgpu_buffer_rsrc_t rs_b3 = g_rsrc(b3_base + koff, b_bytes - koff);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[i] = b_from3[i] ? g_load16(rs_b3, b_voff[i]) : g_load16(rs_b, b_voff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[i] = g_load16(rs_b, b_voff[i]);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(&As[buf][lds_off_[i]]) = ra[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][lds_off_[i]]) = rb[i];
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int frag_row = lane & 31;
+  const int frag_half = lane >> 5;
+  const int a_frag = (wm * 128 + frag_row) * BKP + frag_half * 8;
+  const int b_frag = (wn * 64 + frag_row) * BKP + frag_half * 8;
+  const int nk = K / BK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bf16_t* as = As[buf];
+    const bf16_t* bs = Bs[buf];
+    if (kt + 1 < nk) load_tile(kt + 1);
+    bf16x8_t af[2][4], bfr[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8_t*>(as + a_frag + mi * 32 * BKP);
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) bfr[0][ni] = *reinterpret_cast<const bf16x8_t*>(bs + b_frag + ni * 32 * BKP);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          af[c ^ 1][mi] = *reinterpret_cast<const bf16x8_t*>(as + a_frag + mi * 32 * BKP + (kk + 1) * 16);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          bfr[c ^ 1][ni] = *reinterpret_cast<const bf16x8_t*>(bs + b_frag + ni * 32 * BKP + (kk + 1) * 16);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][mi], bfr[c][ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + mi * 32 + (r >> 2) * 8 + frag_half * 4 + (r & 3);
+      if (row >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int col = tn * 128 + wn * 32 + frag_row;
+        if (col < N) {
+          const float a = acc[mi][0][r], b = acc[mi][1][r];
+          C[(int64_t)row * ldc + col] = f2bf(silu_f(a) * b);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = tn * BN + wn * 64 + ni * 32 + frag_row;
+          if (col < N) {
+            bf16_t* p = C + (int64_t)row * ldc + col;
+            if constexpr (EPI == EPI_RESIDUAL) {
+              const float g = bf2f(gate[(int64_t)row * ld_gate + col]);
+              *p = f2bf(bf2f(*p) + g * acc[mi][ni][r]);
+            } else {
+              *p = f2bf(acc[mi][ni][r]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 
 template <int EPI>
@@ -255,10 +434,15 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
     const int tiles_m = (int)ceil_div(M, BM);
     const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
-#define H3_G(E)                                                                               \
-  hipLaunchKernelGGL((gemm_bf16_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, lda, \
-                     (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,                \
-                     (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n)
+#define H3_G(E)                                                                                 \
+  if (K % BK == 0)                                                                               \
+    hipLaunchKernelGGL((gemm_bf16_fast_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, \
+                       lda, (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,           \
+                       (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n);            \
+  else                                                                                           \
+    hipLaunchKernelGGL((gemm_bf16_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, lda, \
+                       (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,                \
+                       (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n)
     if (epi == EPI_SWIGLU) H3_G(EPI_SWIGLU);
     else if (epi == EPI_RESIDUAL) H3_G(EPI_RESIDUAL);
     else H3_G(EPI_STORE);
