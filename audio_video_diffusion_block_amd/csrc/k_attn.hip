@@ -411,23 +411,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     v_lds[i] = K_ELEMS + r * VS + ch * 8;
   }
   const int v_bytes = (int)(D * vt_cols * 2);
-  uint4 rk[KPT], rv[VPT];
-  auto load_tile = [&](int jt) {
+  // two register sets: tile t is loaded into set t % 2 two steps before it is stored
+  uint4 rk[2][KPT], rv[2][VPT];
+  auto load_tile = [&](int jt, int set) {
     const int j0 = jt * KT;
     const __amdgpu_buffer_rsrc_t rs_k =
         make_rsrc(kbase + (int64_t)j0 * k_row_bytes, min(len - j0, KT) * k_row_bytes);
     const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(vbase + (int64_t)j0 * 2, v_bytes);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) rk[i] = buf_load16(rs_k, k_voff[i]);
+    for (int i = 0; i < KPT; ++i) rk[set][i] = buf_load16(rs_k, k_voff[i]);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) rv[i] = buf_load16(rs_v, v_voff[i]);
+    for (int i = 0; i < VPT; ++i) rv[set][i] = buf_load16(rs_v, v_voff[i]);
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage, int set) {
     bf16_t* st = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[i];
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[set][i];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[i];
+    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[set][i];
   };
 
   const int k_frag = sigma_row(qi) * KS + hf * 8;
@@ -513,7 +514,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     for (int i = 0; i < 4; ++i) kf[i] = kfrag(sk, i >> 1, i & 1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) nxt[0][r] = nxt[1][r] = 0.f;
-    // ---- phase A
+    // ---- phase A.  Slot i: one MFMA of S(next), the fma/exp of softmax slice
+    // i and the pack/row-sum of slice i-1 (so a pack never waits on the exp it
+    // consumes: in-order issue would stall the wave there).
+    float pe[2][SL][2];  // exp results in flight, by slot parity
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], nxt[i & 1], 0, 0, 0);
@@ -526,41 +530,61 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       for (int sl = 0; sl < SL; ++sl) {
         const int slice = i * SL + sl;
         const int g = slice >> 2, t = slice & 3, kb = g >> 1, half = g & 1;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t], scale_log2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t + 1], scale_log2, -m_run));
-        w[g][t] = cvt_pk_bf16(p0, p1);
-        // keep this slice of the softmax here, next to its MFMA (no sinking past the mask branch)
-        asm volatile("" ::"v"(w[g][t]));
-        if (t & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_b, false);
-        else l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_a, false);
+        pe[i & 1][sl][0] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t], scale_log2, -m_run));
+        pe[i & 1][sl][1] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t + 1], scale_log2, -m_run));
+      }
+      if (i > 0) {
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+          const int slice = (i - 1) * SL + sl;
+          const int g = slice >> 2, t = slice & 3;
+          w[g][t] = cvt_pk_bf16(pe[(i - 1) & 1][sl][0], pe[(i - 1) & 1][sl][1]);
+          // keep this slice here, next to its MFMA (no sinking past the mask branch)
+          asm volatile("" ::"v"(w[g][t]));
+          if (t & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_b, false);
+          else l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_a, false);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+      const int slice = (NA - 1) * SL + sl;
+      const int g = slice >> 2, t = slice & 3;
+      w[g][t] = cvt_pk_bf16(pe[(NA - 1) & 1][sl][0], pe[(NA - 1) & 1][sl][1]);
+      if (t & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_b, false);
+      else l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_a, false);
+    }
     const bool more = jt + 1 < n_tiles;
     if (more && (jt + 2) * KT > len) mask_tile(nxt, jt + 1);
-    // ---- phase B
+    // ---- phase B.  Slot i: one P.V MFMA and the row-max step of score pair
+    // group i-2 (the first two slots let the last S(next) MFMAs finish).
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int g = i / (D / 32), db = i % (D / 32);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[g][0], w[g][1], w[g][2], w[g][3]));
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, oacc[db], 0, 0, 0);
-      if (i + 4 < NB) vf[i & 3] = vfrag(sv, (i + 4) / (D / 32), (i + 4) % (D / 32));
+    for (int i = 0; i < NB + 2; ++i) {
+      if (i < NB) {
+        const int g = i / (D / 32), db = i % (D / 32);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[g][0], w[g][1], w[g][2], w[g][3]));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, oacc[db], 0, 0, 0);
+        if (i + 4 < NB) vf[i & 3] = vfrag(sv, (i + 4) / (D / 32), (i + 4) % (D / 32));
+      }
+      if (i >= 2) {
 #pragma unroll
-      for (int e = 0; e < MX; ++e) {
-        const int idx = i * MX + e;
-        mx = fmaxf(mx, nxt[idx >> 4][idx & 15]);
+        for (int e = 0; e < MX; ++e) {
+          const int idx = (i - 2) * MX + e;
+          mx = fmaxf(mx, nxt[idx >> 4][idx & 15]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) update_max(mx);
   };
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  store_tile(0, 0);
   if (n_tiles > 1) {
-    load_tile(1);
-    store_tile(1);
+    load_tile(1, 1);
+    store_tile(1, 1);
   }
   __syncthreads();
   f32x16_t sa[2], sb[2];
@@ -574,19 +598,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
     update_max(mx);
   }
-  if (n_tiles > 2) load_tile(2);
+  if (n_tiles > 2) load_tile(2, 0);
+  if (n_tiles > 3) load_tile(3, 1);
 
-  // after the last tile, S(next) reads a stale stage and is discarded
-  auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+  // step jt reads K(jt+1) and V(jt) from the ring, stores tile jt+2 (loaded
+  // two steps ago into register set jt % 2) and refills that set with tile
+  // jt+4.  After the last tile, S(next) reads a stale stage and is discarded.
+  auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], int set) {
     step_core((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt);
-    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
+    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE, set);
     __syncthreads();
-    if (jt + 3 < n_tiles) load_tile(jt + 3);
+    if (jt + 4 < n_tiles) load_tile(jt + 4, set);
   };
   for (int jt = 0; jt < n_tiles; jt += 2) {
-    step(jt, sa, sb);
+    step(jt, sa, sb, 0);
     if (jt + 1 >= n_tiles) break;
-    step(jt + 1, sb, sa);
+    step(jt + 1, sb, sa, 1);
   }
 
   float l_run = l_a + l_b;
