@@ -343,12 +343,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
 // ---------------------------------------------- software-pipelined MFMA kernel
 //
 // Same operand layouts as above, restructured so the MFMA and VALU pipes
-// overlap within a wave: in iteration j a wave issues S(j+1) = K(j+1) Q^T
-// (MFMA, independent) while it runs the softmax of S(j) (VALU), then P(j).V(j).
-// Keys go through a 3-stage LDS ring: iteration j reads K(j+1) and V(j) and
-// writes tile j+2 into the third stage, so one barrier per tile suffices.
-// 8 waves (256 query rows) share each K/V tile; the row sums use
-// v_dot2_f32_bf16 on the packed bf16 P (the values the MFMA multiplies).
+// overlap: in tile step j a wave issues S(j+1) = K(j+1) Q^T (MFMA,
+// independent) while it runs the softmax of S(j) (VALU), then P(j).V(j).  The
+// two halves of the work-group run these two phases in opposite order, so the
+// two waves sharing a SIMD are in different phases.  Keys go through a 4-stage
+// LDS ring with one barrier per tile.  8 waves (256 query rows) share each K/V
+// tile; the row sums use v_dot2_f32_bf16 on the packed bf16 P (the values the
+// MFMA multiplies).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ q, int64_t ld_q, const bf16_t* __restrict__ k, int64_t ld_k,
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   constexpr int VS = KT + 8;
   constexpr int K_ELEMS = KT * KS;
   constexpr int STAGE = K_ELEMS + D * VS;
-  constexpr int NSTAGE = 3;
+  constexpr int NSTAGE = 4;
   __shared__ __attribute__((aligned(16))) bf16_t smem[NSTAGE * STAGE];
 
   const int s = blockIdx.y;
@@ -494,29 +495,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     }
   };
 
-  // One tile step, hand-ordered so that each wave keeps both pipes busy:
+  // A tile step is two phases, hand-ordered so that each keeps both pipes fed:
   //  phase A: S(next) = K(next) Q^T (16 MFMAs), each followed by 1/16 of the
-  //           softmax of S(cur): 2 fma + 2 exp + 1 pack + 1 dot2 (VALU);
-  //  phase B: O^T += V(cur)^T P^T (16 MFMAs), each followed by one v_max3 of
-  //           the row max of S(next).
+  //           softmax of S(cur): 2 fma + 2 exp + 1 pack + 1 dot2 (VALU-heavy);
+  //  phase B: O^T += V(cur)^T P^T (16 MFMAs), each followed by one step of the
+  //           row max of S(next) (MFMA-heavy).
   // LDS fragments are read 4 MFMAs ahead.  sched_barrier(0) keeps the order.
-  auto step_core = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2],
-                       int jt) {
+  // P (packed bf16) and the first V^T fragments pass from phase A to phase B.
+  uint32_t w[4][4];
+  bf16x8_t vf[4];
+  constexpr int NA = 2 * (D / 16);  // phase A MFMAs: 2 key blocks x D/16 k-steps
+  constexpr int NB = 4 * (D / 32);  // phase B MFMAs: 4 key groups x D/32 d blocks
+  auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2], int jt) {
     const bf16_t* sk = smem + stage_k * STAGE;
     const bf16_t* sv = smem + stage_v * STAGE;
-    constexpr int NA = 2 * (D / 16);  // phase A MFMAs: 2 key blocks x D/16 k-steps
-    constexpr int NB = 4 * (D / 32);  // phase B MFMAs: 4 key groups x D/32 d blocks
     constexpr int SL = 16 / NA;       // softmax slices (2 exps each) per phase-A MFMA
-    constexpr int MX = 32 / NB;       // scores folded into the max per phase-B MFMA
-    bf16x8_t kf[4], vf[4];
-    uint32_t w[4][4];
+    bf16x8_t kf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[i] = kfrag(sk, i >> 1, i & 1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) nxt[0][r] = nxt[1][r] = 0.f;
-    // ---- phase A.  Slot i: one MFMA of S(next), the fma/exp of softmax slice
-    // i and the pack/row-sum of slice i-1 (so a pack never waits on the exp it
-    // consumes: in-order issue would stall the wave there).
+    // Slot i: one MFMA of S(next), the fma/exp of softmax slice i and the
+    // pack/row-sum of slice i-1 (so a pack never waits on the exp it consumes:
+    // in-order issue would stall the wave there).
     float pe[2][SL][2];  // exp results in flight, by slot parity
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -555,10 +556,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       if (t & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_b, false);
       else l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_a, false);
     }
-    const bool more = jt + 1 < n_tiles;
-    if (more && (jt + 2) * KT > len) mask_tile(nxt, jt + 1);
-    // ---- phase B.  Slot i: one P.V MFMA and the row-max step of score pair
-    // group i-2 (the first two slots let the last S(next) MFMAs finish).
+    if (jt + 1 < n_tiles && (jt + 2) * KT > len) mask_tile(nxt, jt + 1);
+  };
+  // nxt holds S(jt+1), written by phase A of tile jt
+  auto phase_b = [&](int stage_v, f32x16_t (&nxt)[2], int jt) {
+    const bf16_t* sv = smem + stage_v * STAGE;
+    constexpr int MX = 32 / NB;       // scores folded into the max per phase-B MFMA
+    // Slot i: one P.V MFMA and the row-max step of score pair group i-2 (the
+    // first two slots let the last S(next) MFMAs finish).
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NB + 2; ++i) {
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) update_max(mx);
+    if (jt + 1 < n_tiles) update_max(mx);
   };
 
   load_tile(0, 0);
@@ -601,11 +606,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   if (n_tiles > 2) load_tile(2, 0);
   if (n_tiles > 3) load_tile(3, 1);
 
-  // step jt reads K(jt+1) and V(jt) from the ring, stores tile jt+2 (loaded
-  // two steps ago into register set jt % 2) and refills that set with tile
-  // jt+4.  After the last tile, S(next) reads a stale stage and is discarded.
+  // Phase rotation: the two wave halves of the work-group share each SIMD
+  // (waves w and w + NW/2).  The first half runs A(jt) then B(jt) in step jt;
+  // the second runs B(jt-1) then A(jt).  Both do the same work between two
+  // barriers, but at any moment one wave of a SIMD is in its VALU-heavy phase
+  // while the other feeds the matrix core.
+  // During step jt the ring holds tiles jt-1 (V, second half), jt (V, first
+  // half) and jt+1 (K, both halves); tile jt+2, loaded two steps ago into
+  // register set jt % 2, goes to the fourth stage, and that set is refilled
+  // with tile jt+4.  After the last tile, S(next) reads a stale stage and is
+  // discarded.
+  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
   auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], int set) {
-    step_core((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt);
+    if (lag && jt > 0) phase_b((jt - 1) % NSTAGE, cur, jt - 1);
+    phase_a((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt);
+    if (!lag) phase_b(jt % NSTAGE, nxt, jt);
     if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE, set);
     __syncthreads();
     if (jt + 4 < n_tiles) load_tile(jt + 4, set);
@@ -614,6 +629,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     step(jt, sa, sb, 0);
     if (jt + 1 >= n_tiles) break;
     step(jt + 1, sb, sa, 1);
+  }
+  if (lag) {
+    // S(n_tiles) sits in sb when n_tiles is odd, else in sa (unused: no max update)
+    if (n_tiles & 1) phase_b((n_tiles - 1) % NSTAGE, sb, n_tiles - 1);
+    else phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1);
   }
 
   float l_run = l_a + l_b;
