@@ -412,24 +412,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     v_lds[i] = K_ELEMS + r * VS + ch * 8;
   }
   const int v_bytes = (int)(D * vt_cols * 2);
-  // two register sets: tile t is loaded into set t % 2 two steps before it is stored
-  uint4 rk[2][KPT], rv[2][VPT];
-  auto load_tile = [&](int jt, int set) {
+  // staging registers: tile t is loaded one step before it is stored
+  uint4 rk[KPT], rv[VPT];
+  auto load_tile = [&](int jt) {
     const int j0 = jt * KT;
     const __amdgpu_buffer_rsrc_t rs_k =
         make_rsrc(kbase + (int64_t)j0 * k_row_bytes, min(len - j0, KT) * k_row_bytes);
     const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(vbase + (int64_t)j0 * 2, v_bytes);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) rk[set][i] = buf_load16(rs_k, k_voff[i]);
+    for (int i = 0; i < KPT; ++i) rk[i] = buf_load16(rs_k, k_voff[i]);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) rv[set][i] = buf_load16(rs_v, v_voff[i]);
+    for (int i = 0; i < VPT; ++i) rv[i] = buf_load16(rs_v, v_voff[i]);
   };
-  auto store_tile = [&](int stage, int set) {
+  auto store_tile = [&](int stage) {
     bf16_t* st = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[set][i];
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[i];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[set][i];
+    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[i];
   };
 
   const int k_frag = sigma_row(qi) * KS + hf * 8;
@@ -508,6 +508,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   constexpr int NB = 4 * (D / 32);  // phase B MFMAs: 4 key groups x D/32 d blocks
   auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2], int jt) {
     const bf16_t* sk = smem + stage_k * STAGE;
+    // the wave in this (VALU-heavy) phase wins issue arbitration against the
+    // other wave of its SIMD, whose P.V MFMAs then fill the matrix pipe
+    __builtin_amdgcn_s_setprio(2);
     const bf16_t* sv = smem + stage_v * STAGE;
     constexpr int SL = 16 / NA;       // softmax slices (2 exps each) per phase-A MFMA
     bf16x8_t kf[4];
@@ -556,6 +559,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       if (t & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_b, false);
       else l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[g][t]), ones, l_a, false);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (jt + 1 < n_tiles && (jt + 2) * KT > len) mask_tile(nxt, jt + 1);
   };
   // nxt holds S(jt+1), written by phase A of tile jt
@@ -585,11 +589,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     if (jt + 1 < n_tiles) update_max(mx);
   };
 
-  load_tile(0, 0);
-  store_tile(0, 0);
+  load_tile(0);
+  store_tile(0);
   if (n_tiles > 1) {
-    load_tile(1, 1);
-    store_tile(1, 1);
+    load_tile(1);
+    store_tile(1);
   }
   __syncthreads();
   f32x16_t sa[2], sb[2];
@@ -603,8 +607,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
     update_max(mx);
   }
-  if (n_tiles > 2) load_tile(2, 0);
-  if (n_tiles > 3) load_tile(3, 1);
+  if (n_tiles > 2) load_tile(2);
 
   // Phase rotation: the two wave halves of the work-group share each SIMD
   // (waves w and w + NW/2).  The first half runs A(jt) then B(jt) in step jt;
@@ -612,23 +615,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   // barriers, but at any moment one wave of a SIMD is in its VALU-heavy phase
   // while the other feeds the matrix core.
   // During step jt the ring holds tiles jt-1 (V, second half), jt (V, first
-  // half) and jt+1 (K, both halves); tile jt+2, loaded two steps ago into
-  // register set jt % 2, goes to the fourth stage, and that set is refilled
-  // with tile jt+4.  After the last tile, S(next) reads a stale stage and is
-  // discarded.
+  // half) and jt+1 (K, both halves); tile jt+2, loaded into registers during
+  // the previous step, goes to the fourth stage, and tile jt+3 is loaded.
+  // After the last tile, S(next) reads a stale stage and is discarded.
   const bool lag = __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
-  auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], int set) {
+  auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     if (lag && jt > 0) phase_b((jt - 1) % NSTAGE, cur, jt - 1);
     phase_a((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt);
     if (!lag) phase_b(jt % NSTAGE, nxt, jt);
-    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE, set);
+    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
     __syncthreads();
-    if (jt + 4 < n_tiles) load_tile(jt + 4, set);
+    if (jt + 3 < n_tiles) load_tile(jt + 3);
   };
   for (int jt = 0; jt < n_tiles; jt += 2) {
-    step(jt, sa, sb, 0);
+    step(jt, sa, sb);
     if (jt + 1 >= n_tiles) break;
-    step(jt + 1, sb, sa, 1);
+    step(jt + 1, sb, sa);
   }
   if (lag) {
     // S(n_tiles) sits in sb when n_tiles is odd, else in sa (unused: no max update)
