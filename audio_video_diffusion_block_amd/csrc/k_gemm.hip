@@ -10,11 +10,11 @@
 // takeaways": SwiGLU and residual updates are fused into neighbouring work.
 //
 // bf16 path (MFMA, gfx950): 256x256 output tile (256x128 for SwiGLU), K step
-// 64, 512 threads = 8 waves as 2 (M) x 4 (N), each wave 128x64 built from
-// 4x2 v_mfma_f32_32x32x16_bf16 tiles.  Two variants: the general one (any K
-// multiple of 8) stages A and B through LDS with the 16-byte chunk index
-// XOR-swizzled by the row; the K % 64 == 0 one (every shape of the block) is
-// described where it is defined.
+// 64.  Two kernels: the general one (any K multiple of 8: 512 threads = 8
+// waves as 2 (M) x 4 (N), each wave 128x64 from 4x2 v_mfma_f32_32x32x16_bf16
+// tiles, A and B staged through registers into LDS with the 16-byte chunk
+// index XOR-swizzled by the row) and the K % 64 == 0 one (every shape of the
+// block), described where it is defined.
 // The next K tile is fetched into registers while the current one is
 // multiplied.  Work-group ids are remapped so that the tiles one XCD runs at
 // a time form a compact 4 (M) x 8 (N) patch: their A and B panels are then
@@ -373,6 +373,202 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_fast_kernel(
   }
 }
 
+// --------------------------------------- bf16 path, K % 64 == 0, one wave/SIMD
+//
+// 256 x 256 output tile (256 x 128 for SwiGLU), K step 64, 256 threads = 4
+// waves as 2 (M) x 2 (N), each wave 128 x 128 from 4 x 4 MFMA tiles whose
+// accumulators (256 floats per lane) live in the accumulation registers.  Per
+// 16-wide k-slice a wave reads 8 fragments for 16 MFMAs, half the LDS traffic
+// per MFMA of a 128 x 64 wave tile.
+//  * Tiles go from global memory straight into LDS (global_load_lds_dwordx4:
+//    no staging registers, no LDS stores).  One such instruction writes 1 KB,
+//    i.e. 8 rows of 64 bf16; lane l writes 16-byte slot l % 8 of row l / 8 and
+//    fetches the global chunk that the swizzle puts there.
+//  * LDS rows are unpadded, 16-byte chunk c of row r at slot c ^ ((r / 2) % 8):
+//    the 16 rows one 16-lane group of a fragment read touches then cover all
+//    16 slot positions of a 256-byte bank line.
+//  * Rows past M (or N) are clamped to the last row: every load is in bounds
+//    and those accumulator rows are never stored.
+//  * Two LDS stages (128 KB): tile k+1 is in flight while tile k is multiplied;
+//    one barrier per K step.
+namespace {
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+constexpr int W4_THREADS = 256;
+constexpr int W4_STAGE = 32768;  // bytes of one 256 x 64 bf16 tile
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+    const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
+    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * W4_STAGE];
+
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int row_a = (int)(lda * 2), row_b = (int)(ldb * 2);
+
+  // ---- DMA assignment: wave w fills LDS rows 64 w .. 64 w + 63 of each tile,
+  // 8 rows per instruction j.  Byte offsets are relative to the tile's first row.
+  const char* a_base = reinterpret_cast<const char*>(A + (int64_t)m0 * lda);
+  const char* b_base;
+  const char* b3_base = nullptr;
+  int b_row0;  // first B row of the tile
+  if constexpr (EPI == EPI_SWIGLU) {
+    b_row0 = tn * 128;
+    b3_base = reinterpret_cast<const char*>(B3 + (int64_t)b_row0 * ldb);
+  } else {
+    b_row0 = tn * BN;
+  }
+  b_base = reinterpret_cast<const char*>(B + (int64_t)b_row0 * ldb);
+  int a_off[8], b_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + j * 8 + (lane >> 3);  // LDS row
+    const int c = (lane & 7) ^ ((r >> 1) & 7);       // global chunk for this slot
+    a_off[j] = (min(m0 + r, M - 1) - m0) * row_a + c * 16;
+    int br;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // tile rows 64 w .. 64 w + 31 are W1 rows, the next 32 the W3 rows of
+      // the same 32 output features (j < 4: W1, j >= 4: W3)
+      br = b_row0 + wave * 32 + ((j * 8 + (lane >> 3)) & 31);
+    } else {
+      br = b_row0 + r;
+    }
+    b_off[j] = (min(br, N - 1) - b_row0) * row_b + c * 16;
+  }
+  // DMA instruction t (0..15) of tile kt: t < 8 fills A rows, t >= 8 B rows.
+  // Issued as inline assembly: the compiler would otherwise count these loads
+  // as pending LDS operations and make every later fragment read wait for
+  // them (lgkmcnt(0)).  Their completion is tracked by vmcnt alone; the K loop
+  // waits for vmcnt(0) before the barrier that publishes the tile.  The
+  // global address is an SGPR base (the tile's row block and K offset) plus
+  // the lane's fixed 32-bit offset; the LDS address goes to M0.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+  auto dma16 = [&](const char* base, int voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds_addr) : "memory", "m0");
+  };
+  auto issue_dma = [&](int kt, int stage, int t) {
+    const int koff = kt * BK * 2;
+    if (t < 8) {
+      dma16(a_base + koff, a_off[t], lds0 + stage * W4_STAGE + wave * 8192 + t * 1024);
+    } else {
+      const int j = t - 8;
+      const char* src = (EPI == EPI_SWIGLU && j >= 4) ? b3_base : b_base;
+      dma16(src + koff, b_off[j], lds0 + (2 + stage) * W4_STAGE + wave * 8192 + j * 1024);
+    }
+  };
+
+  // ---- fragment addresses: A row wm*128 + mi*32 + lane%32, chunk 2 kk + lane/32
+  const int fr = lane & 31, fh = lane >> 5;
+  const int swz = (fr >> 1) & 7;  // (row / 2) % 8 for every mi (rows step by 32)
+  int fa[4], fb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int cs = ((kk * 2 + fh) ^ swz) * 16;
+    fa[kk] = (wm * 128 + fr) * 128 + cs;
+    fb[kk] = 2 * W4_STAGE + (wn * 128 + fr) * 128 + cs;
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) issue_dma(0, 0, t);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // one K step; MORE: tile kt+1 exists and is fetched during slice 0 (the
+  // last step is a separate instantiation, so neither body branches)
+  auto k_step = [&](int kt, auto more_tag) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    const int so = (kt & 1) * W4_STAGE;
+    bf16x8_t af[2][4], bfr[2][4];
+    // fragment j of slice kk: A0, B0..B3, A1..A3 (the order the MFMAs use them)
+    auto read_frag = [&](int kk, int j) {
+      const int c = kk & 1;
+      if (j == 0) af[c][0] = *reinterpret_cast<const bf16x8_t*>(smem + fa[kk] + so);
+      else if (j <= 4) bfr[c][j - 1] = *reinterpret_cast<const bf16x8_t*>(smem + fb[kk] + so + (j - 1) * 4096);
+      else af[c][j - 4] = *reinterpret_cast<const bf16x8_t*>(smem + fa[kk] + so + (j - 4) * 4096);
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      read_frag(0, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // slice kk: 16 MFMAs (mi-major).  The 8 fragments of slice kk+1 are
+    // requested after the first 8 of them (so they land before slice kk+1
+    // starts); in slices 0 and 1 every second MFMA is followed by one DMA of
+    // tile kt+1.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk & 1;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int mi = t >> 2, ni = t & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][mi], bfr[c][ni], acc[mi][ni], 0, 0, 0);
+        if (MORE && kk < 2 && (t & 1)) issue_dma(kt + 1, (kt + 1) & 1, kk * 8 + (t >> 1));
+        if (kk + 1 < 4 && t < 8) read_frag(kk + 1, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // tile kt+1 has landed (own DMAs) and is visible (barrier); stage kt&1 is free
+    if (MORE) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) k_step(kt, std::true_type{});
+  k_step(nk - 1, std::false_type{});
+
+  // ---- epilogue: lane holds column lane%32, rows (r/4)*8 + (lane/32)*4 + r%4
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3);
+      if (row >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = tn * 128 + (wn * 2 + j) * 32 + fr;
+          if (col < N) {
+            const float a = acc[mi][2 * j][r], b = acc[mi][2 * j + 1][r];
+            C[(int64_t)row * ldc + col] = f2bf(silu_f(a) * b);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int col = tn * BN + wn * 128 + ni * 32 + fr;
+          if (col < N) {
+            bf16_t* p = C + (int64_t)row * ldc + col;
+            if constexpr (EPI == EPI_RESIDUAL) {
+              const float g = bf2f(gate[(int64_t)row * ld_gate + col]);
+              *p = f2bf(bf2f(*p) + g * acc[mi][ni][r]);
+            } else {
+              *p = f2bf(acc[mi][ni][r]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 
 template <int EPI>
@@ -435,8 +631,8 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
     const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
 #define H3_G(E)                                                                                 \
-  if (K % BK == 0)                                                                               \
-    hipLaunchKernelGGL((gemm_bf16_fast_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, \
+  if (K >= BK && K % BK == 0)                                                                   \
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<E>), grid, dim3(W4_THREADS), 0, s, (const bf16_t*)A, \
                        lda, (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,           \
                        (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n);            \
   else                                                                                           \
