@@ -195,184 +195,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
   }
 }
 
-// ---------------------------------------------------- bf16 path, K % 64 == 0
-//
-// Same tiling and epilogues as above, with the K loop rebuilt around what
-// the hardware does cheaply:
-//  * A and B tiles sit in LDS as [256][64 + 8]: the 16-byte row padding puts
-//    the 16 rows read by one 16-lane group on distinct bank groups and keeps
-//    every fragment read an immediate offset from one per-lane base;
-//  * tiles are fetched with buffer loads whose base advances in SGPRs each K
-//    step; rows past M (or N) read as zero through the range check, so there
-//    is no per-load predicate;
-//  * the fragments of k-slice kk+1 are read while the 8 MFMAs of slice kk run.
-namespace {
-constexpr int BKP = BK + 8;  // padded LDS row (elements)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t g_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                           (int)(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 g_load16(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-}  // namespace
-
-template <int EPI>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_fast_kernel(
-    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
-    const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
-    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
-    int tiles_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BKP];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BKP];
-
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-
-  // global -> LDS assignment: chunk lchunk of rows lrow + 64 i
-  const int lchunk = tid & 7;
-  const int lrow = tid >> 3;
-  const int a_row_bytes = (int)(lda * 2), b_row_bytes = (int)(ldb * 2);
-  int a_voff[4], b_voff[4], lds_off_[4];
-  const char* a_base = reinterpret_cast<const char*>(A + (int64_t)m0 * lda);
-  const int64_t a_bytes = (int64_t)(M - m0) * a_row_bytes;
-  // B: for SwiGLU the tile's rows come from W1 (first 32 of every 64) and W3
-  const char* b_base;
-  const char* b3_base = nullptr;
-  int64_t b_bytes;
-  if constexpr (EPI == EPI_SWIGLU) {
-    b_base = reinterpret_cast<const char*>(B + (int64_t)tn * 128 * ldb);
-    b3_base = reinterpret_cast<const char*>(B3 + (int64_t)tn * 128 * ldb);
-    b_bytes = (int64_t)(N - tn * 128) * b_row_bytes;
-  } else {
-    b_base = reinterpret_cast<const char*>(B + (int64_t)tn * BN * ldb);
-    b_bytes = (int64_t)(N - tn * BN) * b_row_bytes;
-  }
-  bool b_from3[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 64 * i;
-    a_voff[i] = r * a_row_bytes + lchunk * 16;
-    int br = r;
-    b_from3[i] = false;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int w = r >> 6, within = r & 63;
-      br = w * 32 + (within & 31);
-      b_from3[i] = within >= 32;
-    }
-    b_voff[i] = br * b_row_bytes + lchunk * 16;
-    lds_off_[i] = r * BKP + lchunk * 8;
-  }
-
-  uint4 ra[4], rb[4];
-  auto load_tile = [&](int kt) {
-    const int64_t koff = (int64_t)kt * BK * 2;
-    const __amdgpu_buffer_rsrc_t rs_a = g_rsrc(a_base + koff, a_bytes - koff);
-    const __amdgpu_buffer_rsrc_t rs_b = g_rsrc(b_base + koff, b_bytes - koff);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = g_load16(rs_a, a_voff[i]);
-    if constexpr (EPI == EPI_SWIGLU) {
-      const __amdgpu_buffer_rsrc_t rs_b3 = g_rsrc(b3_base + koff, b_bytes - koff);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = b_from3[i] ? g_load16(rs_b3, b_voff[i]) : g_load16(rs_b, b_voff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = g_load16(rs_b, b_voff[i]);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&As[buf][lds_off_[i]]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][lds_off_[i]]) = rb[i];
-    }
-  };
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  const int frag_row = lane & 31;
-  const int frag_half = lane >> 5;
-  const int a_frag = (wm * 128 + frag_row) * BKP + frag_half * 8;
-  const int b_frag = (wn * 64 + frag_row) * BKP + frag_half * 8;
-  const int nk = K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bf16_t* as = As[buf];
-    const bf16_t* bs = Bs[buf];
-    if (kt + 1 < nk) load_tile(kt + 1);
-    bf16x8_t af[2][4], bfr[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8_t*>(as + a_frag + mi * 32 * BKP);
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) bfr[0][ni] = *reinterpret_cast<const bf16x8_t*>(bs + b_frag + ni * 32 * BKP);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk & 1;
-      if (kk + 1 < BK / 16) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          af[c ^ 1][mi] = *reinterpret_cast<const bf16x8_t*>(as + a_frag + mi * 32 * BKP + (kk + 1) * 16);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          bfr[c ^ 1][ni] = *reinterpret_cast<const bf16x8_t*>(bs + b_frag + ni * 32 * BKP + (kk + 1) * 16);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][mi], bfr[c][ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 128 + mi * 32 + (r >> 2) * 8 + frag_half * 4 + (r & 3);
-      if (row >= M) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
-        const int col = tn * 128 + wn * 32 + frag_row;
-        if (col < N) {
-          const float a = acc[mi][0][r], b = acc[mi][1][r];
-          C[(int64_t)row * ldc + col] = f2bf(silu_f(a) * b);
-        }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = tn * BN + wn * 64 + ni * 32 + frag_row;
-          if (col < N) {
-            bf16_t* p = C + (int64_t)row * ldc + col;
-            if constexpr (EPI == EPI_RESIDUAL) {
-              const float g = bf2f(gate[(int64_t)row * ld_gate + col]);
-              *p = f2bf(bf2f(*p) + g * acc[mi][ni][r]);
-            } else {
-              *p = f2bf(acc[mi][ni][r]);
-            }
-          }
-        }
-      }
-    }
-  }
-}
-
 // --------------------------------------- bf16 path, K % 64 == 0, one wave/SIMD
 //
 // 256 x 256 output tile (256 x 128 for SwiGLU), K step 64, 256 threads = 4
@@ -404,8 +226,9 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
     const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
     const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
     int tiles_n) {
-  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]
-  __shared__ __attribute__((aligned(1024))) char smem[4 * W4_STAGE];
+  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
+  // (256 x 264 bf16 or 128 x 264 fp32 = 135168 bytes)
+  __shared__ __attribute__((aligned(1024))) char smem[135168];
 
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -534,37 +357,86 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
   for (int kt = 0; kt + 1 < nk; ++kt) k_step(kt, std::true_type{});
   k_step(nk - 1, std::false_type{});
 
-  // ---- epilogue: lane holds column lane%32, rows (r/4)*8 + (lane/32)*4 + r%4
+  // ---- epilogue through LDS.  A lane holds column lane%32 and rows
+  // (r/4)*8 + (lane/32)*4 + r%4 of each 32x32 block; the tile is written to LDS
+  // in that layout and read back as row-contiguous 16-byte chunks, so every
+  // global access is a 16-byte vector.  Padded LDS rows keep the lane-per-
+  // column writes of the two lane halves (rows 4 apart) on disjoint banks.
+  __syncthreads();  // every wave is done with the last tile's fragments
+  const int tid = threadIdx.x;
+  if constexpr (EPI == EPI_RESIDUAL) {
+    // out = out + gate * acc with acc in fp32: two passes of 128 rows
+    constexpr int FS = 264;  // floats per LDS row
+    float* ef = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 128 + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3);
-      if (row >= M) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = tn * 128 + (wn * 2 + j) * 32 + fr;
-          if (col < N) {
-            const float a = acc[mi][2 * j][r], b = acc[mi][2 * j + 1][r];
-            C[(int64_t)row * ldc + col] = f2bf(silu_f(a) * b);
-          }
-        }
-      } else {
+          for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = tn * BN + wn * 128 + ni * 32 + fr;
-          if (col < N) {
-            bf16_t* p = C + (int64_t)row * ldc + col;
-            if constexpr (EPI == EPI_RESIDUAL) {
-              const float g = bf2f(gate[(int64_t)row * ld_gate + col]);
-              *p = f2bf(bf2f(*p) + g * acc[mi][ni][r]);
-            } else {
-              *p = f2bf(acc[mi][ni][r]);
-            }
-          }
+            for (int r = 0; r < 16; ++r)
+              ef[(mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3)) * FS + wn * 128 + ni * 32 + fr] = acc[mi][ni][r];
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int chunk = tid + i * W4_THREADS;  // 128 rows x 32 chunks of 8
+        const int rl = chunk >> 5, c8 = (chunk & 31) * 8;
+        const int row = m0 + half * 128 + rl, col = tn * BN + c8;
+        if (row >= M || col >= N) continue;
+        const float* src = ef + rl * FS + c8;
+        bf16_t* po = C + (int64_t)row * ldc + col;
+        const bf16_t* pg = gate + (int64_t)row * ld_gate + col;
+        if (col + 8 <= N) {
+          const float4 y0 = *reinterpret_cast<const float4*>(src);
+          const float4 y1 = *reinterpret_cast<const float4*>(src + 4);
+          const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          uint4 xo = *reinterpret_cast<const uint4*>(po);
+          const uint4 gv = *reinterpret_cast<const uint4*>(pg);
+          bf16_t* xe = reinterpret_cast<bf16_t*>(&xo);
+          const bf16_t* ge = reinterpret_cast<const bf16_t*>(&gv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xe[e] = f2bf(bf2f(xe[e]) + bf2f(ge[e]) * yv[e]);
+          *reinterpret_cast<uint4*>(po) = xo;
+        } else {
+          for (int e = 0; col + e < N; ++e) po[e] = f2bf(bf2f(po[e]) + bf2f(pg[e]) * src[e]);
         }
       }
+      __syncthreads();
+    }
+  } else {
+    // bf16 tile: 256 rows x OC columns (256, or 128 SwiGLU outputs)
+    constexpr int OC = EPI == EPI_SWIGLU ? 128 : 256;
+    constexpr int ES = OC + 8;  // bf16 per LDS row
+    bf16_t* eb = reinterpret_cast<bf16_t*>(smem);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 128 + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3);
+        if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            eb[rl * ES + (wn * 2 + j) * 32 + fr] = f2bf(silu_f(acc[mi][2 * j][r]) * acc[mi][2 * j + 1][r]);
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) eb[rl * ES + wn * 128 + ni * 32 + fr] = f2bf(acc[mi][ni][r]);
+        }
+      }
+    __syncthreads();
+    constexpr int CPR = OC / 8;  // 16-byte chunks per row
+#pragma unroll 4
+    for (int i = 0; i < 256 * CPR / W4_THREADS; ++i) {
+      const int chunk = tid + i * W4_THREADS;
+      const int rl = chunk / CPR, c8 = (chunk % CPR) * 8;
+      const int row = m0 + rl, col = (EPI == EPI_SWIGLU ? tn * 128 : tn * BN) + c8;
+      if (row >= M || col >= N) continue;
+      const bf16_t* src = eb + rl * ES + c8;
+      bf16_t* po = C + (int64_t)row * ldc + col;
+      if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
+      else for (int e = 0; col + e < N; ++e) po[e] = src[e];
     }
   }
 }
