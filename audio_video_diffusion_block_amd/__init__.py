@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libh3dit.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m audio_video_diffusion_block_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python audio_video_diffusion_block_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -96,12 +96,13 @@ _c_temb_ws = _sig("h3_timestep_workspace_size", _sz, [_i32])
 _c_temb = _sig("h3_timestep_modulation", ctypes.c_int,
                [_f, _p, _p, _p, _p, _i32, _i32, _i32, _p, _sz, _i32, _p])
 _c_euler = _sig("h3_euler_update", ctypes.c_int, [_p, _p, _p, _i64, _f, _f, _i32, _p])
+_c_frames = _sig("h3_frames_to_u8", ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _i32, _p])
 
 EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_rope",
             "h3_varlen_attn_workspace_size", "h3_varlen_attn", "h3_modulate_residual",
             "h3_linear", "h3_swiglu_workspace_size", "h3_swiglu", "h3_dit_block_workspace_size",
             "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
-            "h3_euler_update")
+            "h3_euler_update", "h3_frames_to_u8")
 
 
 def _status_string(st: int) -> str:
@@ -275,3 +276,19 @@ def h3_euler_update(z, u, x_next=None, sigma_from: float = 0.0, sigma_to: float 
                     stream=None):
     _check(_c_euler(_ptr(z), _ptr(u), _ptr(x_next), z.numel(), sigma_from, sigma_to, _dt(z),
                     _stream(stream)))
+
+
+def h3_frames_to_u8(frames, out, layout: int = 0, stream=None):
+    """frames: float32 [B, 3, T, H, W] (contiguous); out: uint8 [B, T, H, W, 3]
+    (layout 0) or [B, T, 3, H, W] (layout 1), contiguous."""
+    if frames.dtype != torch.float32 or out.dtype != torch.uint8:
+        raise TypeError("frames must be float32 and out uint8")
+    if not (frames.is_contiguous() and out.is_contiguous()):
+        raise ValueError("frames and out must be contiguous")
+    if frames.dim() != 5 or frames.shape[1] != 3:
+        raise ValueError("frames must be [B, 3, T, H, W]")
+    B, _, T, H, W = frames.shape
+    want = (B, T, H, W, 3) if layout == 0 else (B, T, 3, H, W)
+    if tuple(out.shape) != want:
+        raise ValueError(f"out must have shape {want}")
+    _check(_c_frames(_ptr(frames), B, T, H, W, _ptr(out), layout, _stream(stream)))

@@ -1,6 +1,7 @@
 """Build libh3dit.so (HIP, gfx950) in place: hipcc per source, then one link.
 
-Usage: python -m audio_video_diffusion_block_amd.build [-v]
+Usage: python audio_video_diffusion_block_amd/build.py [-v]
+(run as a file: importing it through the package would load the library first)
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libh3dit.so")
 SOURCES = ["h3_api.cpp", "k_qk_norm_rope.hip", "k_modres.hip", "k_gemm.hip", "k_attn.hip",
-           "k_misc.hip"]
+           "k_misc.hip", "k_frames.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

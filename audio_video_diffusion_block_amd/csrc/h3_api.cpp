@@ -515,4 +515,24 @@ h3_status h3_euler_update(void* z, const void* u, void* x_next, int64_t n, float
                     "euler launch");
 }
 
+h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, int64_t W,
+                          void* out, int32_t layout, void* stream) {
+  g_err[0] = 0;
+  CHECK(B >= 0 && T >= 0 && H >= 0 && W >= 0, "B, T, H, W must be non-negative");
+  CHECK(layout == 0 || layout == 1, "layout must be 0 (BTHWC) or 1 (BTCHW planar)");
+  CHECK(W <= ((int64_t)1 << 31) && H <= ((int64_t)1 << 31), "H and W must be below 2^31");
+  const double total = 3.0 * (double)B * (double)T * (double)H * (double)W;
+  CHECK(total < 9.0e15, "frame tensor too large");
+  if (B == 0 || T == 0 || H == 0 || W == 0) return H3_OK;
+  CHECK(frames && out && aligned16(frames) && aligned16(out),
+        "frames and out must be non-NULL, 16-byte aligned");
+  const int64_t n = 3 * B * T * H * W;
+  const uintptr_t fa = (uintptr_t)frames, oa = (uintptr_t)out;
+  CHECK(oa + (uintptr_t)n <= fa || fa + (uintptr_t)n * 4 <= oa, "frames and out overlap");
+  TRY(check_device());
+  return hip_status(launch_frames_u8((const float*)frames, (uint8_t*)out, B, T, H, W, layout,
+                                     (hipStream_t)stream),
+                    "frames launch");
+}
+
 }  // extern "C"

@@ -45,4 +45,8 @@ hipError_t launch_timestep(bool bf16, float sigma, const void* w1, const void* w
                            const void* table, void* mod_out, int n_blocks, int dim, int emb,
                            void* ws, hipStream_t s);
 
+// decoded frames [B][3][T][H][W] fp32 -> uint8, layout 0 [B][T][H][W][3], 1 [B][T][3][H][W]
+hipError_t launch_frames_u8(const float* in, uint8_t* out, int64_t B, int64_t T, int64_t H,
+                            int64_t W, int layout, hipStream_t s);
+
 }  // namespace h3

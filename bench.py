@@ -376,6 +376,13 @@ def main():
     sw_ws = torch.empty(h3.swiglu_workspace_size(wl.n_loc, wl.ffn_dim, bf), dtype=torch.uint8, device="cuda")
     ops["swiglu_residual"] = timer.time(lambda: h3.h3_swiglu(
         h1, wd["w1"], wd["w3"], wd["w2"], xs, gate=mod[:, 5], ws=sw_ws), reps)
+    # post-DiT tail: the 10 s request's decoded frames (1344x768, 243 frames) to uint8 BTHWC
+    fr = W.FRAMES_10S
+    frames = torch.rand((fr["B"], 3, fr["T"], fr["H"], fr["W"]), device="cuda") * 2.1 - 1.05
+    fout = torch.empty((fr["B"], fr["T"], fr["H"], fr["W"], 3), dtype=torch.uint8, device="cuda")
+    ops["frames_u8"] = timer.time(lambda: h3.h3_frames_to_u8(frames, fout, 0), reps)
+    frames_bytes = frames.numel() * 5  # 4 bytes read + 1 byte written per value
+    del frames, fout
     torch.cuda.synchronize()
     attn_ms = ops["attention"]
     attn_tflops = work["attn_flop"] / attn_ms / 1e9
@@ -390,6 +397,9 @@ def main():
                     "frac_hbm": work["modnorm_bytes"] / ops["modnorm"] / 1e6 / HBM_PEAK_GBS},
         "qk_norm_rope": {"ms": ops["qk_norm_rope"], "GB/s": work["qknorm_bytes"] / ops["qk_norm_rope"] / 1e6,
                          "frac_hbm": work["qknorm_bytes"] / ops["qk_norm_rope"] / 1e6 / HBM_PEAK_GBS},
+        "frames_u8": {"ms": ops["frames_u8"], "GB/s": frames_bytes / ops["frames_u8"] / 1e6,
+                      "frac_hbm": frames_bytes / ops["frames_u8"] / 1e6 / HBM_PEAK_GBS,
+                      "workload": "10 s decoded video, 243 x 3 x 768 x 1344 fp32 -> uint8 BTHWC"},
     }
     total_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
     value = total_flop / step_ms / 1e9  # TFLOP/s of the whole block
@@ -410,7 +420,7 @@ def main():
                    "n_valid": wl.n_valid, "n_loc": wl.n_loc, "dim": C, "heads": H, "head_dim": D,
                    "ffn_dim": wl.ffn_dim, "head_slice": hc, "parallelism": "1 GPU (rank-share stand-in)"},
         "block_ms": step_ms, "attn_tflops": attn_tflops,
-        "fused_op_gbps": {k: breakdown[k]["GB/s"] for k in ("modnorm", "qk_norm_rope")},
+        "fused_op_gbps": {k: breakdown[k]["GB/s"] for k in ("modnorm", "qk_norm_rope", "frames_u8")},
         "breakdown": breakdown, "roofline": roofline,
     }
     if not args.no_cpu_baseline:

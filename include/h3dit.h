@@ -267,6 +267,26 @@ h3_status h3_timestep_modulation(float sigma, const void* w_t1, const void* w_t2
 h3_status h3_euler_update(void* z, const void* u, void* x_next, int64_t n, float sigma_from,
                           float sigma_to, h3_dtype dtype, void* stream);
 
+/* ------------------------------------------------- output frames (post-DiT) */
+
+/*
+ * h3_frames_to_u8 -- decoded video frames to compact uint8 (Why Real-Time
+ * MiniMax H3 Serving Requires More Than a Faster DiT, "Key takeaways":
+ * decoded frames are converted on the GPU, once, into contiguous uint8 BTHWC
+ * data; the H.264 encoder is fed through planar paths).
+ *   frames: device fp32 [B][3][T][H][W] (the decoder's channel-first output,
+ *           nominally in [-1, 1]); read only.
+ *   out:    device uint8; layout 0 writes [B][T][H][W][3] (interleaved RGB),
+ *           layout 1 writes [B][T][3][H][W] (one plane per channel and frame).
+ *   Each value: v = x * 0.5 + 0.5 in fp32, clamped to [0, 1] (NaN -> 0), then
+ *   u = v * 255 rounded half to even.
+ *   Both pointers 16-byte aligned and not overlapping; B, T, H, W >= 0.  A
+ *   width that is a multiple of 16 takes the vectorised path.
+ *   Errors: H3_ERR_ARG on a bad pointer, size or layout (nothing launched).
+ */
+h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, int64_t W,
+                          void* out, int32_t layout, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -116,3 +116,16 @@ def test_block_argument_checks():
     io3 = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 120, 480, 400, 3, 1, FAKE, FAKE, FAKE)
     st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io3), FAKE, need, None)
     assert st == h3.H3_ERR_ARG and "local rows" in h3.last_error()
+
+
+def test_frames_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    st = h3._c_frames(FAKE, 1, 2, 4, 16, FAKE + (1 << 20), 2, None)
+    assert st == h3.H3_ERR_ARG and "layout" in h3.last_error()
+    st = h3._c_frames(FAKE, 1, 2, 4, 16, FAKE + 8 + (1 << 20), 0, None)
+    assert st == h3.H3_ERR_ARG and "aligned" in h3.last_error()
+    st = h3._c_frames(FAKE, 1, 2, 4, 16, FAKE + 64, 0, None)
+    assert st == h3.H3_ERR_ARG and "overlap" in h3.last_error()
+    st = h3._c_frames(FAKE, -1, 2, 4, 16, FAKE + (1 << 20), 0, None)
+    assert st == h3.H3_ERR_ARG
+    assert h3._c_frames(None, 1, 0, 4, 16, None, 0, None) == h3.H3_OK  # empty: nothing launched

@@ -593,3 +593,69 @@ def test_block_brute_force_tiny():
     got = O.dit_block(x, mod, w, pos, np.array([0, 6]), np.array([5]), sh)
     ref = _brute_block(x, mod, w, pos, 5, C, H, D, secs, 1e4, 1e-6)
     assert np.allclose(got, ref, atol=1e-11)
+
+
+# ----------------------------------------------------- output frames (f)
+
+def _u8_exact(x32):
+    """The value rule evaluated independently: every step in float64 (where
+    each intermediate is exact), rounded to float32 explicitly, and the final
+    half-to-even rounding done by hand on the exact float32 product."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    v = (x / 2.0 + 0.5).astype(np.float32).astype(np.float64)   # exact in f64, one f32 rounding
+    v = np.where(np.isnan(v), 0.0, v)
+    v = np.clip(v, 0.0, 1.0)
+    w = (v * 255.0).astype(np.float32).astype(np.float64)        # exact in f64, one f32 rounding
+    r = np.floor(w)
+    frac = w - r
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2.0) == 1.0))
+    return (r + up).astype(np.uint8)
+
+
+def test_frames_closed_form_values():
+    x = np.array([-1.0, 1.0, 0.0, 3.0, -7.0, np.nan, np.inf, -np.inf, 0.5, -0.5],
+                 dtype=np.float32)
+    want = [0, 255, 128, 255, 0, 0, 255, 0, 191, 64]  # 0 -> 127.5 -> 128 (even); 0.5 -> 191.25
+    got = O.frames_to_u8(np.repeat(x.reshape(1, 1, 1, 1, -1), 3, axis=1), 0)[0, 0, 0, :, 0]
+    assert got.tolist() == want
+
+
+def test_frames_against_exact_evaluation():
+    # every bf16 value in [-2, 2] plus random float32 values
+    bits = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    xs = bits.view(np.float32)
+    xs = xs[np.isfinite(xs) & (np.abs(xs) <= 2.0)]
+    xs = np.concatenate([xs, rng.uniform(-1.2, 1.2, 200_000).astype(np.float32)])
+    got = O.frames_to_u8(np.repeat(xs.reshape(1, 1, 1, 1, -1), 3, axis=1), 1)[0, 0, 0, 0]
+    np.testing.assert_array_equal(got, _u8_exact(xs))
+
+
+def test_frames_ties_round_to_even():
+    # float32 inputs whose product v * 255 is exactly k + 0.5 exist; each must go to the even side
+    k = np.arange(255, dtype=np.float64)
+    cand = []
+    for d in range(-64, 65):
+        x = (2.0 * (k + 0.5) / 255.0 - 1.0).astype(np.float32)
+        x = np.nextafter(x, np.float32(np.inf) if d > 0 else np.float32(-np.inf)) if d else x
+        cand.append(x)
+    xs = np.unique(np.concatenate(cand))
+    v = (xs.astype(np.float64) / 2 + 0.5).astype(np.float32)
+    w = (v.astype(np.float64) * 255).astype(np.float32).astype(np.float64)
+    ties = xs[(w - np.floor(w)) == 0.5]
+    assert ties.size > 0
+    u = O.frames_to_u8(np.repeat(ties.reshape(1, 1, 1, 1, -1), 3, axis=1), 0)[0, 0, 0, :, 0]
+    assert np.all(u % 2 == 0)
+
+
+def test_frames_monotone_and_layouts_agree():
+    x = W.frames(3, 2, 3, 4, 24)
+    a = O.frames_to_u8(x, 0)
+    p = O.frames_to_u8(x, 1)
+    B, _, T, H, Wd = x.shape
+    for b, c, t, h, w in [(0, 0, 0, 0, 0), (1, 2, 2, 3, 23), (1, 1, 0, 2, 7), (0, 2, 1, 1, 16)]:
+        assert a[b, t, h, w, c] == p[b, t, c, h, w] == _u8_exact(x[b, c, t, h, w:w + 1])[0]
+    s = np.sort(rng.uniform(-1.5, 1.5, 4096).astype(np.float32))
+    u = O.frames_to_u8(np.repeat(s.reshape(1, 1, 1, 1, -1), 3, axis=1), 0)[0, 0, 0, :, 0]
+    assert np.all(np.diff(u.astype(np.int32)) >= 0)
+    # uint8 BTHWC is the contiguous, interleaved layout
+    assert a.flags["C_CONTIGUOUS"] and a.shape == (B, T, H, Wd, 3)

@@ -158,6 +158,31 @@ def normal(seed: int, name: str, shape, std: float = 1.0, mean: float = 0.0,
     return flat.reshape(shape)
 
 
+def _fill_uniform(out: np.ndarray, seed: int, key: int, idx: int, lo: int, hi: int):
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, key, idx])))
+    out[lo:hi] = g.random(hi - lo, dtype=np.float32)
+
+
+def uniform(seed: int, name: str, shape, low: float, high: float,
+            threads: Optional[int] = None) -> np.ndarray:
+    """float32 U[low, high) draws of `shape`, independent per (seed, name)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    flat = np.empty(n, dtype=np.float32)
+    key = _key(name)
+    chunks = [(i, i * _CHUNK, min(n, (i + 1) * _CHUNK)) for i in range((n + _CHUNK - 1) // _CHUNK)]
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    if len(chunks) <= 1 or threads <= 1:
+        for i, lo, hi in chunks:
+            _fill_uniform(flat, seed, key, i, lo, hi)
+    else:
+        with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda c: _fill_uniform(flat, seed, key, *c), chunks))
+    flat *= np.float32(high - low)
+    flat += np.float32(low)
+    return flat.reshape(shape)
+
+
 def uniform_ints(seed: int, name: str, low: int, high: int, size: int) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _key(name), 0])))
     return g.integers(low, high, size=size, endpoint=True)
@@ -364,3 +389,35 @@ def timestep_weights(wl: Workload, seed: int, dtype: str) -> TimestepWeights:
         w_t1=as_dtype_values(normal(seed, "w_t1", (c, TIME_EMB_DIM), std=WEIGHT_STD), dtype),
         w_t2=as_dtype_values(normal(seed, "w_t2", (6 * c, c), std=WEIGHT_STD), dtype),
         table=as_dtype_values(normal(seed, "mod_table", (wl.n_blocks, 6, c), std=MOD_STD), dtype))
+
+
+# ------------------------------------------------------------- output frames
+
+# 10 s request at 1344x768, 24 FPS: 243 decoded frames, one video
+FRAMES_10S = dict(B=1, T=243, H=768, W=1344)
+
+
+def frames(seed: int, B: int, T: int, H: int, W: int, specials: bool = True) -> np.ndarray:
+    """Decoded-video stand-in, float32 [B, 3, T, H, W].
+
+    Values are U[-1.05, 1.05) (about 5% outside the nominal [-1, 1] range).
+    With `specials`, a seeded 1/64 of the entries are replaced by boundary
+    cases: the exact grid points 2k/255 - 1 (as float32), the float32 values
+    nearest to the half-way points (2k + 1)/255 - 1, +-1, 0, +-inf and NaN.
+    """
+    shape = (B, 3, T, H, W)
+    x = uniform(seed, "frames", shape, -1.05, 1.05)
+    if specials and x.size:
+        k = np.arange(256, dtype=np.float64)
+        grid = (2.0 * k / 255.0 - 1.0).astype(np.float32)
+        half = (2.0 * (k + 0.5) / 255.0 - 1.0).astype(np.float32)
+        table = np.concatenate([grid, half, np.array([-1.0, 1.0, 0.0, np.inf, -np.inf, np.nan],
+                                                     dtype=np.float32)])
+        n = x.size
+        m = max(1, n // 64)
+        where = uniform_ints(seed, "frames.where", 0, n - 1, m)
+        which = uniform_ints(seed, "frames.which", 0, table.size - 1, m)
+        flat = x.reshape(-1)
+        flat[where] = table[which]
+    return x
+
