@@ -59,7 +59,7 @@ class BlockIO(ctypes.Structure):
                 ("cu_slots", _p), ("valid_len", _p), ("n_seg", _i32), ("max_valid_len", _i32),
                 ("n_tok_local", _i64), ("n_buf", _i64), ("tok_begin", _i64),
                 ("head_begin", _i32), ("head_count", _i32), ("qkv_attn", _p), ("o_attn", _p),
-                ("o_local", _p)]
+                ("o_local", _p), ("qkv_send", _p), ("o_recv", _p)]
 
 
 def _sig(name, res, args):
@@ -240,8 +240,13 @@ def block_workspace_size(cfg: BlockConfig, n_tok_local: int, n_buf: int, n_seg: 
 def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots, valid_len,
                          max_valid_len: int, ws=None, n_buf: Optional[int] = None,
                          tok_begin: int = 0, head_begin: int = 0, head_count: Optional[int] = None,
-                         qkv_attn=None, o_attn=None, o_local=None, stream=None):
-    """One block, x [n, C] updated in place.  mod is [n, 6, C] or [1, 6, C] (broadcast)."""
+                         qkv_attn=None, o_attn=None, o_local=None, qkv_send=None, o_recv=None,
+                         stream=None):
+    """One block, x [n, C] updated in place.  mod is [n, 6, C] or [1, 6, C] (broadcast).
+
+    Rank share: qkv_attn/o_attn with either o_local (heads of the other ranks
+    pre-filled) or the peer-major exchange buffers qkv_send [P, n, 3, hc, D]
+    and o_recv [P, n, hc, D] (blocks of the other ranks pre-filled)."""
     n = x.shape[0]
     share = qkv_attn is not None
     n_buf = n_buf if n_buf is not None else (qkv_attn.shape[0] if share else n)
@@ -251,7 +256,7 @@ def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots,
     io = BlockIO(_ptr(x), _ld(x), _ptr(mod), ld_mod, _ptr(pos), _ptr(cu_slots), _ptr(valid_len),
                  n_seg, max_valid_len, n, n_buf, tok_begin, head_begin,
                  head_count if head_count is not None else cfg.n_heads, _ptr(qkv_attn),
-                 _ptr(o_attn), _ptr(o_local))
+                 _ptr(o_attn), _ptr(o_local), _ptr(qkv_send), _ptr(o_recv))
     need = block_workspace_size(cfg, n, n_buf, n_seg)
     if ws is None:
         ws = _bytes_ws(need, x.device)

@@ -369,13 +369,26 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   const bool share = io->qkv_attn != nullptr;
   const int32_t hb = share ? io->head_begin : 0;
   const int32_t hc = share ? io->head_count : H;
+  const bool peer = io->qkv_send != nullptr || io->o_recv != nullptr;
   if (share) {
-    CHECK(io->o_attn && io->o_local, "rank-share mode needs qkv_attn, o_attn and o_local");
     CHECK(hc > 0 && hb >= 0 && hb + hc <= H, "head slice [%d, %d) outside [0, %d)", hb, hb + hc, H);
     CHECK(io->tok_begin >= 0 && io->tok_begin + n <= io->n_buf, "local rows outside the buffer");
-    CHECK(aligned16(io->qkv_attn) && aligned16(io->o_attn) && aligned16(io->o_local),
-          "exchange buffers must be 16-byte aligned");
+    if (peer) {
+      CHECK(io->qkv_send && io->o_recv && io->o_attn, "peer-major layout needs qkv_send, o_recv, o_attn");
+      CHECK(aligned16(io->qkv_attn) && aligned16(io->o_attn) && aligned16(io->qkv_send) &&
+                aligned16(io->o_recv),
+            "exchange buffers must be 16-byte aligned");
+      CHECK(dt == H3_BF16, "the peer-major layout is bf16 only");
+      CHECK(H % hc == 0 && hb % hc == 0, "head_count must divide n_heads and head_begin");
+      CHECK(io->tok_begin == (int64_t)(hb / hc) * n, "peer-major layout needs tok_begin == rank * n_tok_local");
+      CHECK(C % 64 == 0 && ((int64_t)hc * D) % 64 == 0, "peer-major layout needs dim and head_count*D multiples of 64");
+    } else {
+      CHECK(io->o_attn && io->o_local, "rank-share mode needs qkv_attn, o_attn and o_local");
+      CHECK(aligned16(io->qkv_attn) && aligned16(io->o_attn) && aligned16(io->o_local),
+            "exchange buffers must be 16-byte aligned");
+    }
   } else {
+    CHECK(!peer, "qkv_send/o_recv need rank-share mode (qkv_attn)");
     CHECK(io->tok_begin == 0 && io->n_buf == n && (io->head_count == H || io->head_count == 0) &&
               io->head_begin == 0,
           "world-1 mode needs tok_begin 0, n_buf == n_tok_local, full head range");
@@ -413,6 +426,54 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                                           mslot(1), ldm, h1, C, n, C, cfg->norm_kind,
                                           cfg->eps_mod, s),
                  "modulate-1"));
+  const float scale = 1.0f / std::sqrt((float)D);
+  if (peer) {
+    // Peer-major exchange layout: every all-to-all block is contiguous.
+    const int P = H / hc, r = hb / hc;
+    const int64_t sd = (int64_t)hc * D;  // slice width
+    char* send = (char*)io->qkv_send;
+    const int64_t blk = n * 3 * sd * es;  // bytes of one peer block of qkv_send
+    // A2 qkv = h1 w_qkv^T, scattered by its epilogue into [P][n][3][hc][D]
+    GemmMap scatter;
+    scatter.peer_H = H;
+    scatter.peer_hc = hc;
+    scatter.peer_D = D;
+    TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, send, 3 * hd, nullptr,
+                               0, n, (int)(3 * hd), C, s, scatter),
+                   "qkv projection (peer-major)"));
+    // A3 Q/K RMSNorm + RoPE on the local rows, one launch per peer block
+    for (int p = 0; p < P; ++p) {
+      char* b = send + p * blk;
+      TRY(hip_status(launch_qk_norm_rope(bf, D, b, 3 * sd, b + sd * es, 3 * sd, n, hc, w->g_q,
+                                         w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
+                                         cfg->eps_qk, s),
+                     "qk_norm_rope"));
+    }
+    // A4 the all-to-all's own block: rows [tok_begin, +n) of the attention buffer
+    char* qa = (char*)io->qkv_attn;
+    TRY(hip_status(hipMemcpyAsync(qa + io->tok_begin * 3 * sd * es, send + r * blk, blk,
+                                  hipMemcpyDeviceToDevice, s),
+                   "exchange-in self block"));
+    // A5 attention over the whole buffer for the head slice
+    TRY(hip_status(launch_varlen_attn(bf, D, qa, 3 * sd, qa + sd * es, 3 * sd, qa + 2 * sd * es,
+                                      3 * sd, io->o_attn, sd, io->n_buf, hc, io->cu_slots,
+                                      io->valid_len, io->n_seg, io->max_valid_len, scale,
+                                      attn_ws, s),
+                   "attention"));
+    // A6 the reverse all-to-all's own block: o_attn rows [tok_begin, +n) -> o_recv block r
+    const int64_t oblk = n * sd * es;
+    TRY(hip_status(hipMemcpyAsync((char*)io->o_recv + r * oblk,
+                                  (const char*)io->o_attn + io->tok_begin * sd * es, oblk,
+                                  hipMemcpyDeviceToDevice, s),
+                   "exchange-out self block"));
+    // A7 x <- x + gate1 * (o w_o^T), o read from [P][n][hc*D] as K groups of hc*D
+    GemmMap grouped;
+    grouped.a_kgroup = (int)sd;
+    grouped.a_gstride = n * sd;
+    TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, io->o_recv, sd, w->w_o, nullptr, hd, io->x,
+                               io->ld_x, mslot(2), ldm, n, C, (int)hd, s, grouped),
+                   "output projection (peer-major)"));
+  } else {
   // A2 qkv = h1 w_qkv^T
   TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, qkv, 3 * hd, nullptr, 0,
                              n, (int)(3 * hd), C, s),
@@ -422,7 +483,6 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                                      w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
                                      cfg->eps_qk, s),
                  "qk_norm_rope"));
-  const float scale = 1.0f / std::sqrt((float)D);
   const void* o_for_proj;
   if (!share) {
     // A5 attention straight from the QKV buffer
@@ -458,6 +518,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, o_for_proj, hd, w->w_o, nullptr, hd, io->x,
                              io->ld_x, mslot(2), ldm, n, C, (int)hd, s),
                  "output projection"));
+  }
   // A8 h2 = norm(x)(1 + scale2) + shift2   (h2 reuses h1's scratch)
   TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(3),
                                           mslot(4), ldm, h1, C, n, C, cfg->norm_kind,

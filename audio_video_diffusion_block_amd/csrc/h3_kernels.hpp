@@ -21,10 +21,24 @@ hipError_t launch_modulate_residual(bool bf16, void* x, int64_t ld_x, const void
                                     int64_t n_tok, int dim, int norm_kind, float eps,
                                     hipStream_t s);
 
+// Optional operand layouts of the bf16 K % 64 == 0 GEMM (sequence-parallel
+// exchange buffers).  All zero: plain row-major A and C.
+struct GemmMap {
+  // A is grouped along K: columns [g*a_kgroup, (g+1)*a_kgroup) of row m sit at
+  // A + g*a_gstride + m*lda (lda == a_kgroup); a_kgroup % 64 == 0
+  int a_kgroup = 0;
+  int64_t a_gstride = 0;
+  // EPI_STORE scatter: output column n = (which*H + h)*D + d of row m goes to
+  // C + ((p*M + m)*3 + which)*hc*D + j*D + d with h = p*hc + j (peer-major)
+  int peer_H = 0, peer_hc = 0, peer_D = 0;
+  bool empty() const { return a_kgroup == 0 && peer_hc == 0; }
+};
+
 // out = A @ B^T with epilogue; for EPI_SWIGLU, B = W1, B3 = W3 and N = features
 hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B,
                        const void* B3, int64_t ldb, void* C, int64_t ldc, const void* gate,
-                       int64_t ld_gate, int64_t M, int N, int K, hipStream_t s);
+                       int64_t ld_gate, int64_t M, int N, int K, hipStream_t s,
+                       const GemmMap& map = GemmMap{});
 
 size_t attn_workspace_bytes(bool bf16, int64_t n_buf, int n_heads, int head_dim, int n_seg);
 hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld_q,

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
     const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
     const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
-    int tiles_n) {
+    int tiles_n, GemmMap map) {
   // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
   // (256 x 264 bf16 or 128 x 264 fp32 = 135168 bytes)
   __shared__ __attribute__((aligned(1024))) char smem[135168];
@@ -279,10 +279,17 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds_addr) : "memory", "m0");
   };
+  // byte offset of K tile kt in A (grouped-K layouts jump between column groups)
+  auto a_koff = [&](int kt) -> int64_t {
+    const int k0 = kt * BK;
+    if (map.a_kgroup == 0) return (int64_t)k0 * 2;
+    const int g = k0 / map.a_kgroup;
+    return (g * map.a_gstride + (k0 - g * map.a_kgroup)) * 2;
+  };
   auto issue_dma = [&](int kt, int stage, int t) {
     const int koff = kt * BK * 2;
     if (t < 8) {
-      dma16(a_base + koff, a_off[t], lds0 + stage * W4_STAGE + wave * 8192 + t * 1024);
+      dma16(a_base + a_koff(kt), a_off[t], lds0 + stage * W4_STAGE + wave * 8192 + t * 1024);
     } else {
       const int j = t - 8;
       const char* src = (EPI == EPI_SWIGLU && j >= 4) ? b3_base : b_base;
@@ -435,6 +442,13 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
       if (row >= M || col >= N) continue;
       const bf16_t* src = eb + rl * ES + c8;
       bf16_t* po = C + (int64_t)row * ldc + col;
+      if (EPI == EPI_STORE && map.peer_hc) {
+        // peer-major scatter of an 8-column chunk (it never straddles a head)
+        const int hd = map.peer_H * map.peer_D, which = col / hd;
+        const int h = (col - which * hd) / map.peer_D, d = col - which * hd - h * map.peer_D;
+        const int p = h / map.peer_hc, j = h - p * map.peer_hc;
+        po = C + (((int64_t)p * M + row) * 3 + which) * map.peer_hc * map.peer_D + j * map.peer_D + d;
+      }
       if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
       else for (int e = 0; col + e < N; ++e) po[e] = src[e];
     }
@@ -496,8 +510,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 
 hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B,
                        const void* B3, int64_t ldb, void* C, int64_t ldc, const void* gate,
-                       int64_t ld_gate, int64_t M, int N, int K, hipStream_t s) {
+                       int64_t ld_gate, int64_t M, int N, int K, hipStream_t s,
+                       const GemmMap& map) {
   if (M == 0 || N == 0) return hipSuccess;
+  // operand maps exist only on the bf16 K % 64 kernel (and a scatter only for plain stores)
+  if (!map.empty() && (!bf16 || K < BK || K % BK != 0 || (map.a_kgroup % BK) != 0 ||
+                       (map.peer_hc && epi != EPI_STORE)))
+    return hipErrorInvalidValue;
   if (bf16) {
     const int tiles_m = (int)ceil_div(M, BM);
     const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : BN);
@@ -506,7 +525,7 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
   if (K >= BK && K % BK == 0)                                                                   \
     hipLaunchKernelGGL((gemm_bf16_w4_kernel<E>), grid, dim3(W4_THREADS), 0, s, (const bf16_t*)A, \
                        lda, (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,           \
-                       (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n);            \
+                       (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n, map);       \
   else                                                                                           \
     hipLaunchKernelGGL((gemm_bf16_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, lda, \
                        (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,                \

@@ -376,6 +376,18 @@ def main():
     sw_ws = torch.empty(h3.swiglu_workspace_size(wl.n_loc, wl.ffn_dim, bf), dtype=torch.uint8, device="cuda")
     ops["swiglu_residual"] = timer.time(lambda: h3.h3_swiglu(
         h1, wd["w1"], wd["w3"], wd["w2"], xs, gate=mod[:, 5], ws=sw_ws), reps)
+    if wl.share_mode:
+        # the same block with the peer-major exchange buffers (QKV epilogue writes the
+        # all-to-all send layout, the output projection reads the receive layout)
+        P = wl.sp_degree
+        peer = dict(qkv_attn=share["qkv_attn"], o_attn=share["o_attn"],
+                    qkv_send=torch.empty((P, wl.n_loc, 3, hc, D), dtype=bf, device="cuda"),
+                    o_recv=share["o_local"].reshape(wl.n_loc, P, hc * D).transpose(0, 1).contiguous(),
+                    tok_begin=wl.tok_begin, head_begin=wl.head_begin, head_count=hc)
+        xp = x0.clone()
+        ops["block_peer_major"] = timer.time(lambda: h3.h3_dit_block_forward(
+            cfg, wd, xp, mod, pos, cu, vl, max_len, ws=ws, **peer), reps)
+        del peer, xp
     # post-DiT tail: the 10 s request's decoded frames (1344x768, 243 frames) to uint8 BTHWC
     fr = W.FRAMES_10S
     frames = torch.rand((fr["B"], 3, fr["T"], fr["H"], fr["W"]), device="cuda") * 2.1 - 1.05
@@ -397,6 +409,10 @@ def main():
                     "frac_hbm": work["modnorm_bytes"] / ops["modnorm"] / 1e6 / HBM_PEAK_GBS},
         "qk_norm_rope": {"ms": ops["qk_norm_rope"], "GB/s": work["qknorm_bytes"] / ops["qk_norm_rope"] / 1e6,
                          "frac_hbm": work["qknorm_bytes"] / ops["qk_norm_rope"] / 1e6 / HBM_PEAK_GBS},
+        "block_peer_major": ({"ms": ops["block_peer_major"],
+                              "layout": "qkv_send [P,n,3,hc,D] from the QKV epilogue, o_recv [P,n,hc*D] "
+                                        "read in place by the output projection"}
+                             if "block_peer_major" in ops else None),
         "frames_u8": {"ms": ops["frames_u8"], "GB/s": frames_bytes / ops["frames_u8"] / 1e6,
                       "frac_hbm": frames_bytes / ops["frames_u8"] / 1e6 / HBM_PEAK_GBS,
                       "workload": "10 s decoded video, 243 x 3 x 768 x 1344 fp32 -> uint8 BTHWC"},

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 1
+#define H3_ABI_VERSION 2
 
 typedef enum {
   H3_OK = 0,
@@ -225,6 +225,23 @@ typedef struct {
   void* qkv_attn;       /* [n_buf, 3, head_count, D]; rows [tok_begin, +n_tok_local) are written */
   void* o_attn;         /* [n_buf, head_count, D]; written by attention */
   void* o_local;        /* [n_tok_local, H, D]; heads [head_begin, +head_count) are written */
+  /* Peer-major exchange layout (rank-share mode, bf16; optional: both NULL
+   * selects the qkv_attn/o_local form above).  Each all-to-all around
+   * attention then moves one contiguous, equal block per peer and nothing is
+   * rearranged before or after it ([RT-H3] Key takeaways: Fast Ulysses
+   * avoids layout rearrangement around the all-to-all).  With P = n_heads /
+   * head_count peers, this rank r = head_begin / head_count, and tok_begin ==
+   * r * n_tok_local:
+   *   qkv_send [P, n_tok_local, 3, head_count, D]: written by the QKV
+   *     projection's epilogue; block p holds heads [p*hc, (p+1)*hc), the part
+   *     peer p receives.  Block r is copied to qkv_attn rows [tok_begin, ...).
+   *   o_recv [P, n_tok_local, head_count, D]: block p is peer p's attention
+   *     output for the local rows (the reverse all-to-all delivers blocks
+   *     p != r; the caller provides them).  Block r is copied from o_attn,
+   *     and the output projection reads o_recv in place.  o_local is unused.
+   * Needs dim % 64 == 0 and head_count*D % 64 == 0. */
+  void* qkv_send;
+  void* o_recv;
 } h3_block_io;
 
 /*

@@ -41,3 +41,21 @@ def assert_close(got, ref, dtype: str, what: str = "", **override):
     print(f"[{what}] {dtype} " + " ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
     assert not bad, f"{what}: {bad}"
     return e
+
+
+def share_buffers(wl, bi, dtype, peer=False):
+    """The rank-share exchange buffers with the other ranks' rows/heads in place:
+    the qkv_attn/o_local stand-in, or the peer-major qkv_send/o_recv layout."""
+    P, hc, D, n = wl.sp_degree, wl.head_count, wl.head_dim, wl.n_loc
+    extra = dict(qkv_attn=dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), dtype),
+                 o_attn=torch.zeros((wl.n_pad_total, hc * D), dtype=TORCH_DT[dtype], device="cuda"),
+                 tok_begin=wl.tok_begin, head_begin=wl.head_begin, head_count=hc)
+    if peer:
+        # o_recv[p, t] = heads [p*hc, (p+1)*hc) of local row t (block `rank` is overwritten)
+        o_recv = np.ascontiguousarray(bi.o_local.reshape(n, P, hc, D).transpose(1, 0, 2, 3))
+        extra.update(qkv_send=torch.full((P, n, 3, hc, D), float("nan"), dtype=TORCH_DT[dtype],
+                                         device="cuda"),
+                     o_recv=dev(o_recv, dtype))
+    else:
+        extra.update(o_local=dev(bi.o_local.reshape(n, -1), dtype))
+    return extra

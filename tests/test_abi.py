@@ -32,7 +32,13 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
     import audio_video_diffusion_block_amd as h3
     assert set(declared_symbols()) == set(h3.EXPORTED)
-    assert h3.abi_version() == 1
+    declared = int(re.search(r"#define H3_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert h3.abi_version() == declared
+    # the binding's struct mirrors the header's h3_block_io field for field
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} h3_block_io;", text).group(1)
+    fields = re.findall(r"\b([a-z_0-9]+)\s*;", body)
+    assert fields == [f[0] for f in h3.BlockIO._fields_]
 
 
 def test_status_strings():
@@ -129,3 +135,29 @@ def test_frames_argument_checks():
     st = h3._c_frames(FAKE, -1, 2, 4, 16, FAKE + (1 << 20), 0, None)
     assert st == h3.H3_ERR_ARG
     assert h3._c_frames(None, 1, 0, 4, 16, None, 0, None) == h3.H3_OK  # empty: nothing launched
+
+
+def test_peer_major_layout_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    cfg = h3.BlockConfig(256, 4, 64, 704, 16, 24, 24, 1e4, 1e-6, 1e-6, 0, h3.H3_BF16)
+    w = h3.BlockWeights(*([FAKE] * 7))
+
+    def io(**kw):
+        base = dict(x=FAKE, ld_x=256, mod=FAKE, ld_mod=0, pos=FAKE, cu_slots=FAKE, valid_len=FAKE,
+                    n_seg=1, max_valid_len=64, n_tok_local=16, n_buf=64, tok_begin=32,
+                    head_begin=2, head_count=1, qkv_attn=FAKE, o_attn=FAKE, o_local=None,
+                    qkv_send=FAKE, o_recv=FAKE)
+        base.update(kw)
+        return h3.BlockIO(**base)
+
+    ws = h3.block_workspace_size(cfg, 16, 64, 1)
+
+    def run(i, c=cfg):
+        return h3._c_block(ctypes.byref(c), ctypes.byref(w), ctypes.byref(i), FAKE, ws, None)
+
+    assert run(io(tok_begin=16)) == h3.H3_ERR_ARG and "tok_begin" in h3.last_error()
+    assert run(io(o_recv=None)) == h3.H3_ERR_ARG and "o_recv" in h3.last_error()
+    assert run(io(qkv_attn=None, n_buf=16, tok_begin=0, head_begin=0, head_count=4)) == h3.H3_ERR_ARG
+    f32 = h3.BlockConfig(256, 4, 64, 704, 16, 24, 24, 1e4, 1e-6, 1e-6, 0, h3.H3_F32)
+    assert run(io(), f32) == h3.H3_ERR_ARG and "bf16" in h3.last_error()
+

@@ -5,7 +5,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from _util import assert_close, dev, dev_i32, host, TORCH_DT
+from _util import assert_close, dev, dev_i32, host, share_buffers, TORCH_DT
 
 pytestmark = pytest.mark.gpu
 
@@ -19,16 +19,10 @@ def cfg_of(lib, wl, dtype):
                             wl.eps_qk, wl.eps_mod, 0, TORCH_DT[dtype])
 
 
-def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None):
+def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=False):
     x = dev(bi.x if x_override is None else x_override, dtype)
     mod = dev(bi.mod if mod_override is None else mod_override, dtype)
-    extra = {}
-    if wl.share_mode:
-        extra = dict(qkv_attn=dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), dtype),
-                     o_attn=torch.zeros((wl.n_pad_total, wl.head_count * wl.head_dim),
-                                        dtype=TORCH_DT[dtype], device="cuda"),
-                     o_local=dev(bi.o_local.reshape(wl.n_loc, -1), dtype),
-                     tok_begin=wl.tok_begin, head_begin=wl.head_begin, head_count=wl.head_count)
+    extra = share_buffers(wl, bi, dtype, peer) if wl.share_mode else {}
     lib.h3_dit_block_forward(cfg_of(lib, wl, dtype), weights_dev(w, dtype), x, mod, dev_i32(bi.pos),
                              dev_i32(bi.cu_slots), dev_i32(bi.valid_len), int(bi.valid_len.max()),
                              **extra)
@@ -114,6 +108,20 @@ def test_block_tiny_rank_share(lib, dtype):
         got = run_block(lib, wl, w, bi, dtype)
         ref = oracle_block(wl, w, bi)
         check_block(got, ref, bi.x, dtype, f"block share r{rank}")
+
+
+def test_block_tiny_peer_major_layout(lib):
+    """Peer-major exchange buffers (QKV epilogue scattering into the all-to-all send
+    layout, output projection reading the receive layout in place) give exactly
+    the stand-in result, and so match the oracle."""
+    for rank in (0, 2, 3):
+        wl = W.TINY.replace(sp_degree=4, rank=rank)
+        w = W.block_weights(wl, 4, "bf16")
+        bi = W.block_inputs(wl, 4, "bf16")
+        ref_gpu = run_block(lib, wl, w, bi, "bf16")
+        got = run_block(lib, wl, w, bi, "bf16", peer=True)
+        assert np.array_equal(got, ref_gpu), f"rank {rank}"
+        check_block(got, oracle_block(wl, w, bi), bi.x, "bf16", f"block peer-major r{rank}")
 
 
 def test_block_deterministic(lib):

@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from _util import assert_close, dev, dev_i32, host
+from _util import assert_close, dev, dev_i32, host, share_buffers
 
 pytestmark = pytest.mark.gpu
 
@@ -73,3 +73,22 @@ def test_block_share_sampled(lib, share):
     ref = O.dit_block(bi.x, bi.mod, w, bi.pos, bi.cu_slots, bi.valid_len, O.BlockShape.of(wl),
                       bi.qkv_attn, bi.o_local, rows=rows)
     assert_close(got, ref, "bf16", f"block {wl.name} sampled")
+
+
+def test_block_share_peer_major_matches(lib, share):
+    """Peer-major exchange layout at full size: bit-identical to the stand-in form."""
+    wl, w, bi = share
+    wd = {k: dev(getattr(w, k), "bf16") for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")}
+    cfg = lib.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
+                           wl.eps_qk, wl.eps_mod, 0, torch.bfloat16)
+    outs = []
+    for peer in (False, True):
+        print(f"block {wl.name} peer={peer}", flush=True)
+        x = dev(bi.x, "bf16")
+        lib.h3_dit_block_forward(cfg, wd, x, dev(bi.mod, "bf16"), dev_i32(bi.pos),
+                                 dev_i32(bi.cu_slots), dev_i32(bi.valid_len),
+                                 int(bi.valid_len.max()), **share_buffers(wl, bi, "bf16", peer))
+        torch.cuda.synchronize()
+        outs.append(x)
+    assert torch.equal(outs[0], outs[1])
+
