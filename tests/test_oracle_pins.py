@@ -659,3 +659,65 @@ def test_frames_monotone_and_layouts_agree():
     assert np.all(np.diff(u.astype(np.int32)) >= 0)
     # uint8 BTHWC is the contiguous, interleaved layout
     assert a.flags["C_CONTIGUOUS"] and a.shape == (B, T, H, Wd, 3)
+
+
+# ----------------------------------------- FP8 (MX e4m3) operands (f)
+
+def _e4m3_decode(code: int) -> float:
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 0:
+        return s * m * 2.0 ** -9
+    return s * (1 + m / 8) * 2.0 ** (e - 7)
+
+
+def test_e4m3_grid_fixed_points_and_ties():
+    vals = sorted({_e4m3_decode(c) for c in range(256) if (c & 0x7F) != 0x7F})
+    assert max(vals) == 448.0 and min(v for v in vals if v > 0) == 2.0 ** -9
+    v = np.array(vals)
+    np.testing.assert_array_equal(O.e4m3_round(v), v)
+    pos = v[v >= 0]
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = O.e4m3_round(mids)
+    # each midpoint goes to the neighbour whose code (mantissa) is even
+    codes = {_e4m3_decode(c): c for c in range(0x7F)}
+    for m, lo, hi, g in zip(mids, pos[:-1], pos[1:], got):
+        even = lo if codes[lo] % 2 == 0 else hi
+        assert g == even, (m, lo, hi, g)
+    assert O.e4m3_round(np.array([460.0, 464.0]))[1] == 448.0
+
+
+def test_e8m0_rule_against_search():
+    a = np.concatenate([rng.uniform(0, 1, 500) * 10.0 ** rng.integers(-6, 6, 500),
+                        [448.0, 448.0 * 2 ** -3, np.nextafter(448.0, 1e9), 1.0, 0.0]])
+    got = O.e8m0_exponent(a)
+    for ai, gi in zip(a, got):
+        want = 0 if ai == 0 else min(e for e in range(-127, 128) if ai <= 448.0 * 2.0 ** e)
+        assert gi == want, (ai, gi, want)
+
+
+def test_mx_quantize_error_bound_and_top_binade():
+    x = (rng.standard_normal((8, 128)) * 10.0 ** rng.integers(-3, 3, (8, 1))).astype(np.float32)
+    q, e = O.mx_quantize(x)
+    d = O.mx_dequantize(q, e)
+    xb = x.astype(np.float64).reshape(8, 4, 32)
+    amax = np.abs(xb).max(-1)
+    # the block's largest magnitude lands in the top binade of e4m3 (224..448]
+    assert np.all(amax / np.ldexp(1.0, e) > 224.0) and np.all(amax / np.ldexp(1.0, e) <= 448.0)
+    # rounding error: half a quantum of the element's binade (relative 2^-4), or 2^-10 * 2^e below normals
+    err = np.abs(d - x).reshape(8, 4, 32)
+    bound = np.maximum(np.abs(xb) * 2.0 ** -4, np.ldexp(1.0, e)[..., None] * 2.0 ** -10)
+    assert np.all(err <= bound + 1e-300)
+
+
+def test_fp8_operand_attention_close_to_exact():
+    case = W.varlen_case(seed=5, lengths=(100, 37), n_buf=160, n_heads=2, head_dim=64, dtype="bf16")
+    ref = O.varlen_attention(case.q, case.k, case.v, case.cu_slots, case.valid_len)
+    got = O.varlen_attention_fp8_operands(case.q, case.k, case.v, case.cu_slots, case.valid_len)
+    valid = np.zeros(case.q.shape[0], bool)
+    for s in range(len(case.valid_len)):
+        valid[case.cu_slots[s]:case.cu_slots[s] + case.valid_len[s]] = True
+    diff = np.abs(got[valid] - ref[valid])
+    assert diff.max() < 0.1 and diff.mean() < 0.01
+    # the quantization changes the result (this is not the exact path)
+    assert diff.max() > 1e-4
