@@ -97,12 +97,17 @@ _c_temb = _sig("h3_timestep_modulation", ctypes.c_int,
                [_f, _p, _p, _p, _p, _i32, _i32, _i32, _p, _sz, _i32, _p])
 _c_euler = _sig("h3_euler_update", ctypes.c_int, [_p, _p, _p, _i64, _f, _f, _i32, _p])
 _c_frames = _sig("h3_frames_to_u8", ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _i32, _p])
+_c_attn8_ws = _sig("h3_varlen_attn_fp8_workspace_size", _sz, [_i64, _i32, _i32, _i32])
+_c_attn8 = _sig("h3_varlen_attn_fp8", ctypes.c_int,
+                [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _f,
+                 _p, _sz, _i32, _p])
 
 EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_rope",
             "h3_varlen_attn_workspace_size", "h3_varlen_attn", "h3_modulate_residual",
             "h3_linear", "h3_swiglu_workspace_size", "h3_swiglu", "h3_dit_block_workspace_size",
             "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
-            "h3_euler_update", "h3_frames_to_u8")
+            "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
+            "h3_varlen_attn_fp8")
 
 
 def _status_string(st: int) -> str:
@@ -186,6 +191,25 @@ def h3_varlen_attn(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tens
                    n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
                    softmax_scale, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
                    _stream(stream)))
+
+
+def varlen_attn_fp8_workspace_size(n_buf: int, n_heads: int, head_dim: int, n_seg: int) -> int:
+    return _c_attn8_ws(n_buf, n_heads, head_dim, n_seg)
+
+
+def h3_varlen_attn_fp8(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tensor,
+                       valid_len: Optional[torch.Tensor], max_valid_len: int,
+                       softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None, stream=None):
+    """h3_varlen_attn with MX-scaled e4m3 operands (bf16 in, bf16 out)."""
+    n_buf = q.shape[0]
+    n_seg = cu_slots.shape[0] - 1
+    need = varlen_attn_fp8_workspace_size(n_buf, n_heads, head_dim, n_seg)
+    if ws is None:
+        ws = _bytes_ws(need, q.device)
+    _check(_c_attn8(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
+                    n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
+                    softmax_scale, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
+                    _stream(stream)))
 
 
 def h3_modulate_residual(x, y=None, gate=None, shift=None, scale=None, h_out=None,

@@ -122,7 +122,7 @@ h3_status validate_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t n_to
 h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
                         int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf, int32_t H,
                         int32_t D, const int32_t* cu, int32_t n_seg, int32_t max_len,
-                        void* ws, size_t ws_bytes, h3_dtype dt) {
+                        void* ws, size_t ws_bytes, h3_dtype dt, bool fp8 = false) {
   TRY(check_dtype(dt));
   CHECK(n_buf >= 0 && n_buf < (int64_t)INT32_MAX, "n_buf out of range");
   CHECK(H > 0, "n_heads must be positive");
@@ -139,7 +139,8 @@ h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k
   CHECK(ld_q > 0 && ld_k > 0 && ld_v > 0 && ld_o > 0, "row strides must be positive");
   // the bf16 kernel addresses a 64-row key tile and the transposed-V scratch with 32-bit byte offsets
   CHECK(ld_k <= (1 << 23) && n_buf <= (1 << 22), "row stride above 2^23 or n_buf above 2^22");
-  const size_t need = h3::attn_workspace_bytes(dt == H3_BF16, n_buf, H, D, n_seg);
+  const size_t need = fp8 ? h3::attn_fp8_workspace_bytes(n_buf, H, D, n_seg)
+                         : h3::attn_workspace_bytes(dt == H3_BF16, n_buf, H, D, n_seg);
   if (ws_bytes < need)
     return fail(H3_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu", ws_bytes, need);
   CHECK(need == 0 || (ws && aligned16(ws)), "workspace is NULL or not 16-byte aligned");
@@ -246,6 +247,31 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
                                        ld_o, n_buf, n_heads, cu_slots, valid_len, n_seg,
                                        max_valid_len, scale, ws, (hipStream_t)stream),
                     "varlen_attn launch");
+}
+
+size_t h3_varlen_attn_fp8_workspace_size(int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                         int32_t n_seg) {
+  if (n_buf <= 0 || n_heads <= 0 || head_dim <= 0 || n_seg <= 0) return 0;
+  return attn_fp8_workspace_bytes(n_buf, n_heads, head_dim, n_seg);
+}
+
+h3_status h3_varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                             const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
+                             int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
+                             const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
+                             float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
+                             void* stream) {
+  g_err[0] = 0;
+  if (dtype != H3_BF16) return fail(H3_ERR_UNSUPPORTED, "the FP8 attention takes bf16 operands");
+  TRY(validate_attn(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, head_dim, cu_slots, n_seg,
+                    max_valid_len, ws, ws_bytes, dtype, true));
+  if (n_buf == 0) return H3_OK;
+  TRY(check_device());
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  return hip_status(launch_varlen_attn_fp8(head_dim, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf,
+                                           n_heads, cu_slots, valid_len, n_seg, max_valid_len,
+                                           scale, ws, (hipStream_t)stream),
+                    "varlen_attn_fp8 launch");
 }
 
 h3_status h3_modulate_residual(void* x, int64_t ld_x, const void* y, int64_t ld_y,

@@ -743,4 +743,539 @@ hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld
                            n_seg, max_len, scale, ws, s);
 }
 
+
+// ================================================================== FP8 path
+//
+// MiniMax H3 通过 vLLM-Omni 实现 FastH3 实时推理, "FastH3 推理配置" (sparse and
+// quantized attention): an FP8 attention path (SAGE FP8) speeds up the base
+// pipeline at small quality cost.  The pages give no algorithm; this path
+// stores Q (softmax scale and log2 e folded in), K and V as OCP e4m3 with one
+// power-of-two (E8M0) scale per 32 elements along the contraction (head dim
+// for Q and K, keys for V), and rounds the probabilities to e4m3 as 256 * p.
+//
+// gfx950 v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 accumulation):
+// A lane (row + 32 h) byte e pairs with B lane (col + 32 h) byte e; bytes 0-15
+// of both lane halves form the first 32-element block of the contraction
+// (E8M0 scale taken from the row's lane), bytes 16-31 the second (scale from
+// lane row + 32).  The logical contraction index of (h, e) is therefore
+// 32 (e / 16) + 16 h + e % 16, and a 64-deep step covers two scale blocks.
+
+namespace {
+// smallest e in [-127, 127] with amax <= 448 * 2^e (0 for an all-zero block):
+// amax = 1.f * 2^E needs e = E - 8, or E - 7 when 1.f > 1.75
+__device__ __forceinline__ int e8m0_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)(b >> 23) - 127;
+  if (E == -127) return -127;
+  const int e = E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// four values times the power of two s -> four e4m3 bytes (nearest, ties to even)
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d, float s) {
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a * s, b * s, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c * s, d * s, (int)w, true);
+}
+
+// 32 floats -> 32 e4m3 bytes (8 words) and their E8M0 byte
+__device__ __forceinline__ uint32_t quant32(const float* v, uint32_t* w) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = e8m0_exp(amax);
+  const float s = __builtin_ldexpf(1.0f, -e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = pack4_e4m3(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], s);
+  return (uint32_t)(e + 127);
+}
+}  // namespace
+
+// Rows of a head slice (bf16, row stride ld, head h at columns h*D), times
+// `fold` (one fp32 rounding) -> e4m3 [heads][n_buf][D] and E8M0 bytes
+// [heads][n_buf][D/32] stored even blocks first, then odd blocks (lane half h
+// of the MFMA takes blocks 2t + h).  Rows outside every segment's valid range
+// are written as zeros (scale byte 127).  One thread per 32-element block.
+template <int D>
+__global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const bf16_t* __restrict__ x,
+                                                              int64_t ld, int64_t n_buf, int heads,
+                                                              const int* cu, const int* valid,
+                                                              int n_seg, float fold,
+                                                              uint8_t* __restrict__ q8,
+                                                              uint8_t* __restrict__ sc) {
+  constexpr int NB = D / 32;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)heads * n_buf * NB) return;
+  const int blk = (int)(t % NB);
+  const int64_t hr = t / NB;
+  const int64_t row = hr % n_buf;
+  const int head = (int)(hr / n_buf);
+  const int s = find_segment(cu, n_seg, row);
+  const bool ok = s >= 0 && row - cu[s] < seg_valid(cu, valid, s);
+  uint4* dst = reinterpret_cast<uint4*>(q8 + ((int64_t)head * n_buf + row) * D + blk * 32);
+  uint8_t* sdst = sc + ((int64_t)head * n_buf + row) * NB + (blk & 1) * (NB / 2) + (blk >> 1);
+  if (!ok) {
+    dst[0] = make_uint4(0, 0, 0, 0);
+    dst[1] = make_uint4(0, 0, 0, 0);
+    *sdst = 127;
+    return;
+  }
+  const uint4* src = reinterpret_cast<const uint4*>(x + row * ld + head * D + blk * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * i + 2 * k] = __uint_as_float(ws[k] << 16) * fold;
+      v[8 * i + 2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u) * fold;
+    }
+  }
+  uint32_t w[8];
+  *sdst = (uint8_t)quant32(v, w);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// V [rows, heads*D] (row stride ld_v) -> V^T e4m3 [heads][D][cols] with the
+// columns of vt_segment_base, and E8M0 bytes [heads][cols/32][D] (one per
+// 32 keys and dimension).  Keys past the valid length are zeros.  One
+// work-group transposes 64 keys x D dims of one head.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_quant_v_kernel(const bf16_t* __restrict__ v,
+                                                                int64_t ld_v,
+                                                                uint8_t* __restrict__ vt8,
+                                                                uint8_t* __restrict__ vts,
+                                                                int64_t cols, const int* cu,
+                                                                const int* valid) {
+  __shared__ float tile[64][D + 1];
+  const int s = blockIdx.y;
+  const int head = blockIdx.z;
+  const int lo = cu[s];
+  const int len = seg_valid(cu, valid, s);
+  const int j0 = blockIdx.x * 64;
+  if (j0 >= len) return;
+  constexpr int CPR = D / 8;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, c = i % CPR;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (j0 + r < len)
+      val = *reinterpret_cast<const uint4*>(v + (int64_t)(lo + j0 + r) * ld_v + head * D + c * 8);
+    const uint32_t ws[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tile[r][c * 8 + 2 * k] = __uint_as_float(ws[k] << 16);
+      tile[r][c * 8 + 2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u);
+    }
+  }
+  __syncthreads();
+  const int64_t base = vt_segment_base(lo, s) + j0;  // a multiple of 64
+  for (int i = threadIdx.x; i < 2 * D; i += 256) {
+    const int d = i % D, b = i / D;
+    float vv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) vv[k] = tile[b * 32 + k][d];
+    uint32_t w[8];
+    const uint32_t e = quant32(vv, w);
+    uint4* dst = reinterpret_cast<uint4*>(vt8 + ((int64_t)head * D + d) * cols + base + b * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    vts[((int64_t)head * (cols / 32) + (base / 32) + b) * D + d] = (uint8_t)e;
+  }
+}
+
+
+// FP8 flash attention.  Same work split, phase rotation and 4-stage LDS ring
+// as the bf16 kernel; per 64-key tile a wave runs 2*(D/64) MFMAs for S and
+// D/32 for P.V, each 64 deep.
+//  * Scores: S^T = K Q^T with K rows read in the order sigma8 below, so the
+//    accumulator register r of lane half h in key block kb holds key
+//    32 kb + 16 h + r -- exactly the byte (16 kb + r) the P.V MFMA expects in
+//    its B operand.  P never leaves registers.
+//  * The scores come out in log2 units (the softmax scale and log2 e are in
+//    Q).  The running max is raised whenever a tile exceeds it by more than
+//    0.75, so p <= 2^0.75 and 256 p <= 431 stays in e4m3 range.  The kernel
+//    computes 256 p = exp2(s - (m - 8)) directly and stores it as e4m3 with
+//    scale byte 127; O and the row sums (fp32 256 p) share the factor 256.
+//  * LDS rows are padded (K: D + 16 bytes, V^T: 64 + 16) so each 16-lane
+//    group of a 16-byte fragment read covers 16 distinct bank groups.
+namespace {
+// K row read into A-operand row rho of a 32-key block
+__device__ __forceinline__ int sigma8(int rho) {
+  return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+}
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+// 32 wait states: VALU code that reads or rewrites the accumulators of a
+// v_mfma_scale_f32_32x32x64_f8f6f4 issued just before (the compiler's own
+// padding after this instruction has been measured to be too short: the
+// last result registers were read stale)
+__device__ __forceinline__ void scaled_mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// scaled e4m3 x e4m3 MFMA whose operands' scale bytes sit at byte SEL of the scale registers
+template <int SEL>
+__device__ __forceinline__ f32x16_t mfma_e4m3(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c,
+                                             uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, (int)sa, SEL, (int)sb);
+}
+__device__ __forceinline__ i32x8_t frag32(const uint8_t* p0, const uint8_t* p1) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p0);
+  const uint4 b = *reinterpret_cast<const uint4*>(p1);
+  i32x8_t r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+  return r;
+}
+}  // namespace
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qs,
+    const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ks, int64_t n_buf,
+    const uint8_t* __restrict__ vt8, const uint8_t* __restrict__ vts, int64_t vt_cols,
+    bf16_t* __restrict__ o, int64_t ld_o, const int* __restrict__ cu,
+    const int* __restrict__ valid) {
+  constexpr int BMQ = NW * 32;
+  constexpr int NTH = NW * 64;
+  constexpr int NT = D / 64;          // 64-deep steps of S (1 or 2)
+  static_assert(NT == 1 || NT == 2, "head_dim 64 or 128");
+  constexpr int NB = D / 32;          // 32-element scale blocks of a head row
+  constexpr int KSTR = D + 16;        // K tile row stride (bytes)
+  constexpr int VSTR = KT + 16;       // V^T tile row stride (bytes)
+  constexpr int K_OFF = 0;
+  constexpr int V_OFF = KT * KSTR;
+  constexpr int KS_OFF = V_OFF + D * VSTR;  // K scales [KT][NB]
+  constexpr int VS_OFF = KS_OFF + KT * NB;  // V^T scales [2][D]
+  constexpr int STAGE = (VS_OFF + 2 * D + 15) / 16 * 16;
+  constexpr int NSTAGE = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE];
+
+  const int s = blockIdx.y;
+  const int head = blockIdx.z;
+  const int seg_lo = cu[s];
+  const int len = seg_valid(cu, valid, s);
+  const int q0 = blockIdx.x * BMQ;
+  if (q0 >= len) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qi = lane & 31;
+  const int hf = lane >> 5;
+  const int qrow = q0 + wave * 32 + qi;
+  const bool q_ok = qrow < len;
+  const int n_tiles = (len + KT - 1) / KT;
+
+  // ---- Q fragments (B operand of S) and their scale bytes, once
+  i32x8_t qf[NT];
+  uint32_t qsc = 0x7f7f7f7fu;
+  {
+    const uint8_t* qp = q8 + ((int64_t)head * n_buf + seg_lo + (q_ok ? qrow : 0)) * D + 16 * hf;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (q_ok) qf[t] = frag32(qp + 64 * t, qp + 64 * t + 32);
+      else
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[t][i] = 0;
+    }
+    if (q_ok) {
+      const uint8_t* sp = qs + ((int64_t)head * n_buf + seg_lo + qrow) * NB + hf * (NB / 2);
+      qsc = NB / 2 == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : (uint32_t)*sp;
+    }
+  }
+
+  // ---- tile loads: global -> registers -> LDS (one 16-byte chunk per thread
+  // of K and of V^T; 32 threads carry the two scale strips)
+  constexpr int KCH = KT * D / 16;   // 16-byte chunks of a K tile
+  constexpr int VCH = D * KT / 16;   // of a V^T tile
+  static_assert(KCH <= NTH && VCH <= NTH, "one chunk per thread");
+  const char* kbase = reinterpret_cast<const char*>(k8 + ((int64_t)head * n_buf + seg_lo) * D);
+  const char* ksb = reinterpret_cast<const char*>(ks + ((int64_t)head * n_buf + seg_lo) * NB);
+  const int64_t vbase_col = vt_segment_base(seg_lo, s);
+  const char* vbase = reinterpret_cast<const char*>(vt8 + (int64_t)head * D * vt_cols + vbase_col);
+  const char* vsb = reinterpret_cast<const char*>(vts + ((int64_t)head * (vt_cols / 32) + vbase_col / 32) * D);
+  const int v_bytes = (int)(D * vt_cols);
+  const int k_r = tid / (D / 16), k_c = tid % (D / 16);
+  const int v_r = tid / (KT / 16), v_c = tid % (KT / 16);
+  uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0), rs = make_uint4(0, 0, 0, 0);
+  auto load_tile = [&](int jt) {
+    const int j0 = jt * KT;
+    const int nk = min(len - j0, KT);
+    if (tid < KCH)
+      rk = buf_load16(make_rsrc(kbase + (int64_t)j0 * D, nk * D), (k_r * D) + k_c * 16);
+    if (tid < VCH)
+      rv = buf_load16(make_rsrc(vbase + j0, v_bytes), v_r * (int)vt_cols + v_c * 16);
+    if (tid < 16) {
+      // K scales of the tile's rows: KT * NB bytes.  The range is rounded up to
+      // whole 16-byte chunks: the buffer range check zeroes a partly valid
+      // dword, which would drop the last valid key's scale when NB = 2.  Rows
+      // past the valid keys carry zero K data, so their scales are harmless.
+      rs = buf_load16(make_rsrc(ksb + (int64_t)j0 * NB, (nk * NB + 15) & ~15), tid * 16);
+    } else if (tid < 32) {
+      // V^T scales of the tile's two key blocks: 2 * D bytes
+      rs = buf_load16(make_rsrc(vsb + (int64_t)(j0 / 32) * D, 2 * D), (tid - 16) * 16);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    uint8_t* st = smem + stage * STAGE;
+    if (tid < KCH) *reinterpret_cast<uint4*>(st + K_OFF + k_r * KSTR + k_c * 16) = rk;
+    if (tid < VCH) *reinterpret_cast<uint4*>(st + V_OFF + v_r * VSTR + v_c * 16) = rv;
+    if (tid < 16) {
+      if (tid * 16 < KT * NB) *reinterpret_cast<uint4*>(st + KS_OFF + tid * 16) = rs;
+    } else if (tid < 32) {
+      if ((tid - 16) * 16 < 2 * D) *reinterpret_cast<uint4*>(st + VS_OFF + (tid - 16) * 16) = rs;
+    }
+  };
+
+  // ---- fragment addressing
+  const int k_row = sigma8(qi);
+  auto kfrag = [&](const uint8_t* st, int kb, int t) {
+    const uint8_t* p = st + K_OFF + (kb * 32 + k_row) * KSTR + 64 * t + 16 * hf;
+    return frag32(p, p + 32);
+  };
+  auto kscale = [&](const uint8_t* st, int kb) {
+    const uint8_t* p = st + KS_OFF + (kb * 32 + k_row) * NB + hf * (NB / 2);
+    return NB / 2 == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p) : (uint32_t)*p;
+  };
+  auto vfrag = [&](const uint8_t* st, int db) {
+    const uint8_t* p = st + V_OFF + (db * 32 + qi) * VSTR + 16 * hf;
+    return frag32(p, p + 32);
+  };
+  auto vscale = [&](const uint8_t* st, int db) {
+    return (uint32_t)st[VS_OFF + hf * D + db * 32 + qi];
+  };
+
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;
+  float m_ref = -INFINITY;  // m_run - 8: exp2(s - m_ref) = 256 p
+  float l_a = 0.f, l_b = 0.f;
+  constexpr uint32_t PSC = 127u;  // P is stored as 256 p; the row sums carry the same 256
+
+  auto mask_tile = [&](f32x16_t (&sc)[2], int jt) {
+    const int base = jt * KT;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (base + kb * 32 + 16 * hf + r >= len) sc[kb][r] = -INFINITY;
+  };
+  auto update_max = [&](float mx) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    const bool raise = mx > m_run + 0.75f;
+    if (__any(raise)) {
+      scaled_mfma_drain();
+      const float m_new = raise ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      m_ref = m_new - 8.0f;
+      l_a *= alpha;
+      l_b *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+  };
+  auto compute_s = [&](int stage, f32x16_t (&sc)[2]) {
+    const uint8_t* st = smem + stage * STAGE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      const uint32_t ksc = kscale(st, kb);
+      sc[kb] = mfma_e4m3<0>(kfrag(st, kb, 0), qf[0], sc[kb], ksc, qsc);
+      if constexpr (NT > 1) sc[kb] = mfma_e4m3<1>(kfrag(st, kb, 1), qf[NT - 1], sc[kb], ksc, qsc);
+    }
+  };
+
+  // P of the current tile, packed in the B-operand byte order of P.V
+  i32x8_t pw = {0, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int NA = 2 * NT;       // phase A MFMAs
+  constexpr int NBM = D / 32;      // phase B MFMAs
+  constexpr int SPS = 32 / NA;     // scores per phase-A slot (multiple of 4)
+  static_assert(SPS % 4 == 0, "slot holds whole packed words");
+  // phase A: S(next) MFMAs, each followed by 1/NA of the softmax of S(cur)
+  auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], f32x16_t (&cur)[2], int jt) {
+    const uint8_t* sk = smem + stage_k * STAGE;
+    __builtin_amdgcn_s_setprio(2);
+    uint32_t ksc[2];
+    ksc[0] = kscale(sk, 0);
+    ksc[1] = kscale(sk, 1);
+    i32x8_t kf = kfrag(sk, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nxt[0][r] = nxt[1][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int kb = i & 1, t = i >> 1;
+      const i32x8_t a = kf;
+      if (i + 1 < NA) kf = kfrag(sk, (i + 1) & 1, (i + 1) >> 1);
+      if (t == 0) nxt[kb] = mfma_e4m3<0>(a, qf[0], nxt[kb], ksc[kb], qsc);
+      else nxt[kb] = mfma_e4m3<1>(a, qf[NT - 1], nxt[kb], ksc[kb], qsc);
+#pragma unroll
+      for (int w4 = 0; w4 < SPS / 4; ++w4) {
+        const int word = i * (SPS / 4) + w4;  // packed word 0..7: scores 4*word .. 4*word+3
+        const int pkb = word >> 2, r0 = (word & 3) * 4;
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pv[u] = __builtin_amdgcn_exp2f(cur[pkb][r0 + u] - m_ref);  // 256 p
+          (u & 1 ? l_b : l_a) += pv[u];
+        }
+        // the first conversion's upper half is overwritten by the second
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pw[word], false);
+        pw[word] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], lo, true);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (jt + 1 < n_tiles && (jt + 2) * KT > len) {
+      scaled_mfma_drain();
+      mask_tile(nxt, jt + 1);
+    }
+  };
+  // phase B: P.V MFMAs, each followed by part of the row max of S(next)
+  auto phase_b = [&](int stage_v, f32x16_t (&nxt)[2], int jt, bool last = false) {
+    const uint8_t* sv = smem + stage_v * STAGE;
+    float mx = -INFINITY;
+    i32x8_t vf[NBM];
+    uint32_t vsc[NBM];
+#pragma unroll
+    for (int db = 0; db < NBM; ++db) {
+      vf[db] = vfrag(sv, db);
+      vsc[db] = vscale(sv, db);
+    }
+#pragma unroll
+    for (int db = 0; db < NBM; ++db) {
+      oacc[db] = mfma_e4m3<0>(vf[db], pw, oacc[db], vsc[db], PSC);
+#pragma unroll
+      for (int e = 0; e < 32 / NBM; ++e) {
+        const int idx = db * (32 / NBM) + e;
+        mx = fmaxf(mx, nxt[idx >> 4][idx & 15]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // after the last tile's P.V the epilogue reads O: let these MFMAs finish
+    if (last || jt + 1 >= n_tiles) scaled_mfma_drain();
+    if (jt + 1 < n_tiles) update_max(mx);
+  };
+
+  load_tile(0);
+  store_tile(0);
+  if (n_tiles > 1) {
+    load_tile(1);
+    store_tile(1);
+  }
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+  compute_s(0, sa);
+  if (n_tiles == 1) mask_tile(sa, 0);
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
+    update_max(mx);
+  }
+  if (n_tiles > 2) load_tile(2);
+
+  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
+  auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    if (lag && jt > 0) phase_b((jt - 1) % NSTAGE, cur, jt - 1);
+    phase_a((jt + 1) % NSTAGE, nxt, cur, jt);
+    if (!lag) phase_b(jt % NSTAGE, nxt, jt);
+    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
+    __syncthreads();
+    if (jt + 3 < n_tiles) load_tile(jt + 3);
+  };
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    step(jt, sa, sb);
+    if (jt + 1 >= n_tiles) break;
+    step(jt + 1, sb, sa);
+  }
+  // the lagging half's last P.V (its score argument is unused: no max follows)
+  if (lag) phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1, true);
+
+  const float l_run = l_a + l_b;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_ok) return;
+  const float inv = 1.0f / l_tot;
+  bf16_t* op = o + (int64_t)(seg_lo + qrow) * ld_o + head * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + hf * 4;
+      uint2 val;
+      val.x = cvt_pk_bf16(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+      val.y = cvt_pk_bf16(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = val;
+    }
+  }
+}
+
+// workspace: Q and K e4m3 [heads][n_buf][D] + scales, V^T e4m3 [heads][D][cols] + scales
+size_t attn_fp8_workspace_bytes(int64_t n_buf, int n_heads, int head_dim, int n_seg) {
+  const int64_t cols = vt_columns(n_buf, n_seg);
+  const int64_t qk = round_up((int64_t)n_heads * n_buf * head_dim, 256);
+  const int64_t qks = round_up((int64_t)n_heads * n_buf * (head_dim / 32), 256);
+  const int64_t vt = round_up((int64_t)n_heads * head_dim * cols, 256);
+  const int64_t vts = round_up((int64_t)n_heads * (cols / 32) * head_dim, 256);
+  return (size_t)(2 * qk + 2 * qks + vt + vts);
+}
+
+template <int D>
+static hipError_t launch_attn_fp8_d(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                                    const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                                    int64_t n_buf, int n_heads, const int* cu, const int* valid,
+                                    int n_seg, int max_len, float scale, void* ws,
+                                    hipStream_t s) {
+  if (n_buf == 0) return hipSuccess;
+  const unsigned zblocks = (unsigned)ceil_div(n_buf, 4);
+  hipLaunchKernelGGL((zero_pad_rows_kernel<bf16_t>), dim3(zblocks), dim3(256), 0, s,
+                     (bf16_t*)o, ld_o, n_buf, n_heads * D, cu, valid, n_seg);
+  if (max_len == 0) return hipGetLastError();
+  const int64_t cols = vt_columns(n_buf, n_seg);
+  uint8_t* w = (uint8_t*)ws;
+  const int64_t qk = round_up((int64_t)n_heads * n_buf * D, 256);
+  const int64_t qks = round_up((int64_t)n_heads * n_buf * (D / 32), 256);
+  const int64_t vt = round_up((int64_t)n_heads * D * cols, 256);
+  uint8_t *q8 = w, *k8 = w + qk, *qs = w + 2 * qk, *ks = w + 2 * qk + qks;
+  uint8_t *vt8 = w + 2 * qk + 2 * qks, *vts = vt8 + vt;
+  const int64_t nq = (int64_t)n_heads * n_buf * (D / 32);
+  const unsigned qblocks = (unsigned)ceil_div(nq, 256);
+  hipLaunchKernelGGL((quant_rows_e4m3_kernel<D>), dim3(qblocks), dim3(256), 0, s, (const bf16_t*)q,
+                     ld_q, n_buf, n_heads, cu, valid, n_seg, scale * 1.4426950408889634f, q8, qs);
+  hipLaunchKernelGGL((quant_rows_e4m3_kernel<D>), dim3(qblocks), dim3(256), 0, s, (const bf16_t*)k,
+                     ld_k, n_buf, n_heads, cu, valid, n_seg, 1.0f, k8, ks);
+  hipLaunchKernelGGL((transpose_quant_v_kernel<D>), dim3((unsigned)ceil_div(max_len, 64), n_seg, n_heads),
+                     dim3(256), 0, s, (const bf16_t*)v, ld_v, vt8, vts, cols, cu, valid);
+  constexpr int NW = 8;
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW>),
+                     dim3((unsigned)ceil_div(max_len, NW * 32), n_seg, n_heads), dim3(NW * 64), 0,
+                     s, q8, qs, k8, ks, n_buf, vt8, vts, cols, (bf16_t*)o, ld_o, cu, valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_attn_fp8(int head_dim, const void* q, int64_t ld_q, const void* k,
+                                  int64_t ld_k, const void* v, int64_t ld_v, void* o,
+                                  int64_t ld_o, int64_t n_buf, int n_heads, const int* cu,
+                                  const int* valid, int n_seg, int max_len, float scale, void* ws,
+                                  hipStream_t s) {
+  if (head_dim == 128)
+    return launch_attn_fp8_d<128>(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu, valid,
+                                  n_seg, max_len, scale, ws, s);
+  return launch_attn_fp8_d<64>(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu, valid,
+                               n_seg, max_len, scale, ws, s);
+}
+
 }  // namespace h3

@@ -131,6 +131,29 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
                          void* stream);
 
 /*
+ * h3_varlen_attn_fp8 -- the same attention with FP8 operands (MiniMax H3 通过
+ * vLLM-Omni 实现 FastH3 实时推理, "FastH3 推理配置": an FP8 attention path
+ * (SAGE FP8) speeds up the base pipeline at small quality cost).  Same
+ * arguments and output contract as h3_varlen_attn (bf16 q, k, v, o), except:
+ *   q (times softmax_scale * log2 e), k and v are rounded to OCP e4m3 with
+ *   one power-of-two scale per 32 elements along the contraction (head dim
+ *   for q and k, keys of each segment slot for v), and the softmax weights
+ *   are rounded to e4m3 (as 256 * p with scale 2^-8) before P.V.  Accumulation
+ *   is fp32.  The result approximates exact attention; it is not
+ *   bit-compatible with h3_varlen_attn.
+ *   ws: h3_varlen_attn_fp8_workspace_size(...) bytes (quantized operands).
+ *   Errors as h3_varlen_attn; H3_ERR_UNSUPPORTED unless dtype is H3_BF16.
+ */
+size_t h3_varlen_attn_fp8_workspace_size(int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                         int32_t n_seg);
+h3_status h3_varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                             const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
+                             int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
+                             const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
+                             float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
+                             void* stream);
+
+/*
  * h3_modulate_residual -- one pass over rows of width dim:
  *   if y != NULL:     x <- x + gate * y                       (gated residual)
  *   if h_out != NULL: h_out <- norm(x) * (1 + scale) + shift  (modulated norm)

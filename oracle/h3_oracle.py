@@ -468,16 +468,26 @@ def mx_dequantize(q, e, block: int = 32) -> np.ndarray:
     return (qb * np.ldexp(1.0, np.asarray(e))[..., None]).reshape(shp)
 
 
+def fp8_fold(head_dim: int) -> np.float32:
+    """The factor folded into Q: fp32 1/sqrt(D) (correctly rounded fp32 square
+    root and quotient) times fp32 log2(e), one fp32 product."""
+    inv = np.float32(1.0) / np.sqrt(np.float32(head_dim))
+    return np.float32(inv * np.float32(1.4426950408889634))
+
+
 def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None):
     """Attention over the MX-e4m3-quantized operands of the FP8 path, exact
-    otherwise (no rounding of the probabilities).  q, k, v [N, h, D] float32
-    values.  Q is quantized after folding scale * log2(e); the scores are then
+    otherwise (no rounding of the probabilities).  k, v [N, h, D] float32
+    values; q is [N, h, D], or [len(q_rows), h, D] already restricted to the
+    query rows q_rows (buffer rows).  Q is quantized after folding scale * log2(e); the scores are then
     in log2 units, and softmax uses base 2.  The FP8 kernel differs from this
     only by rounding 256 * p to e4m3 and by fp32 accumulation."""
     q = np.asarray(q, dtype=np.float32)
     D = q.shape[-1]
-    c = float(np.float32(1.0 / np.sqrt(D)) * np.float32(1.4426950408889634))
-    qq, qe = mx_quantize(q, fold=c)
+    c = float(fp8_fold(D))
+    rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
+    # Q is quantized row by row: only the rows asked for are needed
+    qsel = q if q_rows is None or q.shape[0] == len(rows) else q[rows]
     kq, ke = mx_quantize(k)
     # V is quantized along the keys of each segment slot: blocks of 32 keys from the slot start
     vt = np.asarray(v, dtype=np.float32)
@@ -495,9 +505,8 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None):
         segT = seg.transpose(1, 2, 0)                     # [h, D, keys]
         vq, ve = mx_quantize(segT)
         vdq[lo:lo + n] = mx_dequantize(vq, ve).transpose(2, 0, 1)[:n]
-    qd = mx_dequantize(qq, qe)
+    qd = mx_dequantize(*mx_quantize(qsel, fold=c))
     kd = mx_dequantize(kq, ke)
-    rows = np.arange(N) if q_rows is None else np.asarray(q_rows)
     out = np.zeros((len(rows), h, D))
     for s in range(len(cu) - 1):
         lo, n = int(cu[s]), int(vl[s])
@@ -505,7 +514,7 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None):
         if sel.size == 0:
             continue
         for hh in range(h):
-            sc = qd[rows[sel], hh] @ kd[lo:lo + n, hh].T          # log2 units
+            sc = qd[sel, hh] @ kd[lo:lo + n, hh].T                  # log2 units
             sc -= sc.max(axis=1, keepdims=True)
             p = np.exp2(sc)
             out[sel, hh] = (p @ vdq[lo:lo + n, hh]) / p.sum(axis=1, keepdims=True)

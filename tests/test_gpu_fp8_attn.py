@@ -1,0 +1,154 @@
+"""FP8 (MX-scaled e4m3) varlen attention against the oracle (GPU).
+
+The quantized operands are compared byte for byte with the oracle's quantizer
+(read back from the documented workspace layout); the output is compared with
+the oracle's attention over the same quantized operands and with the exact
+attention, within tolerances that follow from e4m3's 3-bit mantissa."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from _util import dev, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+# e4m3 byte -> value (OCP: bias 7, 0x7F/0xFF NaN)
+_E4M3 = np.array([(-1.0 if c & 0x80 else 1.0) *
+                  (((c & 7) * 2.0 ** -9) if ((c >> 3) & 15) == 0 else (1 + (c & 7) / 8) * 2.0 ** (((c >> 3) & 15) - 7))
+                  for c in range(256)])
+_E4M3[0x7F] = _E4M3[0xFF] = np.nan
+
+# tolerances (outputs are O(1) means of unit-variance values):
+#   vs the oracle on the same quantized operands, the kernel differs only by
+#   rounding 256 p to e4m3 (relative 2^-4 per weight, averaged over the keys)
+#   and fp32 accumulation;
+#   vs exact attention, the e4m3 rounding of q, k and v adds relative 2^-4 per
+#   element to scores and values.
+TOL_Q = dict(max_abs=6e-2, mean_abs=4e-3)
+TOL_X = dict(max_abs=1.5e-1, mean_abs=1.5e-2)
+
+
+def _run(lib, c, max_len=None):
+    H, D = c.n_heads, c.head_dim
+    q, k, v = (dev(a.reshape(c.n_buf, H * D), "bf16") for a in (c.q, c.k, c.v))
+    o = torch.full((c.n_buf, H * D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(lib.varlen_attn_fp8_workspace_size(c.n_buf, H, D, len(c.valid_len)), 16),
+                     dtype=torch.uint8, device="cuda")
+    ml = int(c.valid_len.max()) if max_len is None else max_len
+    lib.h3_varlen_attn_fp8(q, k, v, o, H, D, dev_i32(c.cu_slots), dev_i32(c.valid_len), ml, ws=ws)
+    torch.cuda.synchronize()
+    return host(o).reshape(c.n_buf, H, D), ws.cpu().numpy()
+
+
+def _valid_mask(c):
+    m = np.zeros(c.n_buf, bool)
+    for s in range(len(c.valid_len)):
+        m[c.cu_slots[s]:c.cu_slots[s] + c.valid_len[s]] = True
+    return m
+
+
+def _close(got, ref, what, max_abs, mean_abs):
+    d = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), what
+    assert d.max() <= max_abs and d.mean() <= mean_abs, f"{what}: max {d.max():.3g} mean {d.mean():.3g}"
+
+
+@pytest.mark.parametrize("lengths,n_buf,H,D", [((480,), 480, 4, 64), ((300, 77, 1, 64), 512, 3, 64),
+                                              ((1000, 129, 17), 1300, 2, 128), ((70,), 96, 1, 128)])
+def test_fp8_attention_small(lib, lengths, n_buf, H, D):
+    c = W.varlen_case(seed=31, lengths=lengths, n_buf=n_buf, n_heads=H, head_dim=D, dtype="bf16",
+                      pad_fill="nan")
+    got, _ = _run(lib, c)
+    m = _valid_mask(c)
+    assert np.all(got[~m] == 0)
+    ref_q = O.varlen_attention_fp8_operands(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    _close(got[m], ref_q[m], f"fp8 vs quantized-operand oracle {lengths}", **TOL_Q)
+    ref_x = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    _close(got[m], ref_x[m], f"fp8 vs exact {lengths}", **TOL_X)
+
+
+def test_fp8_quantized_operands_bit_exact(lib):
+    """Q (scale * log2 e folded), K and V^T in the workspace equal the oracle's MX-e4m3
+    quantization byte for byte, scales included."""
+    H, D = 2, 128
+    c = W.varlen_case(seed=32, lengths=(200, 45), n_buf=300, n_heads=H, head_dim=D, dtype="bf16")
+    _, ws = _run(lib, c)
+    n_buf, NB = c.n_buf, D // 32
+    r256 = lambda x: -(-x // 256) * 256
+    cols = -(-n_buf // 64) * 64 + 128 * (len(c.valid_len) + 1)
+    qk, qks, vt = r256(H * n_buf * D), r256(H * n_buf * NB), r256(H * D * cols)
+    q8 = ws[:H * n_buf * D].reshape(H, n_buf, D)
+    k8 = ws[qk:qk + H * n_buf * D].reshape(H, n_buf, D)
+    qs = ws[2 * qk:2 * qk + H * n_buf * NB].reshape(H, n_buf, NB).astype(np.int64) - 127
+    ks = ws[2 * qk + qks:2 * qk + qks + H * n_buf * NB].reshape(H, n_buf, NB).astype(np.int64) - 127
+    vt8 = ws[2 * qk + 2 * qks:2 * qk + 2 * qks + H * D * cols].reshape(H, D, cols)
+    vts = ws[2 * qk + 2 * qks + vt:2 * qk + 2 * qks + vt + H * (cols // 32) * D].reshape(H, cols // 32, D)
+    # stored scale order: even blocks, then odd blocks
+    order = np.argsort(np.concatenate([np.arange(0, NB, 2), np.arange(1, NB, 2)]))
+    fold = float(O.fp8_fold(D))
+    for s in range(len(c.valid_len)):
+        lo, n = int(c.cu_slots[s]), int(c.valid_len[s])
+        for h in range(H):
+            for name, x, b8, sc, f in (("q", c.q, q8, qs, fold), ("k", c.k, k8, ks, 1.0)):
+                want_q, want_e = O.mx_quantize(x[lo:lo + n, h], fold=f)
+                np.testing.assert_array_equal(_E4M3[b8[h, lo:lo + n]], want_q, err_msg=f"{name} s{s} h{h}")
+                np.testing.assert_array_equal(sc[h, lo:lo + n][:, order], want_e, err_msg=f"{name} scales")
+            base = -(-lo // 64) * 64 + 128 * s
+            npad = -(-n // 64) * 64
+            seg = np.zeros((npad, D), np.float32)
+            seg[:n] = c.v[lo:lo + n, h]
+            want_q, want_e = O.mx_quantize(seg.T)
+            np.testing.assert_array_equal(_E4M3[vt8[h, :, base:base + npad]], want_q, err_msg=f"v s{s} h{h}")
+            got_e = vts[h, base // 32:(base + npad) // 32].astype(np.int64).T - 127
+            np.testing.assert_array_equal(got_e, want_e, err_msg="v scales")
+
+
+def test_fp8_attention_8k_three_segments(lib):
+    """The 4032/1500/17 packing in 8192 rows, 8 heads x 128: NaN pads change nothing,
+    reruns are byte-identical, each segment alone equals the packed run."""
+    c = W.varlen_case(seed=0, dtype="bf16")
+    got, _ = _run(lib, c)
+    m = _valid_mask(c)
+    assert np.all(got[~m] == 0)
+    ref_q = O.varlen_attention_fp8_operands(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    _close(got[m], ref_q[m], "fp8 8k vs quantized-operand oracle", **TOL_Q)
+    got_p, _ = _run(lib, W.varlen_case(seed=0, dtype="bf16", pad_fill="nan"))
+    assert np.array_equal(got_p, got)
+    again, _ = _run(lib, c)
+    assert np.array_equal(again, got)
+    for s in range(3):
+        lo, n = int(c.cu_slots[s]), int(c.valid_len[s])
+        one = W.VarlenCase(n, 8, 128, np.array([0, n], np.int32), np.array([n], np.int32),
+                           c.q[lo:lo + n], c.k[lo:lo + n], c.v[lo:lo + n])
+        alone, _ = _run(lib, one)
+        assert np.array_equal(alone, got[lo:lo + n])
+
+
+def test_fp8_attention_10s_share_sampled(lib):
+    """5 heads x 128 over the 246,208-row buffer of the 10 s request, sampled rows."""
+    wl = W.SHARE_10S
+    bi = W.block_inputs(wl, 0, "bf16")
+    hc, D = wl.head_count, wl.head_dim
+    qa = dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), "bf16")
+    o = torch.full((wl.n_pad_total, hc * D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lib.h3_varlen_attn_fp8(qa[:, :hc * D], qa[:, hc * D:2 * hc * D], qa[:, 2 * hc * D:], o, hc, D,
+                           dev_i32(bi.cu_slots), dev_i32(bi.valid_len), int(bi.valid_len.max()))
+    torch.cuda.synchronize()
+    n = wl.n_valid
+    rows = np.unique(np.concatenate([np.random.default_rng(0).choice(n, 24, replace=False), [0, n - 1]]))
+    got = host(o[torch.from_numpy(rows).cuda()]).reshape(len(rows), hc, D)
+    q, k, v = bi.qkv_attn[:, 0], bi.qkv_attn[:, 1], bi.qkv_attn[:, 2]
+    # Near-uniform attention over random values: the output is a mean of ~2.5e5
+    # terms, and a uniform relative rounding of 2^-4 / sqrt(3) = 3.6% on each
+    # weight (P) or value (V) adds the same relative error to it.  Against the
+    # quantized-operand oracle only the P rounding remains (bound 6%); against
+    # exact attention P and V add up (sqrt(2) x 3.6%, plus the scores: bound 8%).
+    ref_q = O.varlen_attention_fp8_operands(q[rows], k, v, bi.cu_slots, bi.valid_len, q_rows=rows)
+    rel_q = np.linalg.norm(got - ref_q) / np.linalg.norm(ref_q)
+    assert rel_q < 6e-2, rel_q
+    ref = O.varlen_attention(q[rows], k, v, bi.cu_slots, bi.valid_len, q_rows=rows)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel < 8e-2, rel
+    assert np.all(host(o[wl.n_valid:]) == 0)
