@@ -897,7 +897,9 @@ __global__ __launch_bounds__(256) void transpose_quant_v_kernel(const bf16_t* __
 //    Q).  The running max is raised whenever a tile exceeds it by more than
 //    0.75, so p <= 2^0.75 and 256 p <= 431 stays in e4m3 range.  The kernel
 //    computes 256 p = exp2(s - (m - 8)) directly and stores it as e4m3 with
-//    scale byte 127; O and the row sums (fp32 256 p) share the factor 256.
+//    scale byte 127.  The row sums come from the matrix pipe: one more P.V
+//    MFMA whose A operand is all e4m3 ones sums the stored weights of every
+//    query, so numerator and denominator see the same rounded 256 p.
 //  * LDS rows are padded (K: D + 16 bytes, V^T: 64 + 16) so each 16-lane
 //    group of a 16-byte fragment read covers 16 distinct bank groups.
 namespace {
@@ -1053,9 +1055,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;
-  float m_ref = -INFINITY;  // m_run - 8: exp2(s - m_ref) = 256 p
-  float l_a = 0.f, l_b = 0.f;
+  // Scores are kept relative to m_ref = m_run - 8: each score chain starts from
+  // negm (= -m_ref in all 16 registers), so exp2 of a score is 256 p.
+  float m_ref = 0.f;
+  f32x16_t negm;
+  f32x16_t lacc;             // row sums of the stored weights (register 0 is used)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  i32x8_t ones8;             // e4m3 1.0 in every byte
+#pragma unroll
+  for (int r = 0; r < 8; ++r) ones8[r] = 0x38383838;
   constexpr uint32_t PSC = 127u;  // P is stored as 256 p; the row sums carry the same 256
 
   auto mask_tile = [&](f32x16_t (&sc)[2], int jt) {
@@ -1066,19 +1075,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       for (int r = 0; r < 16; ++r)
         if (base + kb * 32 + 16 * hf + r >= len) sc[kb][r] = -INFINITY;
   };
-  auto update_max = [&](float mx) {
+  auto update_max = [&](float mx, f32x16_t (&sc)[2]) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-    const bool raise = mx > m_run + 0.75f;
+    const bool raise = mx > 8.75f;  // tile max above the running max + 0.75
     if (__any(raise)) {
       scaled_mfma_drain();
-      const float m_new = raise ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      m_ref = m_new - 8.0f;
-      l_a *= alpha;
-      l_b *= alpha;
+      const float delta = raise ? mx - 8.0f : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      m_ref += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[0][r] -= delta;
+        sc[1][r] -= delta;
+        negm[r] = -m_ref;
+      }
+      lacc[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1111,8 +1124,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     ksc[0] = kscale(sk, 0);
     ksc[1] = kscale(sk, 1);
     i32x8_t kf = kfrag(sk, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nxt[0][r] = nxt[1][r] = 0.f;
+    nxt[0] = negm;
+    nxt[1] = negm;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int kb = i & 1, t = i >> 1;
@@ -1127,8 +1140,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
         float pv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          pv[u] = __builtin_amdgcn_exp2f(cur[pkb][r0 + u] - m_ref);  // 256 p
-          (u & 1 ? l_b : l_a) += pv[u];
+          pv[u] = __builtin_amdgcn_exp2f(cur[pkb][r0 + u]);  // 256 p
         }
         // the first conversion's upper half is overwritten by the second
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pw[word], false);
@@ -1153,6 +1165,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       vf[db] = vfrag(sv, db);
       vsc[db] = vscale(sv, db);
     }
+    lacc = mfma_e4m3<0>(ones8, pw, lacc, 127u, PSC);
 #pragma unroll
     for (int db = 0; db < NBM; ++db) {
       oacc[db] = mfma_e4m3<0>(vf[db], pw, oacc[db], vsc[db], PSC);
@@ -1165,7 +1178,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     }
     // after the last tile's P.V the epilogue reads O: let these MFMAs finish
     if (last || jt + 1 >= n_tiles) scaled_mfma_drain();
-    if (jt + 1 < n_tiles) update_max(mx);
+    if (jt + 1 < n_tiles) update_max(mx, nxt);
   };
 
   load_tile(0);
@@ -1179,12 +1192,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   compute_s(0, sa);
   if (n_tiles == 1) mask_tile(sa, 0);
   {
+    // first reference: the exact max of S(0) minus 8 (finite: a tile has a valid key)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
-    update_max(mx);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    m_ref = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) - 8.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sa[0][r] -= m_ref;
+      sa[1][r] -= m_ref;
+      negm[r] = -m_ref;
+    }
   }
   if (n_tiles > 2) load_tile(2);
 
@@ -1205,8 +1227,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   // the lagging half's last P.V (its score argument is unused: no max follows)
   if (lag) phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1, true);
 
-  const float l_run = l_a + l_b;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = lacc[0];  // every accumulator row holds the query's sum
   if (!q_ok) return;
   const float inv = 1.0f / l_tot;
   bf16_t* op = o + (int64_t)(seg_lo + qrow) * ld_o + head * D;
