@@ -46,7 +46,8 @@ class H3Error(RuntimeError):
 class BlockConfig(ctypes.Structure):
     _fields_ = [("dim", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn_dim", _i32),
                 ("sec_t", _i32), ("sec_h", _i32), ("sec_w", _i32), ("theta", _f),
-                ("eps_qk", _f), ("eps_mod", _f), ("norm_kind", _i32), ("dtype", _i32)]
+                ("eps_qk", _f), ("eps_mod", _f), ("norm_kind", _i32), ("dtype", _i32),
+                ("attn_fp8", _i32)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -251,10 +252,11 @@ def h3_swiglu(h, w1, w3, w2, out, gate=None, ld_gate: Optional[int] = None,
 
 
 def block_config(dim, n_heads, head_dim, ffn_dim, sections, theta=1e4, eps_qk=1e-6,
-                 eps_mod=1e-6, norm_kind=0, dtype=torch.bfloat16) -> BlockConfig:
+                 eps_mod=1e-6, norm_kind=0, dtype=torch.bfloat16,
+                 attn_fp8=False) -> BlockConfig:
     return BlockConfig(dim, n_heads, head_dim, ffn_dim, sections[0], sections[1], sections[2],
                        theta, eps_qk, eps_mod, norm_kind,
-                       H3_BF16 if dtype == torch.bfloat16 else H3_F32)
+                       H3_BF16 if dtype == torch.bfloat16 else H3_F32, int(bool(attn_fp8)))
 
 
 def block_workspace_size(cfg: BlockConfig, n_tok_local: int, n_buf: int, n_seg: int) -> int:

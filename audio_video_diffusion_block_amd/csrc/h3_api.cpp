@@ -359,8 +359,11 @@ BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int3
   };
   w.h1 = take(n * c->dim * es);
   w.qkv = take(n * 3 * hd * es);
-  w.attn = take((int64_t)attn_workspace_bytes(c->dtype == H3_BF16, share ? n_buf : n,
-                                              share ? head_count : c->n_heads, c->head_dim, n_seg));
+  const int64_t an = share ? n_buf : n;
+  const int ah = share ? head_count : c->n_heads;
+  w.attn = take(c->attn_fp8 ? (int64_t)attn_fp8_workspace_bytes(an, ah, c->head_dim, n_seg)
+                            : (int64_t)attn_workspace_bytes(c->dtype == H3_BF16, an, ah,
+                                                            c->head_dim, n_seg));
   w.o = take(share ? 0 : n * hd * es);
   w.g = take(n * (int64_t)c->ffn_dim * es);
   w.total = off;
@@ -390,6 +393,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   TRY(check_sections(D, cfg->sec_t, cfg->sec_h, cfg->sec_w));
   CHECK(cfg->norm_kind == 0 || cfg->norm_kind == 1, "norm_kind must be 0 or 1");
   CHECK(cfg->theta > 0.f && cfg->eps_qk >= 0.f && cfg->eps_mod >= 0.f, "theta/eps out of range");
+  CHECK(cfg->attn_fp8 == 0 || cfg->attn_fp8 == 1, "attn_fp8 must be 0 or 1");
+  CHECK(!cfg->attn_fp8 || dt == H3_BF16, "the FP8 attention path needs bf16 storage");
   const int64_t n = io->n_tok_local;
   CHECK(n >= 0 && n <= (int64_t)INT32_MAX, "n_tok_local out of range");
   const bool share = io->qkv_attn != nullptr;
@@ -453,6 +458,16 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                                           cfg->eps_mod, s),
                  "modulate-1"));
   const float scale = 1.0f / std::sqrt((float)D);
+  auto attention = [&](const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                       int64_t ldv, void* o, int64_t ldo, int64_t rows, int heads) {
+    return cfg->attn_fp8
+               ? launch_varlen_attn_fp8(D, q, ldq, k, ldk, v, ldv, o, ldo, rows, heads,
+                                        io->cu_slots, io->valid_len, io->n_seg,
+                                        io->max_valid_len, scale, attn_ws, s)
+               : launch_varlen_attn(bf, D, q, ldq, k, ldk, v, ldv, o, ldo, rows, heads,
+                                    io->cu_slots, io->valid_len, io->n_seg, io->max_valid_len,
+                                    scale, attn_ws, s);
+  };
   if (peer) {
     // Peer-major exchange layout: every all-to-all block is contiguous.
     const int P = H / hc, r = hb / hc;
@@ -481,10 +496,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                                   hipMemcpyDeviceToDevice, s),
                    "exchange-in self block"));
     // A5 attention over the whole buffer for the head slice
-    TRY(hip_status(launch_varlen_attn(bf, D, qa, 3 * sd, qa + sd * es, 3 * sd, qa + 2 * sd * es,
-                                      3 * sd, io->o_attn, sd, io->n_buf, hc, io->cu_slots,
-                                      io->valid_len, io->n_seg, io->max_valid_len, scale,
-                                      attn_ws, s),
+    TRY(hip_status(attention(qa, 3 * sd, qa + sd * es, 3 * sd, qa + 2 * sd * es, 3 * sd,
+                             io->o_attn, sd, io->n_buf, hc),
                    "attention"));
     // A6 the reverse all-to-all's own block: o_attn rows [tok_begin, +n) -> o_recv block r
     const int64_t oblk = n * sd * es;
@@ -513,10 +526,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   if (!share) {
     // A5 attention straight from the QKV buffer
     void* o = wsb + L.o;
-    TRY(hip_status(launch_varlen_attn(bf, D, qkv, 3 * hd, qkv + hd * es, 3 * hd,
-                                      qkv + 2 * hd * es, 3 * hd, o, hd, n, H, io->cu_slots,
-                                      io->valid_len, io->n_seg, io->max_valid_len, scale,
-                                      attn_ws, s),
+    TRY(hip_status(attention(qkv, 3 * hd, qkv + hd * es, 3 * hd, qkv + 2 * hd * es, 3 * hd, o,
+                             hd, n, H),
                    "attention"));
     o_for_proj = o;
   } else {
@@ -528,10 +539,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                                     sd * es, s),
                    "exchange-in copy"));
     // A5 attention over the whole buffer for the head slice
-    TRY(hip_status(launch_varlen_attn(bf, D, qa, 3 * sd, qa + sd * es, 3 * sd, qa + 2 * sd * es,
-                                      3 * sd, io->o_attn, sd, io->n_buf, hc, io->cu_slots,
-                                      io->valid_len, io->n_seg, io->max_valid_len, scale,
-                                      attn_ws, s),
+    TRY(hip_status(attention(qa, 3 * sd, qa + sd * es, 3 * sd, qa + 2 * sd * es, 3 * sd,
+                             io->o_attn, sd, io->n_buf, hc),
                    "attention"));
     // A6 this rank's rows of the output into its head slice of o_local
     TRY(hip_status(launch_copy_rows((char*)io->o_attn + io->tok_begin * sd * es, sd * es, 0,

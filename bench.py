@@ -14,7 +14,7 @@ is the float64 oracle, timed on this host on a bounded row sample and
 extrapolated by row count.
 
   python bench.py [--steps K] [--warmup W] [--config share10s|share5s|tiny]
-                  [--no-cpu-baseline] [--only attn|copy|block]
+                  [--no-cpu-baseline] [--only attn|attn_fp8|copy|block]
 """
 from __future__ import annotations
 
@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 METRIC = "varlen attn TFLOP/s + fused-op HBM GB/s; DiT-block ms, 10 s shape, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "audio_video_diffusion_block_amd", "csrc", "k_attn.hip")
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--config", default="share10s")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", choices=["", "attn", "copy", "block"])
+    ap.add_argument("--only", default="", choices=["", "attn", "attn_fp8", "copy", "block"])
     ap.add_argument("--op-reps", type=int, default=3)
     return ap.parse_args()
 
@@ -339,12 +340,17 @@ def main():
     def attn():
         h3.h3_varlen_attn(q_v, k_v, v_v, o_v, hc, D, cu, vl, max_len, ws=attn_ws)
 
-    if args.only == "attn":
+    if args.only in ("attn", "attn_fp8"):
+        fn = attn
+        if args.only == "attn_fp8":
+            ws8 = torch.empty(max(h3.varlen_attn_fp8_workspace_size(n_buf, hc, D, 1), 16),
+                              dtype=torch.uint8, device="cuda")
+            fn = lambda: h3.h3_varlen_attn_fp8(q_v, k_v, v_v, o_v, hc, D, cu, vl, max_len, ws=ws8)
         for _ in range(args.warmup):
-            attn()
+            fn()
         torch.cuda.synchronize()
-        ms = timer.time(attn, max(args.steps, 1))
-        print(json.dumps({"attn_ms": ms, "attn_tflops": work["attn_flop"] / ms / 1e9}))
+        ms = timer.time(fn, max(args.steps, 1))
+        print(json.dumps({"kernel": args.only, "attn_ms": ms, "attn_tflops": work["attn_flop"] / ms / 1e9}))
         return
 
     # ---- timed block steps
@@ -371,6 +377,13 @@ def main():
         qkv[:, :H * D], qkv[:, H * D:2 * H * D], H, D, wd["g_q"], wd["g_k"], pos, wl.sections,
         wl.theta, wl.eps_qk), reps)
     ops["attention"] = timer.time(attn, reps)
+    # the MX-scaled e4m3 attention on the same operands, with its own workspace
+    ws8 = torch.empty(max(h3.varlen_attn_fp8_workspace_size(n_buf, hc, D, 1), 16),
+                      dtype=torch.uint8, device="cuda")
+    o8 = torch.empty_like(o_v)
+    ops["attention_fp8"] = timer.time(lambda: h3.h3_varlen_attn_fp8(
+        q_v, k_v, v_v, o8, hc, D, cu, vl, max_len, ws=ws8), reps)
+    del ws8, o8
     o_in = share["o_local"] if wl.share_mode else o_v
     ops["out_gemm_residual"] = timer.time(lambda: h3.h3_linear(o_in, wd["w_o"], xs, gate=mod[:, 2]), reps)
     sw_ws = torch.empty(h3.swiglu_workspace_size(wl.n_loc, wl.ffn_dim, bf), dtype=torch.uint8, device="cuda")
@@ -388,6 +401,15 @@ def main():
         ops["block_peer_major"] = timer.time(lambda: h3.h3_dit_block_forward(
             cfg, wd, xp, mod, pos, cu, vl, max_len, ws=ws, **peer), reps)
         del peer, xp
+    # the whole block with the FP8 attention step (same launch sequence otherwise)
+    cfg8 = h3.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
+                           wl.eps_qk, wl.eps_mod, 0, bf, attn_fp8=True)
+    ws_b8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, n_buf, 1), dtype=torch.uint8,
+                        device="cuda")
+    x8 = x0.clone()
+    ops["block_fp8_attention"] = timer.time(lambda: h3.h3_dit_block_forward(
+        cfg8, wd, x8, mod, pos, cu, vl, max_len, ws=ws_b8, **share), reps)
+    del ws_b8, x8
     # post-DiT tail: the 10 s request's decoded frames (1344x768, 243 frames) to uint8 BTHWC
     fr = W.FRAMES_10S
     frames = torch.rand((fr["B"], 3, fr["T"], fr["H"], fr["W"]), device="cuda") * 2.1 - 1.05
@@ -398,8 +420,17 @@ def main():
     torch.cuda.synchronize()
     attn_ms = ops["attention"]
     attn_tflops = work["attn_flop"] / attn_ms / 1e9
+    total_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
     breakdown = {
         "attention": {"ms": attn_ms, "TFLOP/s": attn_tflops, "frac_peak": attn_tflops / BF16_PEAK_TFLOPS},
+        "attention_fp8": {"ms": ops["attention_fp8"],
+                          "TFLOP/s": work["attn_flop"] / ops["attention_fp8"] / 1e9,
+                          "frac_peak": work["attn_flop"] / ops["attention_fp8"] / 1e9 / FP8_PEAK_TFLOPS,
+                          "peak": "fp8 dense MFMA", "speedup_vs_bf16": attn_ms / ops["attention_fp8"],
+                          "operands": "MX e4m3 Q/K/V (E8M0 scale per 32), P as e4m3"},
+        "block_fp8_attention": {"ms": ops["block_fp8_attention"],
+                                "TFLOP/s": total_flop / ops["block_fp8_attention"] / 1e9,
+                                "note": "the same block with attention on the FP8 path"},
         "qkv_gemm": {"ms": ops["qkv_gemm"], "TFLOP/s": work["qkv_flop"] / ops["qkv_gemm"] / 1e9},
         "out_gemm_residual": {"ms": ops["out_gemm_residual"],
                               "TFLOP/s": work["out_flop"] / ops["out_gemm_residual"] / 1e9},
@@ -417,7 +448,6 @@ def main():
                       "frac_hbm": frames_bytes / ops["frames_u8"] / 1e6 / HBM_PEAK_GBS,
                       "workload": "10 s decoded video, 243 x 3 x 768 x 1344 fp32 -> uint8 BTHWC"},
     }
-    total_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
     value = total_flop / step_ms / 1e9  # TFLOP/s of the whole block
 
     traffic = traffic_record()

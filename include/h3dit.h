@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 2
+#define H3_ABI_VERSION 3
 
 typedef enum {
   H3_OK = 0,
@@ -214,6 +214,7 @@ typedef struct {
   float eps_mod;      /* modulated-norm epsilon */
   int32_t norm_kind;  /* 0 LayerNorm, 1 RMSNorm (modulated norms) */
   h3_dtype dtype;
+  int32_t attn_fp8;   /* 1: attention through h3_varlen_attn_fp8 (bf16 only); 0: exact path */
 } h3_block_config;
 
 typedef struct {
@@ -276,6 +277,9 @@ typedef struct {
  *   x <- x + gate1 * (o w_o^T);  h2 = norm(x)(1+scale2)+shift2;
  *   x <- x + gate2 * (silu(h2 w1^T) * (h2 w3^T)) w2^T.
  * World 1: qkv_attn == NULL, tok_begin == 0, n_buf == n_tok_local, head_count == H.
+ * cfg->attn_fp8 == 1 runs the attention step as h3_varlen_attn_fp8 does (MX-scaled
+ * e4m3 operands); it needs dtype H3_BF16 (else H3_ERR_ARG), and the workspace size
+ * depends on it, so query it with the same cfg.
  */
 size_t h3_dit_block_workspace_size(const h3_block_config* cfg, int64_t n_tok_local,
                                    int64_t n_buf, int32_t n_seg);

@@ -250,7 +250,7 @@ def _mod_rows(mod, rows):
 
 def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
               qkv_attn_fill=None, o_local_fill=None, rows: Optional[np.ndarray] = None,
-              intermediates: bool = False):
+              intermediates: bool = False, attention=None):
     """One DiT block forward on this GPU's token rows x [n, C].
 
     Steps: h1 = modnorm(x; shift1, scale1) -> qkv = h1 Wqkv^T -> Q/K RMSNorm +
@@ -269,6 +269,8 @@ def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
     [FH3-zh] FastH3 推理配置: sequence-parallel degree 8.)
 
     rows: return only these local rows (keys/values still use every row).
+    attention: the attention step, called as varlen_attention is (default);
+    varlen_attention_fp8_operands gives the block with MX-e4m3 attention.
     Returns x2 [len(rows), C], or a dict of every intermediate if asked.
     """
     sh = shape
@@ -307,7 +309,8 @@ def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
     else:
         kbuf, vbuf = k_loc, v_loc
         qrows = out_rows
-    o_h = varlen_attention(q_loc, kbuf, vbuf, cu_slots, valid_len, q_rows=qrows)
+    attend = varlen_attention if attention is None else attention
+    o_h = attend(q_loc, kbuf, vbuf, cu_slots, valid_len, q_rows=qrows)
     if share:
         o = _f64(o_local_fill)[out_rows].copy()
         o[:, hb:hb + hc] = o_h

@@ -119,6 +119,15 @@ def test_block_argument_checks():
     io2 = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 512, 0, 0, 4, None, None, None)
     st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io2), FAKE, need, None)
     assert st == h3.H3_ERR_ARG and "world-1" in h3.last_error()
+    f8 = h3.block_config(256, 4, 64, 704, (16, 24, 24), attn_fp8=True)
+    assert h3.block_workspace_size(f8, 480, 480, 1) != need
+    import torch
+    f8_f32 = h3.block_config(256, 4, 64, 704, (16, 24, 24), dtype=torch.float32, attn_fp8=True)
+    st = h3._c_block(ctypes.byref(f8_f32), ctypes.byref(w), ctypes.byref(io), FAKE, 1 << 30, None)
+    assert st == h3.H3_ERR_ARG and "bf16" in h3.last_error()
+    f8.attn_fp8 = 2
+    st = h3._c_block(ctypes.byref(f8), ctypes.byref(w), ctypes.byref(io), FAKE, 1 << 30, None)
+    assert st == h3.H3_ERR_ARG and "attn_fp8" in h3.last_error()
     io3 = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 120, 480, 400, 3, 1, FAKE, FAKE, FAKE)
     st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io3), FAKE, need, None)
     assert st == h3.H3_ERR_ARG and "local rows" in h3.last_error()

@@ -14,26 +14,29 @@ def weights_dev(w, dtype):
     return {k: dev(getattr(w, k), dtype) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")}
 
 
-def cfg_of(lib, wl, dtype):
+def cfg_of(lib, wl, dtype, attn_fp8=False):
     return lib.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
-                            wl.eps_qk, wl.eps_mod, 0, TORCH_DT[dtype])
+                            wl.eps_qk, wl.eps_mod, 0, TORCH_DT[dtype], attn_fp8=attn_fp8)
 
 
-def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=False):
+def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=False,
+              attn_fp8=False):
     x = dev(bi.x if x_override is None else x_override, dtype)
     mod = dev(bi.mod if mod_override is None else mod_override, dtype)
     extra = share_buffers(wl, bi, dtype, peer) if wl.share_mode else {}
-    lib.h3_dit_block_forward(cfg_of(lib, wl, dtype), weights_dev(w, dtype), x, mod, dev_i32(bi.pos),
+    lib.h3_dit_block_forward(cfg_of(lib, wl, dtype, attn_fp8), weights_dev(w, dtype), x, mod,
+                             dev_i32(bi.pos),
                              dev_i32(bi.cu_slots), dev_i32(bi.valid_len), int(bi.valid_len.max()),
                              **extra)
     torch.cuda.synchronize()
     return host(x)
 
 
-def oracle_block(wl, w, bi, rows=None, x=None, mod=None):
+def oracle_block(wl, w, bi, rows=None, x=None, mod=None, attention=None):
     return O.dit_block(bi.x if x is None else x, bi.mod if mod is None else mod, w, bi.pos,
                        bi.cu_slots, bi.valid_len, O.BlockShape.of(wl), bi.qkv_attn,
-                       None if bi.o_local is None else bi.o_local, rows=rows)
+                       None if bi.o_local is None else bi.o_local, rows=rows,
+                       attention=attention)
 
 
 def check_block(got, ref, x_in, dtype, what, update=None):
@@ -131,3 +134,42 @@ def test_block_deterministic(lib):
     a = run_block(lib, wl, w, bi, "bf16")
     b = run_block(lib, wl, w, bi, "bf16")
     assert np.array_equal(a, b)
+
+
+def _update_dominant(bi):
+    x = W.round_to_bf16(bi.x / 128)
+    mod = bi.mod.copy()
+    mod[:, O.GATE1] *= 8
+    mod[:, O.GATE2] *= 8
+    return x, W.round_to_bf16(mod)
+
+
+@pytest.mark.parametrize("case", ["world1", "share_r2", "peer_r3"])
+def test_block_fp8_attention(lib, case):
+    """Block with the MX-e4m3 attention path, update-dominant inputs so that the
+    attention branch shows in x2.
+
+    Against the oracle block whose attention quantizes its own float64 q, k, v:
+    elementwise at the bf16 block bar, relative L2 within 5%.  The e4m3 rounding
+    of an operand element is decided by its low bits, so the kernel's bf16 q, k,
+    v (relative 2^-9 from the oracle's) round to the other e4m3 neighbour (a 2^-3
+    relative step) for a few percent of the elements; on these inputs, rounding
+    the oracle's own q, k, v to bf16 before quantizing moves x2 by 2.0% (world 1)
+    and 0.8% (rank share) relative L2, which the 5% bound covers together with
+    the bf16 block error.  Against the exact oracle block: relative L2 within 8%
+    (the quantized-operand oracle itself is 4.0% / 3.1% from it)."""
+    rank = {"world1": None, "share_r2": 2, "peer_r3": 3}[case]
+    wl = W.TINY if rank is None else W.TINY.replace(sp_degree=4, rank=rank)
+    w = W.block_weights(wl, 4, "bf16")
+    bi = W.block_inputs(wl, 4, "bf16")
+    x, mod = _update_dominant(bi)
+    got = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod,
+                    peer=case.startswith("peer"), attn_fp8=True)
+    ref_q = oracle_block(wl, w, bi, x=x, mod=mod, attention=O.varlen_attention_fp8_operands)
+    assert_close(got, ref_q, "bf16", f"block fp8 {case}", rel_l2=5e-2)
+    ref = oracle_block(wl, w, bi, x=x, mod=mod)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref - x)
+    assert rel < 8e-2, f"{case}: update rel L2 vs exact {rel:.3g}"
+    exact_path = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod,
+                           peer=case.startswith("peer"))
+    assert not np.array_equal(got, exact_path)  # the FP8 path really ran
