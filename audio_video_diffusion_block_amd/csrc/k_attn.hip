@@ -746,7 +746,7 @@ hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld
 
 // ================================================================== FP8 path
 //
-// MiniMax H3 通过 vLLM-Omni 实现 FastH3 实时推理, "FastH3 推理配置" (sparse and
+// MiniMax H3 通过 vLLM-Omni 实现 FastH3 实时推理, "超出 FastH3 配置的扩展能力" (sparse and
 // quantized attention): an FP8 attention path (SAGE FP8) speeds up the base
 // pipeline at small quality cost.  The pages give no algorithm; this path
 // stores Q (softmax scale and log2 e folded in), K and V as OCP e4m3 with one

@@ -132,7 +132,7 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
 
 /*
  * h3_varlen_attn_fp8 -- the same attention with FP8 operands (MiniMax H3 通过
- * vLLM-Omni 实现 FastH3 实时推理, "FastH3 推理配置": an FP8 attention path
+ * vLLM-Omni 实现 FastH3 实时推理, "超出 FastH3 配置的扩展能力": an FP8 attention path
  * (SAGE FP8) speeds up the base pipeline at small quality cost).  Same
  * arguments and output contract as h3_varlen_attn (bf16 q, k, v, o), except:
  *   q (times softmax_scale * log2 e), k and v are rounded to OCP e4m3 with

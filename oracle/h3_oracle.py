@@ -413,7 +413,7 @@ def frames_to_u8(frames, layout: int = 0) -> np.ndarray:
 
 # ------------------------------------------- FP8 (MX-scaled e4m3) attention
 
-# [FH3-zh] FastH3 推理配置 (sparse and quantized attention): an FP8 attention
+# [FH3-zh] 超出 FastH3 配置的扩展能力 (sparse and quantized attention): an FP8 attention
 # path (SAGE FP8) gives up to 1.24x on the base pipeline with small quality
 # loss.  The pages give no algorithm.  Reading: Q (with the softmax scale and
 # log2 e folded in), K and V are stored as OCP e4m3 with one power-of-two

@@ -721,3 +721,17 @@ def test_fp8_operand_attention_close_to_exact():
     assert diff.max() < 0.1 and diff.mean() < 0.01
     # the quantization changes the result (this is not the exact path)
     assert diff.max() > 1e-4
+
+
+def test_mx_quantize_exact_on_representable_blocks():
+    """Blocks already of the form e4m3 value x 2^E, with the largest magnitude in
+    the top binade (224..448], come back unchanged, exponent and all."""
+    grid = np.array([_e4m3_decode(c) for c in range(0x7F)])
+    top = grid[grid > 224.0]
+    e = rng.integers(-20, 10, (6, 4))
+    codes = rng.choice(np.concatenate([grid, -grid]), (6, 4, 32))
+    codes[..., 5] = rng.choice(top, (6, 4)) * rng.choice([-1.0, 1.0], (6, 4))
+    x = (codes * np.ldexp(1.0, e)[..., None]).reshape(6, 128).astype(np.float32)
+    q, got_e = O.mx_quantize(x)
+    np.testing.assert_array_equal(got_e, e)
+    np.testing.assert_array_equal(O.mx_dequantize(q, got_e), x)
