@@ -522,3 +522,24 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None):
             p = np.exp2(sc)
             out[sel, hh] = (p @ vdq[lo:lo + n, hh]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+# ------------------------------------------------- FP8 (MX-scaled e4m3) GEMMs
+
+# [FH3-zh] 超出 FastH3 配置的扩展能力 (quantization path): online FP8 lowers the
+# peak HBM footprint by about 39% and the latency by about 5%.  The pages give
+# no format.  Reading: both operands of a projection, the weight [out, in] and
+# the activation [rows, in], are stored as OCP e4m3 with one power-of-two
+# (E8M0) scale per 32 consecutive elements along the contraction (in), the
+# same MX block rule as the FP8 attention operands; the weight is quantized
+# once, the activation on the fly from its bf16 value.  The product of the
+# dequantized operands is exact; only its final rounding to the output type
+# remains.
+
+def linear_fp8_operands(x, w) -> np.ndarray:
+    """x @ w^T over MX-e4m3-quantized operands: x [rows, K] and w [out, K]
+    (float32 values, K a multiple of 32), each quantized along K.  Returns the
+    exact float64 product of the dequantized operands."""
+    xd = mx_dequantize(*mx_quantize(x))
+    wd = mx_dequantize(*mx_quantize(w))
+    return xd @ wd.T

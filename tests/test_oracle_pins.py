@@ -735,3 +735,51 @@ def test_mx_quantize_exact_on_representable_blocks():
     q, got_e = O.mx_quantize(x)
     np.testing.assert_array_equal(got_e, e)
     np.testing.assert_array_equal(O.mx_dequantize(q, got_e), x)
+
+
+# ------------------------------------------------- FP8 (MX e4m3) GEMM operands
+
+def test_fp8_linear_exact_on_grid_and_power_of_two_equivariant():
+    """Operands already on the MX grid pass through unchanged, so the product is
+    the plain matmul; scaling an operand by 2^j scales the result by 2^j exactly
+    (the block exponent absorbs it)."""
+    grid = np.array([_e4m3_decode(c) for c in range(0x7F)])
+    top = grid[grid > 224.0]
+
+    def on_grid(rows, k):
+        e = rng.integers(-12, 4, (rows, k // 32))
+        c = rng.choice(np.concatenate([grid, -grid]), (rows, k // 32, 32))
+        c[..., 0] = rng.choice(top, (rows, k // 32))
+        return (c * np.ldexp(1.0, e)[..., None]).reshape(rows, k).astype(np.float32)
+
+    x, w = on_grid(7, 96), on_grid(5, 96)
+    np.testing.assert_array_equal(O.linear_fp8_operands(x, w), x.astype(np.float64) @ w.astype(np.float64).T)
+    # both operands are quantized: one off-grid operand alone moves the result
+    xo = rng.standard_normal((7, 96)).astype(np.float32)
+    wo = (rng.standard_normal((5, 96)) * 0.02).astype(np.float32)
+    assert not np.array_equal(O.linear_fp8_operands(xo, w), xo.astype(np.float64) @ w.astype(np.float64).T)
+    assert not np.array_equal(O.linear_fp8_operands(x, wo), x.astype(np.float64) @ wo.astype(np.float64).T)
+    xr = rng.standard_normal((6, 128)).astype(np.float32)
+    wr = (rng.standard_normal((9, 128)) * 0.02).astype(np.float32)
+    base = O.linear_fp8_operands(xr, wr)
+    for j in (-5, 3):
+        np.testing.assert_array_equal(O.linear_fp8_operands(np.ldexp(xr, j), wr), np.ldexp(base, j))
+        np.testing.assert_array_equal(O.linear_fp8_operands(xr, np.ldexp(wr, j)), np.ldexp(base, j))
+
+
+def test_fp8_linear_error_bound_and_zero_padding():
+    """Each operand element is off by at most 2^-4 relative (normal range), so
+    |y - y_exact| <= sum_k |x_k w_k| (2 * 2^-4 + 2^-8); appending zero columns
+    to both operands changes nothing."""
+    x = rng.standard_normal((11, 192)).astype(np.float32)
+    w = (rng.standard_normal((13, 192)) * 0.02).astype(np.float32)
+    got = O.linear_fp8_operands(x, w)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T * (2 * 2.0 ** -4 + 2.0 ** -8)
+    assert np.all(np.abs(got - exact) <= bound)
+    assert np.abs(got - exact).max() > 0  # the quantization is applied
+    xp = np.concatenate([x, np.zeros((11, 64), np.float32)], axis=1)
+    wp = np.concatenate([w, np.zeros((13, 64), np.float32)], axis=1)
+    np.testing.assert_array_equal(O.linear_fp8_operands(xp, wp), got)
+    # each row of x is quantized on its own: the result for a row does not depend on the others
+    np.testing.assert_array_equal(O.linear_fp8_operands(x[3:4], w), got[3:4])
