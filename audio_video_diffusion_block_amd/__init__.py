@@ -63,6 +63,10 @@ class BlockIO(ctypes.Structure):
                 ("o_local", _p), ("qkv_send", _p), ("o_recv", _p)]
 
 
+class MxOperand(ctypes.Structure):
+    _fields_ = [("data", _p), ("ld", _i64), ("scale", _p), ("ld_scale", _i64)]
+
+
 def _sig(name, res, args):
     f = getattr(_lib, name)
     f.restype = res
@@ -103,12 +107,22 @@ _c_attn8 = _sig("h3_varlen_attn_fp8", ctypes.c_int,
                 [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _f,
                  _p, _sz, _i32, _p])
 
+_c_mxq = _sig("h3_mx_quantize", ctypes.c_int,
+              [_p, _i64, _i64, _i32, _p, _i64, _p, _i64, _i32, _p])
+_c_lin8 = _sig("h3_linear_fp8", ctypes.c_int,
+               [ctypes.POINTER(MxOperand), ctypes.POINTER(MxOperand), _p, _i64, _i64, _i32, _i32,
+                _p, _i64, _p])
+_c_sw8_ws = _sig("h3_swiglu_fp8_workspace_size", _sz, [_i64, _i32])
+_c_sw8 = _sig("h3_swiglu_fp8", ctypes.c_int,
+              [ctypes.POINTER(MxOperand)] * 4 + [_p, _i64, _p, _i64, _i64, _i32, _i32, _p, _sz, _p])
+
 EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_rope",
             "h3_varlen_attn_workspace_size", "h3_varlen_attn", "h3_modulate_residual",
             "h3_linear", "h3_swiglu_workspace_size", "h3_swiglu", "h3_dit_block_workspace_size",
             "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
-            "h3_varlen_attn_fp8")
+            "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
+            "h3_swiglu_fp8")
 
 
 def _status_string(st: int) -> str:
@@ -249,6 +263,60 @@ def h3_swiglu(h, w1, w3, w2, out, gate=None, ld_gate: Optional[int] = None,
     _check(_c_swiglu(_ptr(h), _ld(h), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out), _ld(out),
                      _ptr(gate), ld_gate or 0, n, c, f, _ptr(ws), ws.numel() * ws.element_size(),
                      _dt(h), _stream(stream)))
+
+
+class MxTensor:
+    """An MX-e4m3 operand on the device: q uint8 [rows, >= round_up(k, 128)]
+    (e4m3 bytes, zeros past k) and s uint8 [rows, >= round_up(k, 128) / 32]
+    (E8M0 bytes), k logical columns."""
+
+    def __init__(self, q: torch.Tensor, s: torch.Tensor, k: int):
+        self.q, self.s, self.k = q, s, k
+
+    @staticmethod
+    def empty(rows: int, k: int, device="cuda") -> "MxTensor":
+        kp = -(-k // 128) * 128
+        return MxTensor(torch.empty((rows, kp), dtype=torch.uint8, device=device),
+                        torch.empty((rows, kp // 32), dtype=torch.uint8, device=device), k)
+
+    def c(self) -> MxOperand:
+        return MxOperand(_ptr(self.q), _ld(self.q), _ptr(self.s), _ld(self.s))
+
+
+def h3_mx_quantize(x, out: Optional[MxTensor] = None, stream=None) -> MxTensor:
+    """bf16 x [rows, cols] -> MxTensor (allocated when out is None)."""
+    rows, cols = x.shape
+    if out is None:
+        out = MxTensor.empty(rows, cols, x.device)
+    _check(_c_mxq(_ptr(x), _ld(x), rows, cols, _ptr(out.q), _ld(out.q), _ptr(out.s), _ld(out.s),
+                  _dt(x), _stream(stream)))
+    return out
+
+
+def h3_linear_fp8(a: MxTensor, w: MxTensor, out, gate=None, ld_gate: Optional[int] = None,
+                  stream=None):
+    """out = a @ w^T over MX operands, or out += gate * (a @ w^T)."""
+    if gate is not None and ld_gate is None:
+        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    ca, cw = a.c(), w.c()
+    _check(_c_lin8(ctypes.byref(ca), ctypes.byref(cw), _ptr(out), _ld(out), a.q.shape[0],
+                   w.q.shape[0], a.k, _ptr(gate), ld_gate or 0, _stream(stream)))
+
+
+def swiglu_fp8_workspace_size(n_tok: int, ffn_dim: int) -> int:
+    return _c_sw8_ws(n_tok, ffn_dim)
+
+
+def h3_swiglu_fp8(h: MxTensor, w1: MxTensor, w3: MxTensor, w2: MxTensor, out, gate=None,
+                  ld_gate: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    n, c, f = h.q.shape[0], h.k, w1.q.shape[0]
+    if gate is not None and ld_gate is None:
+        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    if ws is None:
+        ws = _bytes_ws(swiglu_fp8_workspace_size(n, f), h.q.device)
+    ops = [x.c() for x in (h, w1, w3, w2)]
+    _check(_c_sw8(*[ctypes.byref(o) for o in ops], _ptr(out), _ld(out), _ptr(gate), ld_gate or 0,
+                  n, c, f, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def block_config(dim, n_heads, head_dim, ffn_dim, sections, theta=1e4, eps_qk=1e-6,

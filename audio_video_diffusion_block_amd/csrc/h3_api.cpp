@@ -189,6 +189,40 @@ h3_status validate_linear(const void* a, int64_t lda, const void* w, int64_t ldw
   return H3_OK;
 }
 
+// MX operand of logical width k (columns) with `rows` rows
+h3_status check_mx(const char* name, const h3_mx_operand* x, int64_t k, int64_t rows) {
+  if (!x) return fail(H3_ERR_ARG, "%s is NULL", name);
+  const int64_t kp = h3::round_up(k, 128);
+  if (!x->data || !aligned16(x->data)) return fail(H3_ERR_ARG, "%s: data NULL or not 16-byte aligned", name);
+  if (x->ld < kp || x->ld % 16 != 0 || x->ld > (1 << 23))
+    return fail(H3_ERR_ARG, "%s: ld %lld must be a multiple of 16 in [%lld, 2^23]", name,
+                (long long)x->ld, (long long)kp);
+  if (!x->scale || ((uintptr_t)x->scale & 3u) != 0)
+    return fail(H3_ERR_ARG, "%s: scale NULL or not 4-byte aligned", name);
+  if (x->ld_scale < kp / 32 || x->ld_scale % 4 != 0)
+    return fail(H3_ERR_ARG, "%s: ld_scale %lld must be a multiple of 4, >= %lld", name,
+                (long long)x->ld_scale, (long long)(kp / 32));
+  (void)rows;
+  return H3_OK;
+}
+
+h3::MxOperand mx_of(const h3_mx_operand* x) {
+  h3::MxOperand m;
+  m.data = x->data;
+  m.ld = x->ld;
+  m.scale = x->scale;
+  m.ld_scale = x->ld_scale;
+  return m;
+}
+
+int64_t swiglu_fp8_parts(int64_t n_tok, int32_t ffn_dim, int64_t* g_q, int64_t* g_s) {
+  const int64_t fp = h3::round_up(ffn_dim, 128);
+  const int64_t g = h3::round_up(n_tok * ffn_dim * 2, 256);
+  *g_q = g;
+  *g_s = g + h3::round_up(n_tok * fp, 256);
+  return *g_s + h3::round_up(n_tok * (fp / 32), 256);
+}
+
 }  // namespace
 
 using namespace h3;
@@ -337,6 +371,92 @@ h3_status h3_swiglu(const void* h, int64_t ld_h, const void* w1, const void* w3,
   return hip_status(launch_gemm(bf, gate ? EPI_RESIDUAL : EPI_STORE, ws, ffn_dim, w2, nullptr,
                                 ffn_dim, out, ld_out, gate, ld_gate, n_tok, dim, ffn_dim, s),
                     "swiglu down-projection launch");
+}
+
+// ------------------------------------------------ FP8 (MX e4m3) projections
+
+h3_status h3_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int32_t cols, void* q,
+                         int64_t ld_q, void* scale, int64_t ld_scale, h3_dtype dtype,
+                         void* stream) {
+  g_err[0] = 0;
+  if (dtype != H3_BF16) return fail(H3_ERR_UNSUPPORTED, "MX quantization takes bf16 input");
+  CHECK(rows >= 0 && rows <= (int64_t)INT32_MAX * 4, "rows out of range");
+  CHECK(cols > 0 && cols % 32 == 0, "cols must be a positive multiple of 32");
+  if (rows == 0) return H3_OK;
+  TRY(check_rows("x", x, ld_x, cols, rows, H3_BF16));
+  CHECK(ld_x > 0, "x row stride must be positive");
+  h3_mx_operand o{q, ld_q, scale, ld_scale};
+  TRY(check_mx("q", &o, cols, rows));
+  TRY(check_device());
+  return hip_status(launch_mx_quantize(x, ld_x, rows, cols, q, ld_q, scale, ld_scale,
+                                       (hipStream_t)stream),
+                    "mx_quantize launch");
+}
+
+h3_status h3_linear_fp8(const h3_mx_operand* a, const h3_mx_operand* w, void* out,
+                        int64_t ld_out, int64_t m, int32_t n_out, int32_t k_in,
+                        const void* gate, int64_t ld_gate, void* stream) {
+  g_err[0] = 0;
+  CHECK(m >= 0 && m <= (int64_t)INT32_MAX, "m out of range");
+  CHECK(n_out > 0 && k_in > 0 && k_in % 32 == 0, "n_out > 0 and k_in a positive multiple of 32 required");
+  if (m == 0) return H3_OK;
+  TRY(check_mx("a", a, k_in, m));
+  TRY(check_mx("w", w, k_in, n_out));
+  TRY(check_rows("out", out, ld_out, n_out, m, H3_BF16));
+  CHECK(ld_out > 0, "out row stride must be positive");
+  if (gate) TRY(check_rows("gate", gate, ld_gate, n_out, m, H3_BF16));
+  TRY(check_device());
+  return hip_status(launch_gemm_mx8(gate ? EPI_RESIDUAL : EPI_STORE, mx_of(a), mx_of(w), MxOperand{},
+                                    out, ld_out, gate, ld_gate, m, n_out, k_in,
+                                    (hipStream_t)stream),
+                    "linear_fp8 launch");
+}
+
+size_t h3_swiglu_fp8_workspace_size(int64_t n_tok, int32_t ffn_dim) {
+  if (n_tok <= 0 || ffn_dim <= 0) return 0;
+  int64_t gq, gs;
+  return (size_t)swiglu_fp8_parts(n_tok, ffn_dim, &gq, &gs);
+}
+
+h3_status h3_swiglu_fp8(const h3_mx_operand* h, const h3_mx_operand* w1,
+                        const h3_mx_operand* w3, const h3_mx_operand* w2, void* out,
+                        int64_t ld_out, const void* gate, int64_t ld_gate, int64_t n_tok,
+                        int32_t dim, int32_t ffn_dim, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(n_tok >= 0 && n_tok <= (int64_t)INT32_MAX, "n_tok out of range");
+  CHECK(dim > 0 && dim % 32 == 0 && ffn_dim > 0 && ffn_dim % 32 == 0,
+        "dim and ffn_dim must be positive multiples of 32");
+  if (n_tok == 0) return H3_OK;
+  TRY(check_mx("h", h, dim, n_tok));
+  TRY(check_mx("w1", w1, dim, ffn_dim));
+  TRY(check_mx("w3", w3, dim, ffn_dim));
+  CHECK(w1->ld == w3->ld && w1->ld_scale == w3->ld_scale, "w1 and w3 must share ld and ld_scale");
+  TRY(check_mx("w2", w2, ffn_dim, dim));
+  TRY(check_rows("out", out, ld_out, dim, n_tok, H3_BF16));
+  CHECK(ld_out > 0, "out row stride must be positive");
+  if (gate) TRY(check_rows("gate", gate, ld_gate, dim, n_tok, H3_BF16));
+  int64_t gq_off, gs_off;
+  const size_t need = (size_t)swiglu_fp8_parts(n_tok, ffn_dim, &gq_off, &gs_off);
+  if (ws_bytes < need) return fail(H3_ERR_WORKSPACE, "swiglu_fp8 workspace %zu bytes, need %zu", ws_bytes, need);
+  CHECK(ws && aligned16(ws), "workspace is NULL or not 16-byte aligned");
+  TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const int64_t fp = round_up(ffn_dim, 128);
+  MxOperand g8;
+  g8.data = wsb + gq_off;
+  g8.ld = fp;
+  g8.scale = wsb + gs_off;
+  g8.ld_scale = fp / 32;
+  TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, mx_of(h), mx_of(w1), mx_of(w3), wsb, ffn_dim,
+                                 nullptr, 0, n_tok, ffn_dim, dim, s),
+                 "swiglu_fp8 up-projection launch"));
+  TRY(hip_status(launch_mx_quantize(wsb, ffn_dim, n_tok, ffn_dim, wsb + gq_off, fp, wsb + gs_off,
+                                    fp / 32, s),
+                 "swiglu_fp8 gate quantization launch"));
+  return hip_status(launch_gemm_mx8(gate ? EPI_RESIDUAL : EPI_STORE, g8, mx_of(w2), MxOperand{},
+                                    out, ld_out, gate, ld_gate, n_tok, dim, ffn_dim, s),
+                    "swiglu_fp8 down-projection launch");
 }
 
 // ------------------------------------------------------------------- block

@@ -40,6 +40,25 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
                        int64_t ld_gate, int64_t M, int N, int K, hipStream_t s,
                        const GemmMap& map = GemmMap{});
 
+// MX-scaled e4m3 operand (layout in k_gemm_fp8.hip): e4m3 data [rows][ld]
+// bytes with round_up(K, 128) columns, zeros past K, and E8M0 scale bytes
+// [rows][ld_scale], one per 32 columns
+struct MxOperand {
+  const void* data = nullptr;
+  int64_t ld = 0;
+  const void* scale = nullptr;
+  int64_t ld_scale = 0;
+};
+
+// bf16 x [rows][cols] (cols % 32 == 0) -> MX operand (q, scale)
+hipError_t launch_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int cols, void* q,
+                              int64_t ld_q, void* scale, int64_t ld_s, hipStream_t s);
+// bf16 out = A @ B^T over MX operands (K the logical contraction length); for
+// EPI_SWIGLU, b = W1, b3 = W3 (same ld and ld_scale) and N = features
+hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, const MxOperand& b3,
+                           void* C, int64_t ldc, const void* gate, int64_t ld_gate, int64_t M,
+                           int N, int K, hipStream_t s);
+
 size_t attn_workspace_bytes(bool bf16, int64_t n_buf, int n_heads, int head_dim, int n_seg);
 hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld_q,
                               const void* k, int64_t ld_k, const void* v, int64_t ld_v, void* o,

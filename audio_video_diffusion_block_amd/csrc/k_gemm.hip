@@ -23,8 +23,12 @@
 // fp32 path: a plain LDS-tiled FMA kernel (small problems, parity runs).
 #include "h3_common.hpp"
 #include "h3_kernels.hpp"
+#include "h3_gemm_tile.hpp"
 
 namespace h3 {
+
+using gemm_tile::silu_f;
+using gemm_tile::tile_of;
 
 namespace {
 
@@ -32,27 +36,9 @@ constexpr int BM = 256;
 constexpr int BN = 256;  // rows of the B tile
 constexpr int BK = 64;
 constexpr int NTHREADS = 512;
-constexpr int GROUP_M = 4;
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * BK + ((chunk ^ (row & 7)) << 3);
-}
-
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
-
-// XCD-aware mapping of a linear work-group id to (tile_m, tile_n).
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  const int total8 = total / 8 * 8;
-  // consecutive ids go to different XCDs; give each XCD a contiguous run of tiles
-  const int logical = bid < total8 ? (bid % 8) * (total8 / 8) + bid / 8 : bid;
-  const int per_group = GROUP_M * tiles_n;
-  const int group = logical / per_group;
-  const int first_m = group * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int in_group = logical - group * per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
 }
 
 }  // namespace
@@ -364,95 +350,8 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
   for (int kt = 0; kt + 1 < nk; ++kt) k_step(kt, std::true_type{});
   k_step(nk - 1, std::false_type{});
 
-  // ---- epilogue through LDS.  A lane holds column lane%32 and rows
-  // (r/4)*8 + (lane/32)*4 + r%4 of each 32x32 block; the tile is written to LDS
-  // in that layout and read back as row-contiguous 16-byte chunks, so every
-  // global access is a 16-byte vector.  Padded LDS rows keep the lane-per-
-  // column writes of the two lane halves (rows 4 apart) on disjoint banks.
-  __syncthreads();  // every wave is done with the last tile's fragments
-  const int tid = threadIdx.x;
-  if constexpr (EPI == EPI_RESIDUAL) {
-    // out = out + gate * acc with acc in fp32: two passes of 128 rows
-    constexpr int FS = 264;  // floats per LDS row
-    float* ef = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wm == half) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              ef[(mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3)) * FS + wn * 128 + ni * 32 + fr] = acc[mi][ni][r];
-      }
-      __syncthreads();
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const int chunk = tid + i * W4_THREADS;  // 128 rows x 32 chunks of 8
-        const int rl = chunk >> 5, c8 = (chunk & 31) * 8;
-        const int row = m0 + half * 128 + rl, col = tn * BN + c8;
-        if (row >= M || col >= N) continue;
-        const float* src = ef + rl * FS + c8;
-        bf16_t* po = C + (int64_t)row * ldc + col;
-        const bf16_t* pg = gate + (int64_t)row * ld_gate + col;
-        if (col + 8 <= N) {
-          const float4 y0 = *reinterpret_cast<const float4*>(src);
-          const float4 y1 = *reinterpret_cast<const float4*>(src + 4);
-          const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-          uint4 xo = *reinterpret_cast<const uint4*>(po);
-          const uint4 gv = *reinterpret_cast<const uint4*>(pg);
-          bf16_t* xe = reinterpret_cast<bf16_t*>(&xo);
-          const bf16_t* ge = reinterpret_cast<const bf16_t*>(&gv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xe[e] = f2bf(bf2f(xe[e]) + bf2f(ge[e]) * yv[e]);
-          *reinterpret_cast<uint4*>(po) = xo;
-        } else {
-          for (int e = 0; col + e < N; ++e) po[e] = f2bf(bf2f(po[e]) + bf2f(pg[e]) * src[e]);
-        }
-      }
-      __syncthreads();
-    }
-  } else {
-    // bf16 tile: 256 rows x OC columns (256, or 128 SwiGLU outputs)
-    constexpr int OC = EPI == EPI_SWIGLU ? 128 : 256;
-    constexpr int ES = OC + 8;  // bf16 per LDS row
-    bf16_t* eb = reinterpret_cast<bf16_t*>(smem);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 128 + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3);
-        if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            eb[rl * ES + (wn * 2 + j) * 32 + fr] = f2bf(silu_f(acc[mi][2 * j][r]) * acc[mi][2 * j + 1][r]);
-        } else {
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) eb[rl * ES + wn * 128 + ni * 32 + fr] = f2bf(acc[mi][ni][r]);
-        }
-      }
-    __syncthreads();
-    constexpr int CPR = OC / 8;  // 16-byte chunks per row
-#pragma unroll 4
-    for (int i = 0; i < 256 * CPR / W4_THREADS; ++i) {
-      const int chunk = tid + i * W4_THREADS;
-      const int rl = chunk / CPR, c8 = (chunk % CPR) * 8;
-      const int row = m0 + rl, col = (EPI == EPI_SWIGLU ? tn * 128 : tn * BN) + c8;
-      if (row >= M || col >= N) continue;
-      const bf16_t* src = eb + rl * ES + c8;
-      bf16_t* po = C + (int64_t)row * ldc + col;
-      if (EPI == EPI_STORE && map.peer_hc) {
-        // peer-major scatter of an 8-column chunk (it never straddles a head)
-        const int hd = map.peer_H * map.peer_D, which = col / hd;
-        const int h = (col - which * hd) / map.peer_D, d = col - which * hd - h * map.peer_D;
-        const int p = h / map.peer_hc, j = h - p * map.peer_hc;
-        po = C + (((int64_t)p * M + row) * 3 + which) * map.peer_hc * map.peer_D + j * map.peer_D + d;
-      }
-      if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
-      else for (int e = 0; col + e < N; ++e) po[e] = src[e];
-    }
-  }
+  // ---- epilogue through LDS (shared with the FP8 kernel)
+  gemm_tile::epilogue<EPI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh, map);
 }
 
 // ---------------------------------------------------------------- fp32 path

@@ -201,6 +201,67 @@ h3_status h3_swiglu(const void* h, int64_t ld_h, const void* w1, const void* w3,
                     int64_t ld_gate, int64_t n_tok, int32_t dim, int32_t ffn_dim, void* ws,
                     size_t ws_bytes, h3_dtype dtype, void* stream);
 
+/* ------------------------------------------- FP8 (MX e4m3) projections */
+
+/*
+ * Online FP8 projections (MiniMax H3 通过 vLLM-Omni 实现 FastH3 实时推理,
+ * "超出 FastH3 配置的扩展能力": an online FP8 quantization path lowers the
+ * peak HBM footprint and the latency).  Both operands of a projection are MX
+ * operands: OCP e4m3 values with one power-of-two (E8M0) scale per 32
+ * consecutive elements along the contraction, the smallest scale 2^e with
+ * block amax <= 448 * 2^e, elements rounded to nearest (ties to even).
+ * Weights are quantized once; activations on the fly, from bf16.
+ *
+ * h3_mx_operand -- k logical columns stored as:
+ *   data:  e4m3 bytes [rows][ld]; 16-byte aligned; ld a multiple of 16 with
+ *          round_up(k, 128) <= ld <= 2^23; columns [k, round_up(k, 128)) are zero.
+ *   scale: E8M0 bytes [rows][ld_scale]; 4-byte aligned; ld_scale a multiple of 4,
+ *          >= round_up(k, 128) / 32; byte b scales columns [32 b, 32 b + 32)
+ *          (value = e4m3 * 2^(byte - 127)).
+ * The caller owns both buffers.
+ */
+typedef struct {
+  const void* data;
+  int64_t ld;
+  const void* scale;
+  int64_t ld_scale;
+} h3_mx_operand;
+
+/*
+ * h3_mx_quantize -- bf16 x [rows][cols] (row stride ld_x elements, cols % 32 == 0)
+ * -> MX operand (q, ld_q, scale, ld_scale) as above, including the zero
+ * columns up to round_up(cols, 128) (their scale byte is 127).
+ * Errors: H3_ERR_UNSUPPORTED unless dtype is H3_BF16; H3_ERR_ARG for shapes,
+ * strides or alignment.
+ */
+h3_status h3_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int32_t cols, void* q,
+                         int64_t ld_q, void* scale, int64_t ld_scale, h3_dtype dtype,
+                         void* stream);
+
+/*
+ * h3_linear_fp8 -- out = a w^T over MX operands a [m][k_in] and w [n_out][k_in]
+ * (k_in % 32 == 0), fp32 accumulation, bf16 out [m][n_out] (row stride ld_out).
+ * gate != NULL: out = out + gate * (a w^T) in place (gate bf16 [m][n_out]).
+ */
+h3_status h3_linear_fp8(const h3_mx_operand* a, const h3_mx_operand* w, void* out,
+                        int64_t ld_out, int64_t m, int32_t n_out, int32_t k_in,
+                        const void* gate, int64_t ld_gate, void* stream);
+
+/*
+ * h3_swiglu_fp8 -- the SwiGLU MLP of h3_swiglu over MX operands: h [n_tok][dim],
+ * w1, w3 [ffn_dim][dim] (same ld and ld_scale), w2 [dim][ffn_dim]; the gate
+ * product g = silu(h w1^T) * (h w3^T) is rounded to bf16 and quantized on the
+ * fly into the workspace before the down-projection.  out / gate as in
+ * h3_linear_fp8.  dim % 32 == 0, ffn_dim % 32 == 0.
+ *   ws: h3_swiglu_fp8_workspace_size(n_tok, ffn_dim) bytes, 16-byte aligned; on
+ *   return it starts with g (bf16 [n_tok][ffn_dim]), followed by g's MX operand.
+ */
+size_t h3_swiglu_fp8_workspace_size(int64_t n_tok, int32_t ffn_dim);
+h3_status h3_swiglu_fp8(const h3_mx_operand* h, const h3_mx_operand* w1,
+                        const h3_mx_operand* w3, const h3_mx_operand* w2, void* out,
+                        int64_t ld_out, const void* gate, int64_t ld_gate, int64_t n_tok,
+                        int32_t dim, int32_t ffn_dim, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ whole block */
 
 typedef struct {

@@ -24,6 +24,14 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
+# e4m3 byte -> value (OCP: bias 7, 3 mantissa bits, 0x7F/0xFF NaN), from the format's definition
+E4M3_DECODE = np.array([(-1.0 if c & 0x80 else 1.0) *
+                        (((c & 7) * 2.0 ** -9) if ((c >> 3) & 15) == 0
+                         else (1 + (c & 7) / 8) * 2.0 ** (((c >> 3) & 15) - 7))
+                        for c in range(256)])
+E4M3_DECODE[0x7F] = E4M3_DECODE[0xFF] = np.nan
+
+
 def errors(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

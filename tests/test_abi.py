@@ -170,3 +170,44 @@ def test_peer_major_layout_argument_checks():
     f32 = h3.BlockConfig(256, 4, 64, 704, 16, 24, 24, 1e4, 1e-6, 1e-6, 0, h3.H3_F32)
     assert run(io(), f32) == h3.H3_ERR_ARG and "bf16" in h3.last_error()
 
+
+
+def test_fp8_projection_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    M = h3.MxOperand
+    # quantize: bf16 only, cols a multiple of 32, padded row length
+    assert h3._c_mxq(FAKE, 256, 10, 256, FAKE, 256, FAKE, 8, h3.H3_F32, None) == h3.H3_ERR_UNSUPPORTED
+    st = h3._c_mxq(FAKE, 256, 10, 200, FAKE, 256, FAKE, 8, h3.H3_BF16, None)
+    assert st == h3.H3_ERR_ARG and "32" in h3.last_error()
+    st = h3._c_mxq(FAKE, 704, 10, 704, FAKE, 704, FAKE, 24, h3.H3_BF16, None)
+    assert st == h3.H3_ERR_ARG and "ld" in h3.last_error()  # needs round_up(704, 128) = 768
+    st = h3._c_mxq(FAKE, 704, 10, 704, FAKE, 768, FAKE, 22, h3.H3_BF16, None)
+    assert st == h3.H3_ERR_ARG and "ld_scale" in h3.last_error()
+    assert h3._c_mxq(None, 704, 0, 704, None, 768, None, 24, h3.H3_BF16, None) == h3.H3_OK
+    # linear: k a multiple of 32; scale alignment and stride
+    a = M(FAKE, 256, FAKE, 8)
+    w = M(FAKE, 256, FAKE, 8)
+    st = h3._c_lin8(ctypes.byref(a), ctypes.byref(w), FAKE, 64, 10, 64, 250, None, 0, None)
+    assert st == h3.H3_ERR_ARG
+    bad = M(FAKE, 256, FAKE + 2, 8)
+    st = h3._c_lin8(ctypes.byref(bad), ctypes.byref(w), FAKE, 64, 10, 64, 256, None, 0, None)
+    assert st == h3.H3_ERR_ARG and "scale" in h3.last_error()
+    bad = M(FAKE, 256, FAKE, 6)
+    st = h3._c_lin8(ctypes.byref(a), ctypes.byref(bad), FAKE, 64, 10, 64, 256, None, 0, None)
+    assert st == h3.H3_ERR_ARG and "ld_scale" in h3.last_error()
+    bad = M(FAKE + 8, 256, FAKE, 8)
+    st = h3._c_lin8(ctypes.byref(bad), ctypes.byref(w), FAKE, 64, 10, 64, 256, None, 0, None)
+    assert st == h3.H3_ERR_ARG and "aligned" in h3.last_error()
+    # swiglu: w1 and w3 share strides; workspace size
+    h = M(FAKE, 256, FAKE, 8)
+    w13 = M(FAKE, 256, FAKE, 8)
+    w3b = M(FAKE, 384, FAKE, 12)
+    w2 = M(FAKE, 768, FAKE, 24)
+    args = lambda w3_, ws: [ctypes.byref(h), ctypes.byref(w13), ctypes.byref(w3_), ctypes.byref(w2),
+                            FAKE, 256, None, 0, 10, 256, 704, FAKE, ws, None]
+    st = h3._c_sw8(*args(w3b, 1 << 30))
+    assert st == h3.H3_ERR_ARG and "share" in h3.last_error()
+    need = h3._c_sw8_ws(10, 704)
+    assert need >= 10 * 704 * 2 + 10 * 768 + 10 * 24
+    st = h3._c_sw8(*args(w13, need - 16))
+    assert st == h3.H3_ERR_WORKSPACE

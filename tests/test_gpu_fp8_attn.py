@@ -10,15 +10,9 @@ import torch
 
 import oracle as O
 import workloads as W
-from _util import dev, dev_i32, host
+from _util import E4M3_DECODE as _E4M3, dev, dev_i32, host
 
 pytestmark = pytest.mark.gpu
-
-# e4m3 byte -> value (OCP: bias 7, 0x7F/0xFF NaN)
-_E4M3 = np.array([(-1.0 if c & 0x80 else 1.0) *
-                  (((c & 7) * 2.0 ** -9) if ((c >> 3) & 15) == 0 else (1 + (c & 7) / 8) * 2.0 ** (((c >> 3) & 15) - 7))
-                  for c in range(256)])
-_E4M3[0x7F] = _E4M3[0xFF] = np.nan
 
 # tolerances (outputs are O(1) means of unit-variance values):
 #   vs the oracle on the same quantized operands, the kernel differs only by
