@@ -47,12 +47,16 @@ class BlockConfig(ctypes.Structure):
     _fields_ = [("dim", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn_dim", _i32),
                 ("sec_t", _i32), ("sec_h", _i32), ("sec_w", _i32), ("theta", _f),
                 ("eps_qk", _f), ("eps_mod", _f), ("norm_kind", _i32), ("dtype", _i32),
-                ("attn_fp8", _i32)]
+                ("attn_fp8", _i32), ("gemm_fp8", _i32)]
+
+
+class MxOperand(ctypes.Structure):
+    _fields_ = [("data", _p), ("ld", _i64), ("scale", _p), ("ld_scale", _i64)]
 
 
 class BlockWeights(ctypes.Structure):
     _fields_ = [("w_qkv", _p), ("w_o", _p), ("w1", _p), ("w3", _p), ("w2", _p), ("g_q", _p),
-                ("g_k", _p)]
+                ("g_k", _p), ("mx", ctypes.POINTER(MxOperand))]
 
 
 class BlockIO(ctypes.Structure):
@@ -61,10 +65,6 @@ class BlockIO(ctypes.Structure):
                 ("n_tok_local", _i64), ("n_buf", _i64), ("tok_begin", _i64),
                 ("head_begin", _i32), ("head_count", _i32), ("qkv_attn", _p), ("o_attn", _p),
                 ("o_local", _p), ("qkv_send", _p), ("o_recv", _p)]
-
-
-class MxOperand(ctypes.Structure):
-    _fields_ = [("data", _p), ("ld", _i64), ("scale", _p), ("ld_scale", _i64)]
 
 
 def _sig(name, res, args):
@@ -321,10 +321,17 @@ def h3_swiglu_fp8(h: MxTensor, w1: MxTensor, w3: MxTensor, w2: MxTensor, out, ga
 
 def block_config(dim, n_heads, head_dim, ffn_dim, sections, theta=1e4, eps_qk=1e-6,
                  eps_mod=1e-6, norm_kind=0, dtype=torch.bfloat16,
-                 attn_fp8=False) -> BlockConfig:
+                 attn_fp8=False, gemm_fp8=False) -> BlockConfig:
     return BlockConfig(dim, n_heads, head_dim, ffn_dim, sections[0], sections[1], sections[2],
                        theta, eps_qk, eps_mod, norm_kind,
-                       H3_BF16 if dtype == torch.bfloat16 else H3_F32, int(bool(attn_fp8)))
+                       H3_BF16 if dtype == torch.bfloat16 else H3_F32, int(bool(attn_fp8)),
+                       int(bool(gemm_fp8)))
+
+
+def block_weights_mx(weights: dict, stream=None) -> list:
+    """MX copies (MxTensor) of a block's bf16 projection weights, in the order
+    h3_block_weights.mx takes them: w_qkv, w_o, w1, w3, w2."""
+    return [h3_mx_quantize(weights[k], stream=stream) for k in ("w_qkv", "w_o", "w1", "w3", "w2")]
 
 
 def block_workspace_size(cfg: BlockConfig, n_tok_local: int, n_buf: int, n_seg: int) -> int:
@@ -345,7 +352,12 @@ def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots,
     share = qkv_attn is not None
     n_buf = n_buf if n_buf is not None else (qkv_attn.shape[0] if share else n)
     n_seg = cu_slots.shape[0] - 1
-    w = BlockWeights(*(_ptr(weights[k]) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")))
+    mx = None
+    if weights.get("mx") is not None:
+        # MX copies of w_qkv, w_o, w1, w3, w2 (MxTensor each) for cfg.gemm_fp8
+        mx = (MxOperand * 5)(*[m.c() for m in weights["mx"]])
+    w = BlockWeights(*(_ptr(weights.get(k)) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")),
+                     ctypes.cast(mx, ctypes.POINTER(MxOperand)) if mx is not None else None)
     ld_mod = 0 if mod.shape[0] == 1 else mod.stride(0)
     io = BlockIO(_ptr(x), _ld(x), _ptr(mod), ld_mod, _ptr(pos), _ptr(cu_slots), _ptr(valid_len),
                  n_seg, max_valid_len, n, n_buf, tok_begin, head_begin,

@@ -463,7 +463,8 @@ h3_status h3_swiglu_fp8(const h3_mx_operand* h, const h3_mx_operand* w1,
 
 namespace {
 struct BlockWs {
-  size_t h1, qkv, attn, o, g, total;
+  size_t h1, qkv, attn, o, g, xq, xs, gq, gs, total;
+  int64_t xkp, fkp;  // padded widths of the activation and g MX operands
 };
 
 BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int32_t n_seg,
@@ -486,6 +487,15 @@ BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int3
                                                             c->head_dim, n_seg));
   w.o = take(share ? 0 : n * hd * es);
   w.g = take(n * (int64_t)c->ffn_dim * es);
+  if (c->gemm_fp8) {
+    // MX copies of the projection inputs: h1 / o / h2 share one (width max(C, H*D)), g its own
+    w.xkp = round_up(c->dim > hd ? c->dim : hd, 128);
+    w.fkp = round_up(c->ffn_dim, 128);
+    w.xq = take(n * w.xkp);
+    w.xs = take(n * (w.xkp / 32));
+    w.gq = take(n * w.fkp);
+    w.gs = take(n * (w.fkp / 32));
+  }
   w.total = off;
   return w;
 }
@@ -515,6 +525,13 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   CHECK(cfg->theta > 0.f && cfg->eps_qk >= 0.f && cfg->eps_mod >= 0.f, "theta/eps out of range");
   CHECK(cfg->attn_fp8 == 0 || cfg->attn_fp8 == 1, "attn_fp8 must be 0 or 1");
   CHECK(!cfg->attn_fp8 || dt == H3_BF16, "the FP8 attention path needs bf16 storage");
+  CHECK(cfg->gemm_fp8 == 0 || cfg->gemm_fp8 == 1, "gemm_fp8 must be 0 or 1");
+  const bool f8 = cfg->gemm_fp8 == 1;
+  if (f8) {
+    CHECK(dt == H3_BF16, "the FP8 projections need bf16 storage");
+    CHECK(C % 32 == 0 && F % 32 == 0 && ((int64_t)H * D) % 32 == 0,
+          "the FP8 projections need dim, ffn_dim and n_heads*head_dim multiples of 32");
+  }
   const int64_t n = io->n_tok_local;
   CHECK(n >= 0 && n <= (int64_t)INT32_MAX, "n_tok_local out of range");
   const bool share = io->qkv_attn != nullptr;
@@ -552,8 +569,21 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   TRY(check_rows("x", io->x, io->ld_x, C, n, dt));
   CHECK(io->ld_x > 0, "x row stride must be positive");
   TRY(check_rows("mod", io->mod, io->ld_mod, 6 * (int64_t)C, n, dt));
-  const void* wp[] = {w->w_qkv, w->w_o, w->w1, w->w3, w->w2, w->g_q, w->g_k};
-  for (const void* p : wp) CHECK(p && aligned16(p), "a weight pointer is NULL or misaligned");
+  if (f8) {
+    CHECK(w->mx, "gemm_fp8 needs the MX weights (weights.mx)");
+    const int64_t hd_ = (int64_t)H * D;
+    TRY(check_mx("w_qkv (mx)", &w->mx[0], C, 3 * hd_));
+    TRY(check_mx("w_o (mx)", &w->mx[1], hd_, C));
+    TRY(check_mx("w1 (mx)", &w->mx[2], C, F));
+    TRY(check_mx("w3 (mx)", &w->mx[3], C, F));
+    TRY(check_mx("w2 (mx)", &w->mx[4], F, C));
+    CHECK(w->mx[2].ld == w->mx[3].ld && w->mx[2].ld_scale == w->mx[3].ld_scale,
+          "w1 and w3 (mx) must share ld and ld_scale");
+    CHECK(w->g_q && w->g_k && aligned16(w->g_q) && aligned16(w->g_k), "a gain pointer is NULL or misaligned");
+  } else {
+    const void* wp[] = {w->w_qkv, w->w_o, w->w1, w->w3, w->w2, w->g_q, w->g_k};
+    for (const void* p : wp) CHECK(p && aligned16(p), "a weight pointer is NULL or misaligned");
+  }
   const BlockWs L = block_ws_layout(cfg, n, io->n_buf, io->n_seg, share, hc);
   if (ws_bytes < L.total)
     return fail(H3_ERR_WORKSPACE, "block workspace %zu bytes, need %zu", ws_bytes, L.total);
@@ -588,6 +618,19 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                                     io->cu_slots, io->valid_len, io->n_seg, io->max_valid_len,
                                     scale, attn_ws, s);
   };
+  // FP8 projections: the activation is quantized into the workspace, then multiplied
+  MxOperand xq;
+  xq.data = wsb + L.xq;
+  xq.ld = L.xkp;
+  xq.scale = wsb + L.xs;
+  xq.ld_scale = L.xkp / 32;
+  auto quant_act = [&](const void* src, int64_t ld_src, int cols, int kgroup = 0,
+                       int64_t gstride = 0) {
+    return hip_status(launch_mx_quantize(src, ld_src, n, cols, wsb + L.xq, L.xkp, wsb + L.xs,
+                                         L.xkp / 32, s, kgroup, gstride),
+                      "activation quantization");
+  };
+  auto wmx = [&](int i) { return f8 ? mx_of(&w->mx[i]) : MxOperand{}; };
   if (peer) {
     // Peer-major exchange layout: every all-to-all block is contiguous.
     const int P = H / hc, r = hb / hc;
@@ -599,9 +642,16 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
     scatter.peer_H = H;
     scatter.peer_hc = hc;
     scatter.peer_D = D;
-    TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, send, 3 * hd, nullptr,
-                               0, n, (int)(3 * hd), C, s, scatter),
-                   "qkv projection (peer-major)"));
+    if (f8) {
+      TRY(quant_act(h1, C, C));
+      TRY(hip_status(launch_gemm_mx8(EPI_STORE, xq, wmx(0), MxOperand{}, send, 3 * hd, nullptr, 0,
+                                     n, (int)(3 * hd), C, s, scatter),
+                     "qkv projection (peer-major, fp8)"));
+    } else {
+      TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, send, 3 * hd,
+                                 nullptr, 0, n, (int)(3 * hd), C, s, scatter),
+                     "qkv projection (peer-major)"));
+    }
     // A3 Q/K RMSNorm + RoPE on the local rows, one launch per peer block
     for (int p = 0; p < P; ++p) {
       char* b = send + p * blk;
@@ -629,14 +679,28 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
     GemmMap grouped;
     grouped.a_kgroup = (int)sd;
     grouped.a_gstride = n * sd;
-    TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, io->o_recv, sd, w->w_o, nullptr, hd, io->x,
-                               io->ld_x, mslot(2), ldm, n, C, (int)hd, s, grouped),
-                   "output projection (peer-major)"));
+    if (f8) {
+      TRY(quant_act(io->o_recv, sd, (int)hd, (int)sd, n * sd));
+      TRY(hip_status(launch_gemm_mx8(EPI_RESIDUAL, xq, wmx(1), MxOperand{}, io->x, io->ld_x,
+                                     mslot(2), ldm, n, C, (int)hd, s),
+                     "output projection (peer-major, fp8)"));
+    } else {
+      TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, io->o_recv, sd, w->w_o, nullptr, hd, io->x,
+                                 io->ld_x, mslot(2), ldm, n, C, (int)hd, s, grouped),
+                     "output projection (peer-major)"));
+    }
   } else {
   // A2 qkv = h1 w_qkv^T
-  TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, qkv, 3 * hd, nullptr, 0,
-                             n, (int)(3 * hd), C, s),
-                 "qkv projection"));
+  if (f8) {
+    TRY(quant_act(h1, C, C));
+    TRY(hip_status(launch_gemm_mx8(EPI_STORE, xq, wmx(0), MxOperand{}, qkv, 3 * hd, nullptr, 0, n,
+                                   (int)(3 * hd), C, s),
+                   "qkv projection (fp8)"));
+  } else {
+    TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, qkv, 3 * hd, nullptr,
+                               0, n, (int)(3 * hd), C, s),
+                   "qkv projection"));
+  }
   // A3 Q/K RMSNorm + RoPE on the local rows
   TRY(hip_status(launch_qk_norm_rope(bf, D, qkv, 3 * hd, qkv + hd * es, 3 * hd, n, H, w->g_q,
                                      w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
@@ -670,9 +734,16 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
     o_for_proj = io->o_local;
   }
   // A7 x <- x + gate1 * (o w_o^T)
-  TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, o_for_proj, hd, w->w_o, nullptr, hd, io->x,
-                             io->ld_x, mslot(2), ldm, n, C, (int)hd, s),
-                 "output projection"));
+  if (f8) {
+    TRY(quant_act(o_for_proj, hd, (int)hd));
+    TRY(hip_status(launch_gemm_mx8(EPI_RESIDUAL, xq, wmx(1), MxOperand{}, io->x, io->ld_x,
+                                   mslot(2), ldm, n, C, (int)hd, s),
+                   "output projection (fp8)"));
+  } else {
+    TRY(hip_status(launch_gemm(bf, EPI_RESIDUAL, o_for_proj, hd, w->w_o, nullptr, hd, io->x,
+                               io->ld_x, mslot(2), ldm, n, C, (int)hd, s),
+                   "output projection"));
+  }
   }
   // A8 h2 = norm(x)(1 + scale2) + shift2   (h2 reuses h1's scratch)
   TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(3),
@@ -681,6 +752,22 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                  "modulate-2"));
   // A9 g = silu(h2 w1^T) * (h2 w3^T)
   void* g = wsb + L.g;
+  if (f8) {
+    TRY(quant_act(h1, C, C));
+    TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, xq, wmx(2), wmx(3), g, F, nullptr, 0, n, F, C, s),
+                   "swiglu up-projection (fp8)"));
+    // A10 x <- x + gate2 * (g w2^T), g quantized on the fly
+    TRY(hip_status(launch_mx_quantize(g, F, n, F, wsb + L.gq, L.fkp, wsb + L.gs, L.fkp / 32, s),
+                   "gate-product quantization"));
+    MxOperand gq;
+    gq.data = wsb + L.gq;
+    gq.ld = L.fkp;
+    gq.scale = wsb + L.gs;
+    gq.ld_scale = L.fkp / 32;
+    return hip_status(launch_gemm_mx8(EPI_RESIDUAL, gq, wmx(4), MxOperand{}, io->x, io->ld_x,
+                                      mslot(5), ldm, n, C, F, s),
+                      "swiglu down-projection (fp8)");
+  }
   TRY(hip_status(launch_gemm(bf, EPI_SWIGLU, h1, C, w->w1, w->w3, C, g, F, nullptr, 0, n, F, C, s),
                  "swiglu up-projection"));
   // A10 x <- x + gate2 * (g w2^T)

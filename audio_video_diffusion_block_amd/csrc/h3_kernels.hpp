@@ -50,14 +50,16 @@ struct MxOperand {
   int64_t ld_scale = 0;
 };
 
-// bf16 x [rows][cols] (cols % 32 == 0) -> MX operand (q, scale)
+// bf16 x [rows][cols] (cols % 32 == 0) -> MX operand (q, scale); kgroup > 0:
+// columns [g*kgroup, (g+1)*kgroup) of row r at x + g*gstride + r*ld_x (elements)
 hipError_t launch_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int cols, void* q,
-                              int64_t ld_q, void* scale, int64_t ld_s, hipStream_t s);
+                              int64_t ld_q, void* scale, int64_t ld_s, hipStream_t s,
+                              int kgroup = 0, int64_t gstride = 0);
 // bf16 out = A @ B^T over MX operands (K the logical contraction length); for
 // EPI_SWIGLU, b = W1, b3 = W3 (same ld and ld_scale) and N = features
 hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, const MxOperand& b3,
                            void* C, int64_t ldc, const void* gate, int64_t ld_gate, int64_t M,
-                           int N, int K, hipStream_t s);
+                           int N, int K, hipStream_t s, const GemmMap& map = GemmMap{});
 
 size_t attn_workspace_bytes(bool bf16, int64_t n_buf, int n_heads, int head_dim, int n_seg);
 hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld_q,

@@ -39,9 +39,12 @@ using namespace fp8;
 
 // bf16 rows [rows][cols] (cols % 32 == 0) -> MX operand with kp columns
 // (zeros and scale byte 127 past cols).  One thread per 32-element block.
+// kgroup > 0: the source is grouped along the columns -- columns
+// [g*kgroup, (g+1)*kgroup) of row r sit at x + g*gstride + r*ld_x.
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16_t* __restrict__ x,
                                                             int64_t ld_x, int64_t rows, int cols,
-                                                            int kp, uint8_t* __restrict__ q,
+                                                            int kp, int kgroup, int64_t gstride,
+                                                            uint8_t* __restrict__ q,
                                                             int64_t ld_q,
                                                             uint8_t* __restrict__ sc,
                                                             int64_t ld_s) {
@@ -53,7 +56,12 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16_t* __rest
   uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   uint32_t e = 127;
   if (b * 32 < cols) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld_x + b * 32);
+    int64_t c0 = b * 32;
+    if (kgroup > 0) {
+      const int g = b * 32 / kgroup;
+      c0 = g * gstride + (b * 32 - g * kgroup);
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld_x + c0);
     float v[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ B3, int64_t ldb,
     const uint8_t* __restrict__ Bs, const uint8_t* __restrict__ B3s, int64_t ld_bs, bf16_t* C,
     int64_t ldc, const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, GemmMap map) {
   // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
   __shared__ __attribute__((aligned(1024))) char smem[135168];
 
@@ -258,27 +266,30 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
   // the epilogue reads every accumulator: let the last scaled MFMAs finish
   scaled_mfma_drain();
 
-  gemm_tile::epilogue<EPI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh,
-                           GemmMap{});
+  gemm_tile::epilogue<EPI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh, map);
 }
 
 // ------------------------------------------------------------------ launch
 
 hipError_t launch_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int cols, void* q,
-                              int64_t ld_q, void* scale, int64_t ld_s, hipStream_t s) {
+                              int64_t ld_q, void* scale, int64_t ld_s, hipStream_t s, int kgroup,
+                              int64_t gstride) {
   if (rows == 0) return hipSuccess;
+  if (kgroup < 0 || kgroup % 32 != 0) return hipErrorInvalidValue;
   const int kp = (int)round_up((int64_t)cols, 128);
   const int64_t threads = rows * (kp / 32);
   hipLaunchKernelGGL(mx_quant_rows_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0,
-                     s, (const bf16_t*)x, ld_x, rows, cols, kp, (uint8_t*)q, ld_q,
-                     (uint8_t*)scale, ld_s);
+                     s, (const bf16_t*)x, ld_x, rows, cols, kp, kgroup, gstride, (uint8_t*)q,
+                     ld_q, (uint8_t*)scale, ld_s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, const MxOperand& b3,
                            void* C, int64_t ldc, const void* gate, int64_t ld_gate, int64_t M,
-                           int N, int K, hipStream_t s) {
+                           int N, int K, hipStream_t s, const GemmMap& map) {
   if (M == 0 || N == 0) return hipSuccess;
+  // only the store epilogue's peer-major scatter applies here (A is an MX operand)
+  if (map.a_kgroup != 0 || (map.peer_hc && epi != EPI_STORE)) return hipErrorInvalidValue;
   const int kp = (int)round_up((int64_t)K, 128);
   const int tiles_m = (int)ceil_div(M, F8_BM);
   const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : F8_BN);
@@ -288,7 +299,7 @@ hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, cons
                      (const uint8_t*)a.data, a.ld, (const uint8_t*)a.scale, a.ld_scale,        \
                      (const uint8_t*)b.data, (const uint8_t*)b3.data, b.ld,                    \
                      (const uint8_t*)b.scale, (const uint8_t*)b3.scale, b.ld_scale, (bf16_t*)C, \
-                     ldc, (const bf16_t*)gate, ld_gate, (int)M, N, kp, tiles_m, tiles_n)
+                     ldc, (const bf16_t*)gate, ld_gate, (int)M, N, kp, tiles_m, tiles_n, map)
   if (epi == EPI_SWIGLU) H3_G(EPI_SWIGLU);
   else if (epi == EPI_RESIDUAL) H3_G(EPI_RESIDUAL);
   else H3_G(EPI_STORE);

@@ -401,15 +401,30 @@ def main():
         ops["block_peer_major"] = timer.time(lambda: h3.h3_dit_block_forward(
             cfg, wd, xp, mod, pos, cu, vl, max_len, ws=ws, **peer), reps)
         del peer, xp
-    # the whole block with the FP8 attention step (same launch sequence otherwise)
-    cfg8 = h3.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
-                           wl.eps_qk, wl.eps_mod, 0, bf, attn_fp8=True)
-    ws_b8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, n_buf, 1), dtype=torch.uint8,
-                        device="cuda")
-    x8 = x0.clone()
-    ops["block_fp8_attention"] = timer.time(lambda: h3.h3_dit_block_forward(
-        cfg8, wd, x8, mod, pos, cu, vl, max_len, ws=ws_b8, **share), reps)
-    del ws_b8, x8
+    # FP8 projections on MX operands: weights quantized once, activations on the fly
+    wmx = h3.block_weights_mx(wd)
+    h1m = h3.h3_mx_quantize(h1)
+    ops["act_quant"] = timer.time(lambda: h3.h3_mx_quantize(h1, h1m), reps)
+    ops["qkv_gemm_fp8"] = timer.time(lambda: h3.h3_linear_fp8(h1m, wmx[0], qkv), reps)
+    om = h3.h3_mx_quantize(o_in)
+    ops["out_gemm_residual_fp8"] = timer.time(lambda: h3.h3_linear_fp8(om, wmx[1], xs, gate=mod[:, 2]), reps)
+    sw8_ws = torch.empty(h3.swiglu_fp8_workspace_size(wl.n_loc, wl.ffn_dim), dtype=torch.uint8, device="cuda")
+    ops["swiglu_residual_fp8"] = timer.time(lambda: h3.h3_swiglu_fp8(
+        h1m, wmx[2], wmx[3], wmx[4], xs, gate=mod[:, 5], ws=sw8_ws), reps)
+    del om, sw8_ws
+    # the whole block with FP8 steps (same launch sequence otherwise)
+    wd8 = {"mx": wmx, "g_q": wd["g_q"], "g_k": wd["g_k"]}
+    for key, a8, g8 in (("block_fp8_attention", True, False), ("block_fp8_projections", False, True),
+                        ("block_fp8", True, True)):
+        cfg8 = h3.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
+                               wl.eps_qk, wl.eps_mod, 0, bf, attn_fp8=a8, gemm_fp8=g8)
+        ws_b8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, n_buf, 1), dtype=torch.uint8,
+                            device="cuda")
+        x8 = x0.clone()
+        ops[key] = timer.time(lambda: h3.h3_dit_block_forward(
+            cfg8, wd8 if g8 else wd, x8, mod, pos, cu, vl, max_len, ws=ws_b8, **share), reps)
+        del ws_b8, x8
+    del wmx, h1m, wd8
     # post-DiT tail: the 10 s request's decoded frames (1344x768, 243 frames) to uint8 BTHWC
     fr = W.FRAMES_10S
     frames = torch.rand((fr["B"], 3, fr["T"], fr["H"], fr["W"]), device="cuda") * 2.1 - 1.05
@@ -431,6 +446,21 @@ def main():
         "block_fp8_attention": {"ms": ops["block_fp8_attention"],
                                 "TFLOP/s": total_flop / ops["block_fp8_attention"] / 1e9,
                                 "note": "the same block with attention on the FP8 path"},
+        "block_fp8_projections": {"ms": ops["block_fp8_projections"],
+                                  "TFLOP/s": total_flop / ops["block_fp8_projections"] / 1e9,
+                                  "note": "the same block with the four projections on MX-e4m3 operands"},
+        "block_fp8": {"ms": ops["block_fp8"], "TFLOP/s": total_flop / ops["block_fp8"] / 1e9,
+                      "speedup_vs_bf16": step_ms / ops["block_fp8"],
+                      "note": "FP8 attention and FP8 projections together"},
+        "qkv_gemm_fp8": {"ms": ops["qkv_gemm_fp8"], "TFLOP/s": work["qkv_flop"] / ops["qkv_gemm_fp8"] / 1e9,
+                         "frac_peak": work["qkv_flop"] / ops["qkv_gemm_fp8"] / 1e9 / FP8_PEAK_TFLOPS},
+        "out_gemm_residual_fp8": {"ms": ops["out_gemm_residual_fp8"],
+                                  "TFLOP/s": work["out_flop"] / ops["out_gemm_residual_fp8"] / 1e9},
+        "swiglu_residual_fp8": {"ms": ops["swiglu_residual_fp8"],
+                                "TFLOP/s": (work["w13_flop"] + work["w2_flop"]) / ops["swiglu_residual_fp8"] / 1e9,
+                                "note": "includes quantizing g"},
+        "act_quant": {"ms": ops["act_quant"], "GB/s": wl.n_loc * C * (2 + 1 + 1 / 32) / ops["act_quant"] / 1e6,
+                      "note": "h1 bf16 -> MX e4m3 (one per projection input)"},
         "qkv_gemm": {"ms": ops["qkv_gemm"], "TFLOP/s": work["qkv_flop"] / ops["qkv_gemm"] / 1e9},
         "out_gemm_residual": {"ms": ops["out_gemm_residual"],
                               "TFLOP/s": work["out_flop"] / ops["out_gemm_residual"] / 1e9},

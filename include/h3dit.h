@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 3
+#define H3_ABI_VERSION 4
 
 typedef enum {
   H3_OK = 0,
@@ -276,6 +276,7 @@ typedef struct {
   int32_t norm_kind;  /* 0 LayerNorm, 1 RMSNorm (modulated norms) */
   h3_dtype dtype;
   int32_t attn_fp8;   /* 1: attention through h3_varlen_attn_fp8 (bf16 only); 0: exact path */
+  int32_t gemm_fp8;   /* 1: the four projections on MX operands (bf16 only, weights.mx); 0: bf16 */
 } h3_block_config;
 
 typedef struct {
@@ -286,6 +287,8 @@ typedef struct {
   const void* w2;     /* [C, F] */
   const void* g_q;    /* [D] */
   const void* g_k;    /* [D] */
+  const h3_mx_operand* mx;  /* gemm_fp8: [5] MX copies of w_qkv, w_o, w1, w3, w2
+                               (w1 and w3 with the same ld and ld_scale); else NULL */
 } h3_block_weights;
 
 typedef struct {
@@ -341,6 +344,10 @@ typedef struct {
  * cfg->attn_fp8 == 1 runs the attention step as h3_varlen_attn_fp8 does (MX-scaled
  * e4m3 operands); it needs dtype H3_BF16 (else H3_ERR_ARG), and the workspace size
  * depends on it, so query it with the same cfg.
+ * cfg->gemm_fp8 == 1 runs the four projections as h3_linear_fp8 / h3_swiglu_fp8 do:
+ * each bf16 activation (h1, o, h2, g) is quantized to an MX operand in the workspace
+ * just before its projection, the weights come from w->mx (the bf16 weight pointers
+ * may then be NULL).  Needs dtype H3_BF16 and dim, ffn_dim, H*D multiples of 32.
  */
 size_t h3_dit_block_workspace_size(const h3_block_config* cfg, int64_t n_tok_local,
                                    int64_t n_buf, int32_t n_seg);

@@ -250,7 +250,7 @@ def _mod_rows(mod, rows):
 
 def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
               qkv_attn_fill=None, o_local_fill=None, rows: Optional[np.ndarray] = None,
-              intermediates: bool = False, attention=None):
+              intermediates: bool = False, attention=None, projection=None):
     """One DiT block forward on this GPU's token rows x [n, C].
 
     Steps: h1 = modnorm(x; shift1, scale1) -> qkv = h1 Wqkv^T -> Q/K RMSNorm +
@@ -271,9 +271,12 @@ def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
     rows: return only these local rows (keys/values still use every row).
     attention: the attention step, called as varlen_attention is (default);
     varlen_attention_fp8_operands gives the block with MX-e4m3 attention.
+    projection: the four projections, called as linear is (default);
+    linear_fp8_operands gives the block with MX-e4m3 projections.
     Returns x2 [len(rows), C], or a dict of every intermediate if asked.
     """
     sh = shape
+    proj = linear if projection is None else projection
     x = np.asarray(x)
     n = x.shape[0]
     H, D, C = sh.n_heads, sh.head_dim, sh.dim
@@ -290,10 +293,10 @@ def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
     heads = slice(hb, hb + hc) if share else slice(0, H)
     wk = wq[1, heads].reshape(-1, C)
     wv = wq[2, heads].reshape(-1, C)
-    k_loc = linear(h1, wk).reshape(n, -1, D)
-    v_loc = linear(h1, wv).reshape(n, -1, D)
+    k_loc = proj(h1, wk).reshape(n, -1, D)
+    v_loc = proj(h1, wv).reshape(n, -1, D)
     h1r = h1[out_rows]
-    q_loc = linear(h1r, wq[0, heads].reshape(-1, C)).reshape(len(out_rows), -1, D)
+    q_loc = proj(h1r, wq[0, heads].reshape(-1, C)).reshape(len(out_rows), -1, D)
     pos = np.asarray(pos)
     # norm + RoPE on the local rows (q only on out_rows)
     kq_dummy = np.zeros_like(k_loc)
@@ -316,15 +319,15 @@ def dit_block(x, mod, w, pos, cu_slots, valid_len, shape: BlockShape,
         o[:, hb:hb + hc] = o_h
     else:
         o = o_h
-    y1 = linear(o.reshape(len(out_rows), H * D), w.w_o)
+    y1 = proj(o.reshape(len(out_rows), H * D), w.w_o)
     mod_r = _mod_rows(mod, out_rows)
     xr = _f64(x[out_rows])
     x1 = gated_residual(xr, mod_r[:, GATE1], y1)
     h2 = modulated_norm(x1, mod_r[:, SHIFT2], mod_r[:, SCALE2], sh.eps_mod, sh.norm_kind)
-    a = linear(h2, w.w1)
-    b = linear(h2, w.w3)
+    a = proj(h2, w.w1)
+    b = proj(h2, w.w3)
     g = swiglu_gate(a, b)
-    y2 = linear(g, w.w2)
+    y2 = proj(g, w.w2)
     x2 = gated_residual(x1, mod_r[:, GATE2], y2)
     if not intermediates:
         return x2

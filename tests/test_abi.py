@@ -211,3 +211,45 @@ def test_fp8_projection_argument_checks():
     assert need >= 10 * 704 * 2 + 10 * 768 + 10 * 24
     st = h3._c_sw8(*args(w13, need - 16))
     assert st == h3.H3_ERR_WORKSPACE
+
+
+def _struct_fields(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} " + name + ";", text).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        first, *rest = decl.split(",")
+        names.append(re.findall(r"[A-Za-z_0-9]+", first)[-1])
+        names += [r.strip() for r in rest]
+    return names
+
+
+def test_binding_structs_mirror_the_header():
+    import audio_video_diffusion_block_amd as h3
+    for name, cls in (("h3_block_config", h3.BlockConfig), ("h3_block_weights", h3.BlockWeights),
+                      ("h3_block_io", h3.BlockIO), ("h3_mx_operand", h3.MxOperand)):
+        assert _struct_fields(name) == [f[0] for f in cls._fields_], name
+
+
+def test_block_gemm_fp8_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    import torch
+    w = h3.BlockWeights(*([FAKE] * 7))
+    io = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 480, 0, 0, 4, None, None, None)
+    cfg = h3.block_config(256, 4, 64, 704, (16, 24, 24), gemm_fp8=True)
+    need = h3.block_workspace_size(cfg, 480, 480, 1)
+    assert need > h3.block_workspace_size(h3.block_config(256, 4, 64, 704, (16, 24, 24)), 480, 480, 1)
+    st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), FAKE, need, None)
+    assert st == h3.H3_ERR_ARG and "weights.mx" in h3.last_error()
+    f32 = h3.block_config(256, 4, 64, 704, (16, 24, 24), dtype=torch.float32, gemm_fp8=True)
+    st = h3._c_block(ctypes.byref(f32), ctypes.byref(w), ctypes.byref(io), FAKE, 1 << 30, None)
+    assert st == h3.H3_ERR_ARG and "bf16" in h3.last_error()
+    mx = (h3.MxOperand * 5)(h3.MxOperand(FAKE, 256, FAKE, 8), h3.MxOperand(FAKE, 256, FAKE, 8),
+                            h3.MxOperand(FAKE, 256, FAKE, 8), h3.MxOperand(FAKE, 384, FAKE, 12),
+                            h3.MxOperand(FAKE, 768, FAKE, 24))
+    w.mx = ctypes.cast(mx, ctypes.POINTER(h3.MxOperand))
+    st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), FAKE, need, None)
+    assert st == h3.H3_ERR_ARG and "share" in h3.last_error()  # w1 / w3 strides differ

@@ -14,17 +14,22 @@ def weights_dev(w, dtype):
     return {k: dev(getattr(w, k), dtype) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")}
 
 
-def cfg_of(lib, wl, dtype, attn_fp8=False):
+def cfg_of(lib, wl, dtype, attn_fp8=False, gemm_fp8=False):
     return lib.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
-                            wl.eps_qk, wl.eps_mod, 0, TORCH_DT[dtype], attn_fp8=attn_fp8)
+                            wl.eps_qk, wl.eps_mod, 0, TORCH_DT[dtype], attn_fp8=attn_fp8,
+                            gemm_fp8=gemm_fp8)
 
 
 def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=False,
-              attn_fp8=False):
+              attn_fp8=False, gemm_fp8=False):
     x = dev(bi.x if x_override is None else x_override, dtype)
     mod = dev(bi.mod if mod_override is None else mod_override, dtype)
     extra = share_buffers(wl, bi, dtype, peer) if wl.share_mode else {}
-    lib.h3_dit_block_forward(cfg_of(lib, wl, dtype, attn_fp8), weights_dev(w, dtype), x, mod,
+    wd = weights_dev(w, dtype)
+    if gemm_fp8:
+        # only the MX copies and the gains reach the block
+        wd = {"mx": lib.block_weights_mx(wd), "g_q": wd["g_q"], "g_k": wd["g_k"]}
+    lib.h3_dit_block_forward(cfg_of(lib, wl, dtype, attn_fp8, gemm_fp8), wd, x, mod,
                              dev_i32(bi.pos),
                              dev_i32(bi.cu_slots), dev_i32(bi.valid_len), int(bi.valid_len.max()),
                              **extra)
@@ -32,11 +37,11 @@ def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=Fa
     return host(x)
 
 
-def oracle_block(wl, w, bi, rows=None, x=None, mod=None, attention=None):
+def oracle_block(wl, w, bi, rows=None, x=None, mod=None, attention=None, projection=None):
     return O.dit_block(bi.x if x is None else x, bi.mod if mod is None else mod, w, bi.pos,
                        bi.cu_slots, bi.valid_len, O.BlockShape.of(wl), bi.qkv_attn,
                        None if bi.o_local is None else bi.o_local, rows=rows,
-                       attention=attention)
+                       attention=attention, projection=projection)
 
 
 def check_block(got, ref, x_in, dtype, what, update=None):
@@ -173,3 +178,42 @@ def test_block_fp8_attention(lib, case):
     exact_path = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod,
                            peer=case.startswith("peer"))
     assert not np.array_equal(got, exact_path)  # the FP8 path really ran
+
+
+@pytest.mark.parametrize("case", ["world1", "share_r2", "peer_r3", "peer_r0_attn_fp8"])
+def test_block_fp8_projections(lib, case):
+    """Block with the four projections on MX-e4m3 operands (and, in one case, the
+    FP8 attention too), update-dominant inputs.
+
+    The activations the kernel quantizes (h1, o, h2, g) are bf16 values that
+    carry the block's earlier bf16 roundings, while the oracle quantizes its
+    float64 ones; a value within 2^-9 of an e4m3 rounding midpoint (a few
+    percent of them) lands on the other e4m3 neighbour, a 2^-3 relative step.
+    On these inputs, rounding only the oracle's activations to bf16 before
+    quantizing moves the update by 6.5% (world 1) and 4.7% (rank share)
+    relative L2, and the quantized-operand oracle is 9.3% / 7.5% from the
+    exact one (10.1% / 8.1% with FP8 attention as well).  Bounds: update
+    relative L2 < 12% against the quantized-operand oracle, < 15% against the
+    exact oracle -- a wiring mistake (wrong weight, buffer or layout) moves it
+    by O(100%)."""
+    rank = {"world1": None, "share_r2": 2, "peer_r3": 3, "peer_r0_attn_fp8": 0}[case]
+    wl = W.TINY if rank is None else W.TINY.replace(sp_degree=4, rank=rank)
+    w = W.block_weights(wl, 4, "bf16")
+    bi = W.block_inputs(wl, 4, "bf16")
+    x, mod = _update_dominant(bi)
+    peer = case.startswith("peer")
+    attn8 = case.endswith("attn_fp8")
+    got = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
+                    attn_fp8=attn8, gemm_fp8=True)
+    assert np.all(np.isfinite(got))
+    ref_q = oracle_block(wl, w, bi, x=x, mod=mod, projection=O.linear_fp8_operands,
+                         attention=O.varlen_attention_fp8_operands if attn8 else None)
+    ref = oracle_block(wl, w, bi, x=x, mod=mod)
+    upd = np.linalg.norm(ref - x)
+    rel_q = np.linalg.norm(got - ref_q) / upd
+    rel_x = np.linalg.norm(got - ref) / upd
+    print(f"[block fp8 projections {case}] vs quantized-operand oracle {rel_q:.3g}, vs exact {rel_x:.3g}")
+    assert rel_q < 0.12 and rel_x < 0.15, (rel_q, rel_x)
+    bf16_path = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
+                          attn_fp8=attn8)
+    assert not np.array_equal(got, bf16_path)  # the FP8 projections really ran
