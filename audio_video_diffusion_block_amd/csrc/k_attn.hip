@@ -852,9 +852,9 @@ __global__ __launch_bounds__(256) void transpose_quant_v_kernel(const bf16_t* __
 }
 
 
-// FP8 flash attention.  Same work split, phase rotation and 4-stage LDS ring
-// as the bf16 kernel; per 64-key tile a wave runs 2*(D/64) MFMAs for S and
-// D/32 for P.V, each 64 deep.
+// FP8 flash attention.  Same work split and phase rotation as the bf16
+// kernel; per 64-key tile a wave runs 2*(D/64) MFMAs for S and D/32 for P.V,
+// each 64 deep.
 //  * Scores: S^T = K Q^T with K rows read in the order sigma8 below, so the
 //    accumulator register r of lane half h in key block kb holds key
 //    32 kb + 16 h + r -- exactly the byte (16 kb + r) the P.V MFMA expects in
@@ -866,8 +866,14 @@ __global__ __launch_bounds__(256) void transpose_quant_v_kernel(const bf16_t* __
 //    scale byte 127.  The row sums come from the matrix pipe: one more P.V
 //    MFMA whose A operand is all e4m3 ones sums the stored weights of every
 //    query, so numerator and denominator see the same rounded 256 p.
-//  * LDS rows are padded (K: D + 16 bytes, V^T: 64 + 16) so each 16-lane
-//    group of a 16-byte fragment read covers 16 distinct bank groups.
+//  * Tiles go from global memory straight into LDS (global_load_lds_dwordx4:
+//    no staging registers, no LDS stores), into a 5-stage ring: tile t + 4 is
+//    requested right after the barrier of step t and has two steps to land.
+//    Rows past the valid keys are clamped to the last valid row (their scores
+//    are masked).
+//  * LDS rows are unpadded; 16-byte chunk c of a row r sits at slot
+//    c ^ swz(r), chosen so that the 16 rows one 16-lane group of a fragment
+//    read touches (for K, in the sigma8 order) fall on 16 distinct bank groups.
 namespace {
 // K row read into A-operand row rho of a 32-key block
 __device__ __forceinline__ int sigma8(int rho) {
@@ -895,14 +901,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   constexpr int NT = D / 64;          // 64-deep steps of S (1 or 2)
   static_assert(NT == 1 || NT == 2, "head_dim 64 or 128");
   constexpr int NB = D / 32;          // 32-element scale blocks of a head row
-  constexpr int KSTR = D + 16;        // K tile row stride (bytes)
-  constexpr int VSTR = KT + 16;       // V^T tile row stride (bytes)
-  constexpr int K_OFF = 0;
-  constexpr int V_OFF = KT * KSTR;
-  constexpr int KS_OFF = V_OFF + D * VSTR;  // K scales [KT][NB]
+  constexpr int K_OFF = 0;                  // K [KT][D] bytes, swizzled rows
+  constexpr int V_OFF = KT * D;             // V^T [D][KT] bytes, swizzled rows
+  constexpr int KS_OFF = V_OFF + D * KT;    // K scales [KT][NB]
   constexpr int VS_OFF = KS_OFF + KT * NB;  // V^T scales [2][D]
-  constexpr int STAGE = (VS_OFF + 2 * D + 15) / 16 * 16;
-  constexpr int NSTAGE = 4;
+  constexpr int STAGE = VS_OFF + 2 * D;
+  static_assert(STAGE % 16 == 0 && KT == 64, "stage layout");
+  constexpr int NSTAGE = 5;
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE];
 
   const int s = blockIdx.y;
@@ -939,62 +944,83 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     }
   }
 
-  // ---- tile loads: global -> registers -> LDS (one 16-byte chunk per thread
-  // of K and of V^T; 32 threads carry the two scale strips)
-  constexpr int KCH = KT * D / 16;   // 16-byte chunks of a K tile
-  constexpr int VCH = D * KT / 16;   // of a V^T tile
-  static_assert(KCH <= NTH && VCH <= NTH, "one chunk per thread");
+  // ---- tile loads: global -> LDS directly.  Per tile, K takes D/16 1-KB
+  // instructions (waves 0 ..), V^T D/16 (the last waves), the K scales (2 D
+  // bytes) part of one more on wave 0 and the V^T scales on wave NW - 1.
+  // The DMA instructions are inline assembly: the compiler would otherwise
+  // count them as pending LDS operations and make fragment reads wait on them;
+  // their completion is tracked with explicit vmcnt waits before barriers.
+  constexpr int KI = D / 16;                         // K instructions per tile
+  constexpr int VI = D / 16;                         // V^T instructions per tile
+  static_assert(KI <= NW && VI <= NW, "one instruction per wave");
   const char* kbase = reinterpret_cast<const char*>(k8 + ((int64_t)head * n_buf + seg_lo) * D);
   const char* ksb = reinterpret_cast<const char*>(ks + ((int64_t)head * n_buf + seg_lo) * NB);
   const int64_t vbase_col = vt_segment_base(seg_lo, s);
   const char* vbase = reinterpret_cast<const char*>(vt8 + (int64_t)head * D * vt_cols + vbase_col);
   const char* vsb = reinterpret_cast<const char*>(vts + ((int64_t)head * (vt_cols / 32) + vbase_col / 32) * D);
-  const int v_bytes = (int)(D * vt_cols);
-  const int k_r = tid / (D / 16), k_c = tid % (D / 16);
-  const int v_r = tid / (KT / 16), v_c = tid % (KT / 16);
-  uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0), rs = make_uint4(0, 0, 0, 0);
-  auto load_tile = [&](int jt) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // swizzles (slot of chunk c in row r is c ^ swz(r)); see the bank argument above
+  auto kswz = [](int r) { return D == 128 ? (((r >> 1) + 4 * (r >> 4)) & 7) : (((r >> 2) ^ (r >> 3)) & 3); };
+  auto vswz = [](int r) { return ((r >> 2) ^ (r >> 3)) & 3; };
+  constexpr int KCPR = D / 16;                       // 16-byte chunks per K row
+  constexpr int KRPI = 1024 / D;                     // K rows per instruction
+  const int k_dma_row = wv * KRPI + lane / KCPR;     // used by waves wv < KI
+  const int k_dma_chunk = (lane % KCPR) ^ kswz(k_dma_row);
+  const int v_dma_row = (wv - (NW - VI)) * 16 + lane / 4;   // used by waves wv >= NW - VI
+  const int v_dma_off = v_dma_row * (int)vt_cols + ((lane % 4) ^ vswz(v_dma_row)) * 16;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+  auto dma16 = [&](const char* base, int voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds_addr) : "memory", "m0");
+  };
+  // DMA instructions this wave issues per tile (every wave runs every tile)
+  const int n_dma = (wv < KI) + (wv >= NW - VI) + (wv == 0) + (wv == NW - 1);
+  auto issue_tile = [&](int jt) {
     const int j0 = jt * KT;
     const int nk = min(len - j0, KT);
-    if (tid < KCH)
-      rk = buf_load16(make_rsrc(kbase + (int64_t)j0 * D, nk * D), (k_r * D) + k_c * 16);
-    if (tid < VCH)
-      rv = buf_load16(make_rsrc(vbase + j0, v_bytes), v_r * (int)vt_cols + v_c * 16);
-    if (tid < 16) {
-      // K scales of the tile's rows: KT * NB bytes.  The range is rounded up to
-      // whole 16-byte chunks: the buffer range check zeroes a partly valid
-      // dword, which would drop the last valid key's scale when NB = 2.  Rows
-      // past the valid keys carry zero K data, so their scales are harmless.
-      rs = buf_load16(make_rsrc(ksb + (int64_t)j0 * NB, (nk * NB + 15) & ~15), tid * 16);
-    } else if (tid < 32) {
-      // V^T scales of the tile's two key blocks: 2 * D bytes
-      rs = buf_load16(make_rsrc(vsb + (int64_t)(j0 / 32) * D, 2 * D), (tid - 16) * 16);
-    }
+    const uint32_t st = lds0 + (jt % NSTAGE) * STAGE;
+    if (wv < KI)
+      dma16(kbase + (int64_t)j0 * D, min(k_dma_row, nk - 1) * D + k_dma_chunk * 16,
+            st + K_OFF + wv * 1024);
+    if (wv >= NW - VI)
+      dma16(vbase + j0, v_dma_off, st + V_OFF + (wv - (NW - VI)) * 1024);
+    // scales: 16-byte chunks wholly past the valid rows are skipped (the stale
+    // LDS scales they would have replaced belong to masked keys)
+    if (wv == 0 && lane < 2 * D / 16 && lane * 16 < nk * NB)
+      dma16(ksb + (int64_t)j0 * NB, lane * 16, st + KS_OFF);
+    if (wv == NW - 1 && lane < 2 * D / 16)
+      dma16(vsb + (int64_t)(j0 / 32) * D, lane * 16, st + VS_OFF);
   };
-  auto store_tile = [&](int stage) {
-    uint8_t* st = smem + stage * STAGE;
-    if (tid < KCH) *reinterpret_cast<uint4*>(st + K_OFF + k_r * KSTR + k_c * 16) = rk;
-    if (tid < VCH) *reinterpret_cast<uint4*>(st + V_OFF + v_r * VSTR + v_c * 16) = rv;
-    if (tid < 16) {
-      if (tid * 16 < KT * NB) *reinterpret_cast<uint4*>(st + KS_OFF + tid * 16) = rs;
-    } else if (tid < 32) {
-      if ((tid - 16) * 16 < 2 * D) *reinterpret_cast<uint4*>(st + VS_OFF + (tid - 16) * 16) = rs;
-    }
+  // wait until at most `tiles` tiles of this wave's DMA are still in flight
+  auto wait_dma = [&](int tiles) {
+    const int n = tiles * n_dma;
+    if (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   };
 
   // ---- fragment addressing
   const int k_row = sigma8(qi);
+  int k_slot[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) k_slot[t][p] = ((4 * t + 2 * p + hf) ^ kswz(k_row)) * 16;
+  const int v_slot0 = (hf ^ vswz(qi)) * 16, v_slot1 = ((2 + hf) ^ vswz(qi)) * 16;
   auto kfrag = [&](const uint8_t* st, int kb, int t) {
-    const uint8_t* p = st + K_OFF + (kb * 32 + k_row) * KSTR + 64 * t + 16 * hf;
-    return frag32(p, p + 32);
+    const uint8_t* p = st + K_OFF + (kb * 32 + k_row) * D;
+    return frag32(p + k_slot[t][0], p + k_slot[t][1]);
   };
   auto kscale = [&](const uint8_t* st, int kb) {
     const uint8_t* p = st + KS_OFF + (kb * 32 + k_row) * NB + hf * (NB / 2);
     return NB / 2 == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p) : (uint32_t)*p;
   };
   auto vfrag = [&](const uint8_t* st, int db) {
-    const uint8_t* p = st + V_OFF + (db * 32 + qi) * VSTR + 16 * hf;
-    return frag32(p, p + 32);
+    const uint8_t* p = st + V_OFF + (db * 32 + qi) * KT;
+    return frag32(p + v_slot0, p + v_slot1);
   };
   auto vscale = [&](const uint8_t* st, int db) {
     return (uint32_t)st[VS_OFF + hf * D + db * 32 + qi];
@@ -1131,12 +1157,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     if (jt + 1 < n_tiles) update_max(mx, nxt);
   };
 
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) {
-    load_tile(1);
-    store_tile(1);
-  }
+  // tiles 0 .. 3 in flight; 0 and 1 must land before the first step
+  for (int t = 0; t < 4 && t < n_tiles; ++t) issue_tile(t);
+  wait_dma(n_tiles > 3 ? 2 : (n_tiles > 2 ? 1 : 0));
   __syncthreads();
   f32x16_t sa[2], sb[2];
   compute_s(0, sa);
@@ -1158,16 +1181,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       negm[r] = -m_ref;
     }
   }
-  if (n_tiles > 2) load_tile(2);
 
-  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
+  // During step jt the ring holds tiles jt-1 (V, second half), jt (V, first
+  // half) and jt+1 (K, both halves); jt+2 and jt+3 are in flight.  Tile jt+2
+  // is waited for before the barrier that ends the step, and tile jt+4 goes
+  // into the stage of tile jt-1 right after it.
+  const bool lag = wv >= NW / 2;
   auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     if (lag && jt > 0) phase_b((jt - 1) % NSTAGE, cur, jt - 1);
     phase_a((jt + 1) % NSTAGE, nxt, cur, jt);
     if (!lag) phase_b(jt % NSTAGE, nxt, jt);
-    if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
+    wait_dma(jt + 3 < n_tiles ? 1 : 0);
     __syncthreads();
-    if (jt + 3 < n_tiles) load_tile(jt + 3);
+    if (jt + 4 < n_tiles) issue_tile(jt + 4);
   };
   for (int jt = 0; jt < n_tiles; jt += 2) {
     step(jt, sa, sb);
