@@ -244,6 +244,26 @@ def run_loop_bench(args, h3, torch, W):
     loop_ms = timer.time(lambda: loop(record=True), steps)
     wall = (time.perf_counter() - t_start) * 1e3 / steps
     per_fwd = [a.elapsed_time(b) for a, b in fwd_ms]
+    # the same loop with FP8 attention and FP8 projections (MX weights quantized once, untimed)
+    cfg8 = h3.block_config(C, H, D, wl.ffn_dim, wl.sections, wl.theta, wl.eps_qk, wl.eps_mod, 0, bf,
+                           attn_fp8=True, gemm_fp8=True)
+    ws8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, wl.n_pad_total, 1), dtype=torch.uint8,
+                      device="cuda")
+    blocks8 = [{"mx": h3.block_weights_mx(bw), "g_q": bw["g_q"], "g_k": bw["g_k"]} for bw in blocks]
+
+    def loop8():
+        z.copy_(z0)
+        x.copy_(z0)
+        for k in range(len(sig) - 1):
+            h3.h3_timestep_modulation(sig[k], t1, t2, tab, mods, ws=tws)
+            for b in range(wl.n_blocks):
+                h3.h3_dit_block_forward(cfg8, blocks8[b], x, mods[b:b + 1], pos, cu, vl, max_len, ws=ws8, **share)
+            h3.h3_euler_update(z, x, x, sig[k], sig[k + 1])
+
+    loop8()
+    torch.cuda.synchronize()
+    loop8_ms = timer.time(loop8, steps)
+    del blocks8, ws8
     work = algorithmic_work(wl)
     blk_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
     total_flop = blk_flop * wl.n_blocks * (len(sig) - 1)
@@ -259,6 +279,8 @@ def run_loop_bench(args, h3, torch, W):
                    "blocks": wl.n_blocks, "forwards": len(sig) - 1, "parallelism": "1 GPU (rank-share stand-in)"},
         "loop_ms": loop_ms, "wall_ms": wall, "ms_per_forward": per_fwd[-(len(sig) - 1):],
         "ms_per_block": loop_ms / (wl.n_blocks * (len(sig) - 1)),
+        "fp8_loop_ms": loop8_ms, "fp8_speedup": loop_ms / loop8_ms,
+        "fp8_note": "the same loop with FP8 attention and FP8 projections (MX e4m3 operands)",
     }
     print(json.dumps(out))
 
