@@ -546,3 +546,51 @@ def linear_fp8_operands(x, w) -> np.ndarray:
     xd = mx_dequantize(*mx_quantize(x))
     wd = mx_dequantize(*mx_quantize(w))
     return xd @ wd.T
+
+
+# ------------------------------------------------------------ Skip-Softmax
+
+# [FH3-zh] 超出 FastH3 配置的扩展能力 (sparse and quantized attention):
+# Skip-Softmax is named among the attention variants that speed up the base
+# pipeline at small quality cost; the pages give no rule.  Reading: keys are
+# visited in blocks of 64 from the segment start and queries in groups of 32
+# consecutive valid rows from the segment start; a key block is skipped for a
+# query group -- its probabilities are taken as zero -- when, for every row of
+# the group, the block's largest score is more than |t| below the row's
+# running maximum over the blocks visited before it (scores in log2 units,
+# i.e. q.k * scale * log2 e; t < 0).  The first block is never skipped.  A
+# skipped key's weight is at most 2^t times the row's largest weight.
+
+def varlen_attention_skip(q, k, v, cu_slots, valid_len, skip_log2: float,
+                          scale: Optional[float] = None, q_group: int = 32,
+                          k_block: int = 64) -> np.ndarray:
+    """Attention with the Skip-Softmax rule above; q, k, v [n_buf, H, D].
+    Returns [n_buf, H, D] (rows outside every segment are 0) and applies the
+    rule exactly in float64: a block is skipped or kept whole."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n_buf, h, d = k.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    c = scale * np.log2(np.e)
+    out = np.zeros((n_buf, h, d))
+    cu = np.asarray(cu_slots)
+    vl = np.asarray(valid_len) if valid_len is not None else np.diff(cu)
+    for s in range(len(cu) - 1):
+        lo, n = int(cu[s]), int(vl[s])
+        for head in range(h):
+            sc = (q[lo:lo + n, head] @ k[lo:lo + n, head].T) * c   # log2 units
+            for g0 in range(0, n, q_group):
+                rows = slice(g0, min(g0 + q_group, n))
+                keep = np.zeros(n, dtype=bool)
+                m_run = None
+                for b0 in range(0, n, k_block):
+                    blk = slice(b0, min(b0 + k_block, n))
+                    bmax = sc[rows, blk].max(axis=1)
+                    if m_run is not None and np.all(bmax < m_run + skip_log2):
+                        continue
+                    keep[blk] = True
+                    m_run = bmax if m_run is None else np.maximum(m_run, bmax)
+                ss = sc[rows][:, keep]
+                p = np.exp2(ss - ss.max(axis=1, keepdims=True))
+                out[lo + g0:lo + min(g0 + q_group, n), head] = (p @ v[lo:lo + n, head][keep]) / p.sum(axis=1, keepdims=True)
+    return out

@@ -783,3 +783,56 @@ def test_fp8_linear_error_bound_and_zero_padding():
     np.testing.assert_array_equal(O.linear_fp8_operands(xp, wp), got)
     # each row of x is quantized on its own: the result for a row does not depend on the others
     np.testing.assert_array_equal(O.linear_fp8_operands(x[3:4], w), got[3:4])
+
+
+# ------------------------------------------------------------ Skip-Softmax
+
+def _blocky_case(n=320, h=1, d=64, far=(1, 3), seed=7):
+    """Every query is 4 e0 + N(0, 0.3^2) noise; keys are N(0, 1) except in the
+    64-key blocks listed in `far`, whose keys are -55 e0 + N(0, 1): their scores
+    sit near -40 (log2 units, scale 1/8) while the others are O(1), so with
+    t = -10 exactly the far blocks fall below the threshold."""
+    g = np.random.default_rng(seed)
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    q = 4.0 * e0 + 0.3 * g.standard_normal((n, h, d))
+    k = g.standard_normal((n, h, d))
+    v = g.standard_normal((n, h, d))
+    for b in far:
+        k[b * 64:(b + 1) * 64] -= 55.0 * e0
+    return q, k, v
+
+
+def test_skip_softmax_reduces_to_exact_and_to_kept_blocks():
+    q, k, v = _blocky_case()
+    n = q.shape[0]
+    cu, vl = np.array([0, n]), np.array([n])
+    exact = O.varlen_attention(q, k, v, cu, vl)
+    # no threshold to cross: identical to exact attention
+    np.testing.assert_allclose(O.varlen_attention_skip(q, k, v, cu, vl, -1e9), exact, rtol=0, atol=1e-12)
+    # t = -10: the far blocks are skipped, so each row is exact attention over the kept keys
+    got = O.varlen_attention_skip(q, k, v, cu, vl, -10.0)
+    keep = np.ones(n, bool)
+    keep[64:128] = keep[192:256] = False
+    scale = 1 / np.sqrt(q.shape[-1])
+    want = np.stack([O.attention_dense(q[:, 0], k[keep, 0], v[keep, 0], scale)], axis=1)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # the skipped weight is tiny: the result stays within 2^-10 * 128 * max|v| of exact
+    assert np.abs(got - exact).max() <= 2.0 ** -10 * 128 * np.abs(v).max()
+    assert np.abs(got - exact).max() > 0
+
+
+def test_skip_softmax_first_block_and_group_rule():
+    """The first block is always kept, and one row of a group that still needs a
+    block keeps it for the whole group."""
+    q, k, v = _blocky_case(far=(0,))
+    n = q.shape[0]
+    cu, vl = np.array([0, n]), np.array([n])
+    got = O.varlen_attention_skip(q, k, v, cu, vl, -10.0)
+    np.testing.assert_allclose(got, O.varlen_attention(q, k, v, cu, vl), rtol=1e-10, atol=1e-12)
+    q2, k2, v2 = _blocky_case(far=(2,))
+    q2[5] = -q2[5]          # row 5 of group 0 now prefers block 2
+    got2 = O.varlen_attention_skip(q2, k2, v2, cu, vl, -10.0)
+    exact2 = O.varlen_attention(q2, k2, v2, cu, vl)
+    np.testing.assert_allclose(got2[:32], exact2[:32], rtol=1e-10, atol=1e-12)   # group 0 keeps block 2
+    assert np.abs(got2[32:64] - exact2[32:64]).max() > 0                     # group 1 skips it
