@@ -47,7 +47,7 @@ class BlockConfig(ctypes.Structure):
     _fields_ = [("dim", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn_dim", _i32),
                 ("sec_t", _i32), ("sec_h", _i32), ("sec_w", _i32), ("theta", _f),
                 ("eps_qk", _f), ("eps_mod", _f), ("norm_kind", _i32), ("dtype", _i32),
-                ("attn_fp8", _i32), ("gemm_fp8", _i32)]
+                ("attn_fp8", _i32), ("gemm_fp8", _i32), ("attn_skip_log2", _f)]
 
 
 class MxOperand(ctypes.Structure):
@@ -75,6 +75,11 @@ def _sig(name, res, args):
 
 
 _lib.h3_abi_version.restype = ctypes.c_int
+# the ctypes structures below mirror this version of include/h3dit.h
+ABI_VERSION = 5
+if _lib.h3_abi_version() != ABI_VERSION:
+    raise ImportError(f"{LIB_PATH} has ABI version {_lib.h3_abi_version()}, the binding "
+                      f"expects {ABI_VERSION}: rebuild it")
 _lib.h3_status_string.restype = ctypes.c_char_p
 _lib.h3_status_string.argtypes = [ctypes.c_int]
 _lib.h3_last_error.restype = ctypes.c_char_p
@@ -107,6 +112,9 @@ _c_attn8 = _sig("h3_varlen_attn_fp8", ctypes.c_int,
                 [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _f,
                  _p, _sz, _i32, _p])
 
+_c_attn_skip = _sig("h3_varlen_attn_skip", ctypes.c_int,
+                    [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32,
+                     _f, _f, _p, _sz, _i32, _p])
 _c_mxq = _sig("h3_mx_quantize", ctypes.c_int,
               [_p, _i64, _i64, _i32, _p, _i64, _p, _i64, _i32, _p])
 _c_lin8 = _sig("h3_linear_fp8", ctypes.c_int,
@@ -122,7 +130,7 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
-            "h3_swiglu_fp8")
+            "h3_swiglu_fp8", "h3_varlen_attn_skip")
 
 
 def _status_string(st: int) -> str:
@@ -206,6 +214,22 @@ def h3_varlen_attn(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tens
                    n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
                    softmax_scale, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
                    _stream(stream)))
+
+
+def h3_varlen_attn_skip(q, k, v, o, n_heads: int, head_dim: int, cu_slots, valid_len,
+                        max_valid_len: int, skip_log2: float, softmax_scale: float = 0.0,
+                        ws: Optional[torch.Tensor] = None, stream=None):
+    """bf16 attention with Skip-Softmax: key blocks of 64 whose scores are all
+    more than |skip_log2| (log2 units) below a query group's running max are
+    skipped (workspace as h3_varlen_attn)."""
+    n_buf = q.shape[0]
+    n_seg = cu_slots.shape[0] - 1
+    if ws is None:
+        ws = _bytes_ws(varlen_attn_workspace_size(n_buf, n_heads, head_dim, n_seg, q.dtype), q.device)
+    _check(_c_attn_skip(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
+                        n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
+                        softmax_scale, skip_log2, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
+                        _stream(stream)))
 
 
 def varlen_attn_fp8_workspace_size(n_buf: int, n_heads: int, head_dim: int, n_seg: int) -> int:
@@ -321,11 +345,11 @@ def h3_swiglu_fp8(h: MxTensor, w1: MxTensor, w3: MxTensor, w2: MxTensor, out, ga
 
 def block_config(dim, n_heads, head_dim, ffn_dim, sections, theta=1e4, eps_qk=1e-6,
                  eps_mod=1e-6, norm_kind=0, dtype=torch.bfloat16,
-                 attn_fp8=False, gemm_fp8=False) -> BlockConfig:
+                 attn_fp8=False, gemm_fp8=False, attn_skip_log2=0.0) -> BlockConfig:
     return BlockConfig(dim, n_heads, head_dim, ffn_dim, sections[0], sections[1], sections[2],
                        theta, eps_qk, eps_mod, norm_kind,
                        H3_BF16 if dtype == torch.bfloat16 else H3_F32, int(bool(attn_fp8)),
-                       int(bool(gemm_fp8)))
+                       int(bool(gemm_fp8)), attn_skip_log2)
 
 
 def block_weights_mx(weights: dict, stream=None) -> list:

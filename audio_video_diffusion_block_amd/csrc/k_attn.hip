@@ -351,11 +351,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
 // LDS ring with one barrier per tile.  8 waves (256 query rows) share each K/V
 // tile; the row sums use v_dot2_f32_bf16 on the packed bf16 P (the values the
 // MFMA multiplies).
-template <int D, int NW>
+// SKIP (Skip-Softmax): a wave gives a key tile exactly zero weight and leaves
+// out its P.V when, for each of its valid query rows, the tile's largest score
+// is more than |skip_log2| (log2 units) below the row's exact running max over
+// the tiles before it.  The decision for tile j+1 is taken once its scores are
+// known (the row max of phase B) and is uniform over the wave.
+template <int D, int NW, bool SKIP = false>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ q, int64_t ld_q, const bf16_t* __restrict__ k, int64_t ld_k,
     const bf16_t* __restrict__ vt, int64_t vt_cols, bf16_t* __restrict__ o, int64_t ld_o,
-    const int* __restrict__ cu, const int* __restrict__ valid, float scale_log2) {
+    const int* __restrict__ cu, const int* __restrict__ valid, float scale_log2,
+    float skip_log2 = 0.f) {
   constexpr int BMQ = NW * 32;
   constexpr int NTH = NW * 64;
   constexpr int KCH = D / 8;
@@ -454,6 +460,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY;
+  float m_true = -INFINITY;  // SKIP: exact running max (log2 units)
   float l_a = 0.f, l_b = 0.f;
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
   const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   };
   // raise the running max to the tile max if it exceeds it by more than 8
   // (log2 units) and rescale O and l; skipped on most tiles
-  auto update_max = [&](float mx) {
+  auto update_max = [&](float mx) -> float {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
@@ -494,6 +501,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    return mx_s;
+  };
+  // SKIP: whether the tile whose row max is mx_s (log2 units) is skipped; the
+  // running max then takes it in
+  auto skip_decision = [&](float mx_s) -> bool {
+    const bool row_skips = !q_ok || mx_s < m_true + skip_log2;
+    const bool skip = __all(row_skips);
+    m_true = fmaxf(m_true, mx_s);
+    return skip;
   };
 
   // A tile step is two phases, hand-ordered so that each keeps both pipes fed:
@@ -507,7 +523,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   bf16x8_t vf[4];
   constexpr int NA = 2 * (D / 16);  // phase A MFMAs: 2 key blocks x D/16 k-steps
   constexpr int NB = 4 * (D / 32);  // phase B MFMAs: 4 key groups x D/32 d blocks
-  auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2], int jt) {
+  // SKIP: the softmax of a skipped tile runs with +inf in place of the
+  // running max, so its weights are exactly 0 and its row sums unchanged
+  // (branch-free: a branch per slot costs more than the VALU work it saves)
+  auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2], int jt,
+                     bool skip) {
+    const float m_sub = (SKIP && skip) ? INFINITY : m_run;
     const bf16_t* sk = smem + stage_k * STAGE;
     // the wave in this (VALU-heavy) phase wins issue arbitration against the
     // other wave of its SIMD, whose P.V MFMAs then fill the matrix pipe
@@ -535,8 +556,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       for (int sl = 0; sl < SL; ++sl) {
         const int slice = i * SL + sl;
         const int g = slice >> 2, t = slice & 3, kb = g >> 1, half = g & 1;
-        pe[i & 1][sl][0] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t], scale_log2, -m_run));
-        pe[i & 1][sl][1] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t + 1], scale_log2, -m_run));
+        pe[i & 1][sl][0] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t], scale_log2, -m_sub));
+        pe[i & 1][sl][1] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t + 1], scale_log2, -m_sub));
       }
       if (i > 0) {
 #pragma unroll
@@ -563,8 +584,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     __builtin_amdgcn_s_setprio(0);
     if (jt + 1 < n_tiles && (jt + 2) * KT > len) mask_tile(nxt, jt + 1);
   };
-  // nxt holds S(jt+1), written by phase A of tile jt
-  auto phase_b = [&](int stage_v, f32x16_t (&nxt)[2], int jt) {
+  // nxt holds S(jt+1), written by phase A of tile jt.  SKIP: a skipped tile's
+  // P.V MFMAs are left out; returns whether tile jt+1 is skipped.
+  auto phase_b = [&](int stage_v, f32x16_t (&nxt)[2], int jt, bool skip) -> bool {
     const bf16_t* sv = smem + stage_v * STAGE;
     constexpr int MX = 32 / NB;       // scores folded into the max per phase-B MFMA
     // Slot i: one P.V MFMA and the row-max step of score pair group i-2 (the
@@ -575,7 +597,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       if (i < NB) {
         const int g = i / (D / 32), db = i % (D / 32);
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[g][0], w[g][1], w[g][2], w[g][3]));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, oacc[db], 0, 0, 0);
+        if (!(SKIP && skip))
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pb, oacc[db], 0, 0, 0);
         if (i + 4 < NB) vf[i & 3] = vfrag(sv, (i + 4) / (D / 32), (i + 4) % (D / 32));
       }
       if (i >= 2) {
@@ -587,7 +610,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (jt + 1 < n_tiles) update_max(mx);
+    if (jt + 1 < n_tiles) {
+      const float mx_s = update_max(mx);
+      if constexpr (SKIP) return skip_decision(mx_s);
+    }
+    return false;
   };
 
   load_tile(0);
@@ -606,7 +633,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
-    update_max(mx);
+    m_true = update_max(mx);  // the first tile is never skipped
   }
   if (n_tiles > 2) load_tile(2);
 
@@ -620,10 +647,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   // the previous step, goes to the fourth stage, and tile jt+3 is loaded.
   // After the last tile, S(next) reads a stale stage and is discarded.
   const bool lag = __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
+  // SKIP flags: sk_cur for the tile whose softmax runs in this step, sk_prev
+  // for the lagging half's P.V of the tile before it
+  bool sk_cur = false, sk_prev = false;
   auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
-    if (lag && jt > 0) phase_b((jt - 1) % NSTAGE, cur, jt - 1);
-    phase_a((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt);
-    if (!lag) phase_b(jt % NSTAGE, nxt, jt);
+    if (lag && jt > 0) {
+      sk_prev = sk_cur;
+      sk_cur = phase_b((jt - 1) % NSTAGE, cur, jt - 1, sk_prev);
+    }
+    phase_a((jt + 1) % NSTAGE, nxt, jt % NSTAGE, cur, jt, sk_cur);
+    if (!lag) sk_cur = phase_b(jt % NSTAGE, nxt, jt, sk_cur);
     if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
     __syncthreads();
     if (jt + 3 < n_tiles) load_tile(jt + 3);
@@ -635,8 +668,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   }
   if (lag) {
     // S(n_tiles) sits in sb when n_tiles is odd, else in sa (unused: no max update)
-    if (n_tiles & 1) phase_b((n_tiles - 1) % NSTAGE, sb, n_tiles - 1);
-    else phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1);
+    if (n_tiles & 1) phase_b((n_tiles - 1) % NSTAGE, sb, n_tiles - 1, sk_cur);
+    else phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1, sk_cur);
   }
 
   float l_run = l_a + l_b;
@@ -692,12 +725,12 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(
 
 // ------------------------------------------------------------ launcher
 
-template <int D>
+template <int D, bool SKIP = false>
 static hipError_t launch_attn_d(bool bf16, const void* q, int64_t ld_q, const void* k,
                                 int64_t ld_k, const void* v, int64_t ld_v, void* o,
                                 int64_t ld_o, int64_t n_buf, int n_heads, const int* cu,
                                 const int* valid, int n_seg, int max_len, float scale, void* ws,
-                                hipStream_t s) {
+                                hipStream_t s, float skip_log2 = 0.f) {
   if (n_buf == 0) return hipSuccess;
   // rows that are not valid rows of any segment get zeros
   const unsigned zblocks = (unsigned)ceil_div(n_buf, 4);
@@ -715,10 +748,10 @@ static hipError_t launch_attn_d(bool bf16, const void* q, int64_t ld_q, const vo
                        dim3(256), 0, s, (const bf16_t*)v, ld_v, (bf16_t*)ws, cols, cu, valid);
     constexpr int NW = 8;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_fwd_bf16_pipe_kernel<D, NW>),
+    hipLaunchKernelGGL((attn_fwd_bf16_pipe_kernel<D, NW, SKIP>),
                        dim3((unsigned)ceil_div(max_len, NW * 32), n_seg, n_heads), dim3(NW * 64), 0,
                        s, (const bf16_t*)q, ld_q, (const bf16_t*)k, ld_k, (const bf16_t*)ws, cols,
-                       (bf16_t*)o, ld_o, cu, valid, scale_log2);
+                       (bf16_t*)o, ld_o, cu, valid, scale_log2, skip_log2);
   } else {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)ceil_div(max_len, 128), n_seg, n_heads),
                        dim3(128), 0, s, (const float*)q, ld_q, (const float*)k, ld_k,
@@ -742,6 +775,18 @@ hipError_t launch_varlen_attn(bool bf16, int head_dim, const void* q, int64_t ld
                               n_seg, max_len, scale, ws, s);
   return launch_attn_d<64>(bf16, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu, valid,
                            n_seg, max_len, scale, ws, s);
+}
+
+hipError_t launch_varlen_attn_skip(int head_dim, const void* q, int64_t ld_q, const void* k,
+                                   int64_t ld_k, const void* v, int64_t ld_v, void* o,
+                                   int64_t ld_o, int64_t n_buf, int n_heads, const int* cu,
+                                   const int* valid, int n_seg, int max_len, float scale,
+                                   float skip_log2, void* ws, hipStream_t s) {
+  if (head_dim == 128)
+    return launch_attn_d<128, true>(true, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu,
+                                    valid, n_seg, max_len, scale, ws, s, skip_log2);
+  return launch_attn_d<64, true>(true, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu,
+                                 valid, n_seg, max_len, scale, ws, s, skip_log2);
 }
 
 

@@ -406,6 +406,31 @@ def main():
     ops["attention_fp8"] = timer.time(lambda: h3.h3_varlen_attn_fp8(
         q_v, k_v, v_v, o8, hc, D, cu, vl, max_len, ws=ws8), reps)
     del ws8, o8
+    # Skip-Softmax on the same operands (t = -20: random scores leave no key
+    # block that far below the running max, so this is the rule's overhead)
+    o_sk = torch.empty_like(o_v)
+    ops["attention_skip_random"] = timer.time(lambda: h3.h3_varlen_attn_skip(
+        q_v, k_v, v_v, o_sk, hc, D, cu, vl, max_len, -20.0, ws=attn_ws), reps)
+    # ... and on operands where attention is concentrated: every query is
+    # 4 e0 + noise and 3 of 4 key blocks (after the first) score ~4.5 log2
+    # units below the others, so with t = -3 they are skipped
+    gsk = torch.Generator(device="cuda").manual_seed(11)
+    qs = (torch.randn((n_buf, hc, D), generator=gsk, device="cuda") * 0.05)
+    qs[:, :, 0] += 4.0
+    ks = torch.randn((n_buf, hc, D), generator=gsk, device="cuda")
+    far = torch.rand((n_buf + 63) // 64, generator=gsk, device="cuda") < 0.75
+    far[0] = False
+    far_rows = far.repeat_interleave(64)[:n_buf]
+    c_far = 4.5 / (4.0 * 1.4426950408889634 / D ** 0.5)
+    ks[far_rows] = torch.randn((int(far_rows.sum()), hc, D), generator=gsk, device="cuda") * 0.05
+    ks[far_rows, :, 0] -= c_far
+    qs, ks = qs.reshape(n_buf, hc * D).to(bf), ks.reshape(n_buf, hc * D).to(bf)
+    ops["attention_concentrated_exact"] = timer.time(lambda: h3.h3_varlen_attn(
+        qs, ks, v_v, o_sk, hc, D, cu, vl, max_len, ws=attn_ws), reps)
+    ops["attention_concentrated_skip"] = timer.time(lambda: h3.h3_varlen_attn_skip(
+        qs, ks, v_v, o_sk, hc, D, cu, vl, max_len, -3.0, ws=attn_ws), reps)
+    skip_frac = float(far.float().mean())
+    del qs, ks, o_sk, far, far_rows
     o_in = share["o_local"] if wl.share_mode else o_v
     ops["out_gemm_residual"] = timer.time(lambda: h3.h3_linear(o_in, wd["w_o"], xs, gate=mod[:, 2]), reps)
     sw_ws = torch.empty(h3.swiglu_workspace_size(wl.n_loc, wl.ffn_dim, bf), dtype=torch.uint8, device="cuda")
@@ -465,6 +490,14 @@ def main():
                           "frac_peak": work["attn_flop"] / ops["attention_fp8"] / 1e9 / FP8_PEAK_TFLOPS,
                           "peak": "fp8 dense MFMA", "speedup_vs_bf16": attn_ms / ops["attention_fp8"],
                           "operands": "MX e4m3 Q/K/V (E8M0 scale per 32), P as e4m3"},
+        "attention_skip": {"random_ms": ops["attention_skip_random"],
+                           "random_vs_exact": ops["attention_skip_random"] / attn_ms,
+                           "concentrated_exact_ms": ops["attention_concentrated_exact"],
+                           "concentrated_skip_ms": ops["attention_concentrated_skip"],
+                           "concentrated_speedup": ops["attention_concentrated_exact"] / ops["attention_concentrated_skip"],
+                           "concentrated_far_block_frac": skip_frac,
+                           "note": "Skip-Softmax; random operands t=-20 (no block skipped), concentrated "
+                                   "operands t=-3 (the far key blocks skipped)"},
         "block_fp8_attention": {"ms": ops["block_fp8_attention"],
                                 "TFLOP/s": total_flop / ops["block_fp8_attention"] / 1e9,
                                 "note": "the same block with attention on the FP8 path"},

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 4
+#define H3_ABI_VERSION 5
 
 typedef enum {
   H3_OK = 0,
@@ -129,6 +129,28 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
                          const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
                          float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
                          void* stream);
+
+/*
+ * h3_varlen_attn_skip -- h3_varlen_attn with Skip-Softmax (MiniMax H3 通过
+ * vLLM-Omni 实现 FastH3 实时推理, "超出 FastH3 配置的扩展能力": Skip-Softmax is
+ * named among the attention variants that speed up the base pipeline).
+ * Keys are visited in blocks of 64 from each segment's start, queries in
+ * groups of 32 consecutive valid rows; a block is skipped for a group (its
+ * probabilities are exactly zero and its P.V products are not computed) when, for
+ * every valid row of the group, the block's largest score q.k * scale *
+ * log2(e) is below the row's running maximum over the blocks before it plus
+ * skip_log2.  The first block is never skipped.  A skipped key's weight is at
+ * most 2^skip_log2 times its row's largest weight.  skip_log2 < 0 (-inf: no
+ * block is skipped and the result equals h3_varlen_attn's bit for bit).
+ * Arguments, layouts, workspace and errors as h3_varlen_attn; bf16 only
+ * (H3_ERR_UNSUPPORTED otherwise).
+ */
+h3_status h3_varlen_attn_skip(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                              const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
+                              int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
+                              const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
+                              float softmax_scale, float skip_log2, void* ws, size_t ws_bytes,
+                              h3_dtype dtype, void* stream);
 
 /*
  * h3_varlen_attn_fp8 -- the same attention with FP8 operands (MiniMax H3 通过
@@ -277,6 +299,8 @@ typedef struct {
   h3_dtype dtype;
   int32_t attn_fp8;   /* 1: attention through h3_varlen_attn_fp8 (bf16 only); 0: exact path */
   int32_t gemm_fp8;   /* 1: the four projections on MX operands (bf16 only, weights.mx); 0: bf16 */
+  float attn_skip_log2; /* < 0: attention through h3_varlen_attn_skip with this threshold t
+                           (bf16 only, not with attn_fp8; -inf never skips); 0: exact path */
 } h3_block_config;
 
 typedef struct {

@@ -14,14 +14,14 @@ def weights_dev(w, dtype):
     return {k: dev(getattr(w, k), dtype) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")}
 
 
-def cfg_of(lib, wl, dtype, attn_fp8=False, gemm_fp8=False):
+def cfg_of(lib, wl, dtype, attn_fp8=False, gemm_fp8=False, attn_skip_log2=0.0):
     return lib.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
                             wl.eps_qk, wl.eps_mod, 0, TORCH_DT[dtype], attn_fp8=attn_fp8,
-                            gemm_fp8=gemm_fp8)
+                            gemm_fp8=gemm_fp8, attn_skip_log2=attn_skip_log2)
 
 
 def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=False,
-              attn_fp8=False, gemm_fp8=False):
+              attn_fp8=False, gemm_fp8=False, attn_skip_log2=0.0):
     x = dev(bi.x if x_override is None else x_override, dtype)
     mod = dev(bi.mod if mod_override is None else mod_override, dtype)
     extra = share_buffers(wl, bi, dtype, peer) if wl.share_mode else {}
@@ -29,7 +29,7 @@ def run_block(lib, wl, w, bi, dtype, x_override=None, mod_override=None, peer=Fa
     if gemm_fp8:
         # only the MX copies and the gains reach the block
         wd = {"mx": lib.block_weights_mx(wd), "g_q": wd["g_q"], "g_k": wd["g_k"]}
-    lib.h3_dit_block_forward(cfg_of(lib, wl, dtype, attn_fp8, gemm_fp8), wd, x, mod,
+    lib.h3_dit_block_forward(cfg_of(lib, wl, dtype, attn_fp8, gemm_fp8, attn_skip_log2), wd, x, mod,
                              dev_i32(bi.pos),
                              dev_i32(bi.cu_slots), dev_i32(bi.valid_len), int(bi.valid_len.max()),
                              **extra)
@@ -217,3 +217,24 @@ def test_block_fp8_projections(lib, case):
     bf16_path = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
                           attn_fp8=attn8)
     assert not np.array_equal(got, bf16_path)  # the FP8 projections really ran
+
+
+@pytest.mark.parametrize("case", ["world1", "share_r2", "peer_r3"])
+def test_block_skip_softmax_option(lib, case):
+    """The block's Skip-Softmax option reaches the attention step with the
+    block's own layouts.  On these random-weight inputs every key block has a
+    score within 0.4 log2 units of its group's running max (checked on the
+    oracle's q and k), so no block is skipped at t = -20 or t = -2 and the block
+    must equal the exact block bit for bit; the skip rule itself is checked
+    against the oracle in the attention tests."""
+    rank = {"world1": None, "share_r2": 2, "peer_r3": 3}[case]
+    wl = W.TINY if rank is None else W.TINY.replace(sp_degree=4, rank=rank)
+    w = W.block_weights(wl, 4, "bf16")
+    bi = W.block_inputs(wl, 4, "bf16")
+    x, mod = _update_dominant(bi)
+    peer = case.startswith("peer")
+    base = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer)
+    for t in (-20.0, -2.0):
+        got = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
+                        attn_skip_log2=t)
+        assert np.array_equal(got, base), (case, t)

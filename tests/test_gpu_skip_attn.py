@@ -1,0 +1,108 @@
+"""Skip-Softmax attention (GPU) against the oracle's Skip-Softmax rule.
+
+Inputs are built so that every skip decision has a wide margin (on these
+seeds the closest skipped block sits 2.2 log2 units below the threshold and
+the closest kept one 1.7 above, far beyond the ~1e-5 by which the kernel's
+fp32 scores differ from the oracle's float64 ones), so both take the same
+decisions; the kept blocks then go through the exact attention path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from _util import assert_close, dev, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _blocky(lengths, n_buf, H, D, far_frac, seed):
+    """q = 4 e0 + N(0, 0.05^2); keys N(0, 1), except in a seeded subset of each
+    segment's 64-key blocks (never the first), whose keys are -c e0 + N(0,
+    0.05^2) with c set so that their scores sit at -4.5 log2 units.  The kept
+    blocks' maxima are near +1.3, so with t = -3 the far blocks are skipped
+    with a margin of ~3 and the others kept with a margin of ~4, while the
+    skipped weight (2^-4.5 per key relative to the row max) is large enough to
+    see in the output."""
+    g = np.random.default_rng(seed)
+    e0 = np.zeros(D, np.float32)
+    e0[0] = 1.0
+    c = 4.5 / (4.0 * np.log2(np.e) / np.sqrt(D))
+    q = (4.0 * e0 + 0.05 * g.standard_normal((n_buf, H, D))).astype(np.float32)
+    k = g.standard_normal((n_buf, H, D)).astype(np.float32)
+    v = g.standard_normal((n_buf, H, D)).astype(np.float32)
+    # each segment's slot: its length rounded up to 32 plus 16 padding rows,
+    # the last slot running to the end of the buffer
+    cu = np.zeros(len(lengths) + 1, np.int64)
+    for s, n in enumerate(lengths):
+        cu[s + 1] = cu[s] + 32 * (-(-n // 32)) + 16
+    assert cu[-1] <= n_buf
+    cu[-1] = n_buf
+    far_blocks = 0
+    for s, n in enumerate(lengths):
+        for b in range(1, -(-n // 64)):
+            if g.random() < far_frac:
+                lo = cu[s] + 64 * b
+                hi = min(lo + 64, cu[s] + n)
+                k[lo:hi] = -c * e0 + 0.05 * g.standard_normal((hi - lo, H, D))
+                far_blocks += 1
+    r = lambda a: W.round_to_bf16(a)
+    return r(q), r(k), r(v), cu, np.asarray(lengths), far_blocks
+
+
+def _run(lib, q, k, v, cu, vl, H, D, skip_log2):
+    n_buf = q.shape[0]
+    qd, kd, vd = (dev(a.reshape(n_buf, H * D), "bf16") for a in (q, k, v))
+    o = torch.full((n_buf, H * D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if skip_log2 is None:
+        lib.h3_varlen_attn(qd, kd, vd, o, H, D, dev_i32(cu), dev_i32(vl), int(vl.max()))
+    else:
+        lib.h3_varlen_attn_skip(qd, kd, vd, o, H, D, dev_i32(cu), dev_i32(vl), int(vl.max()), skip_log2)
+    torch.cuda.synchronize()
+    return host(o).reshape(n_buf, H, D)
+
+
+@pytest.mark.parametrize("lengths,n_buf,H,D", [((700, 333, 64), 1200, 2, 128), ((500, 40), 640, 3, 64)])
+def test_skip_matches_oracle_rule(lib, lengths, n_buf, H, D):
+    q, k, v, cu, vl, far = _blocky(lengths, n_buf, H, D, 0.5, seed=3)
+    assert far > 0
+    got = _run(lib, q, k, v, cu, vl, H, D, -3.0)
+    ref = O.varlen_attention_skip(q, k, v, cu, vl, -3.0)
+    exact = O.varlen_attention(q, k, v, cu, vl)
+    valid = np.zeros(n_buf, bool)
+    for s in range(len(vl)):
+        valid[cu[s]:cu[s] + vl[s]] = True
+    assert_close(got[valid], ref[valid], "bf16", f"skip {lengths}")
+    assert np.all(got[~valid] == 0)
+    # the kernel took the skips: it sits on the Skip-Softmax result, several
+    # times closer to it than to exact attention
+    to_ref = np.abs(got[valid] - ref[valid]).mean()
+    to_exact = np.abs(got[valid] - exact[valid]).mean()
+    assert to_exact > 3 * to_ref, (to_ref, to_exact)
+
+
+@pytest.mark.parametrize("lengths,n_buf,H,D", [((700, 333, 64), 1200, 2, 128), ((500, 40), 640, 3, 64)])
+def test_skip_without_skips_is_the_exact_kernel(lib, lengths, n_buf, H, D):
+    """-inf threshold, and a finite one with nothing below it: bit for bit the exact path."""
+    q, k, v, cu, vl, _ = _blocky(lengths, n_buf, H, D, 0.0, seed=4)
+    base = _run(lib, q, k, v, cu, vl, H, D, None)
+    assert np.array_equal(_run(lib, q, k, v, cu, vl, H, D, float("-inf")), base)
+    assert np.array_equal(_run(lib, q, k, v, cu, vl, H, D, -30.0), base)
+
+
+def test_skip_10s_share_random_inputs_skip_nothing(lib):
+    """On the 10 s share's random operands no key block is far enough below the
+    running max for t = -20: the Skip-Softmax path equals the exact one."""
+    wl = W.SHARE_10S
+    N, hc, D = wl.n_pad_total, wl.head_count, wl.head_dim
+    g = torch.Generator(device="cuda").manual_seed(5)
+    qa = torch.randn((N, 3 * hc * D), generator=g, device="cuda").to(torch.bfloat16)
+    q, k, v = qa[:, :hc * D], qa[:, hc * D:2 * hc * D], qa[:, 2 * hc * D:]
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    vl = torch.tensor([wl.n_valid], dtype=torch.int32, device="cuda")
+    o1 = torch.empty((N, hc * D), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    lib.h3_varlen_attn(q, k, v, o1, hc, D, cu, vl, wl.n_valid)
+    lib.h3_varlen_attn_skip(q, k, v, o2, hc, D, cu, vl, wl.n_valid, -20.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
