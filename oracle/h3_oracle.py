@@ -481,13 +481,15 @@ def fp8_fold(head_dim: int) -> np.float32:
     return np.float32(inv * np.float32(1.4426950408889634))
 
 
-def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None):
+def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, skip_log2=None):
     """Attention over the MX-e4m3-quantized operands of the FP8 path, exact
     otherwise (no rounding of the probabilities).  k, v [N, h, D] float32
     values; q is [N, h, D], or [len(q_rows), h, D] already restricted to the
     query rows q_rows (buffer rows).  Q is quantized after folding scale * log2(e); the scores are then
     in log2 units, and softmax uses base 2.  The FP8 kernel differs from this
-    only by rounding 256 * p to e4m3 and by fp32 accumulation."""
+    only by rounding 256 * p to e4m3 and by fp32 accumulation.
+    skip_log2: apply the Skip-Softmax rule (skip_softmax_rows) to the scores
+    of the quantized operands; q must then hold every buffer row."""
     q = np.asarray(q, dtype=np.float32)
     D = q.shape[-1]
     c = float(fp8_fold(D))
@@ -521,6 +523,10 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None):
             continue
         for hh in range(h):
             sc = qd[sel, hh] @ kd[lo:lo + n, hh].T                  # log2 units
+            if skip_log2 is not None:
+                assert sel.size == n and np.all(rows[sel] == np.arange(lo, lo + n))
+                out[sel, hh] = skip_softmax_rows(sc, vdq[lo:lo + n, hh], skip_log2)
+                continue
             sc -= sc.max(axis=1, keepdims=True)
             p = np.exp2(sc)
             out[sel, hh] = (p @ vdq[lo:lo + n, hh]) / p.sum(axis=1, keepdims=True)
@@ -561,6 +567,29 @@ def linear_fp8_operands(x, w) -> np.ndarray:
 # i.e. q.k * scale * log2 e; t < 0).  The first block is never skipped.  A
 # skipped key's weight is at most 2^t times the row's largest weight.
 
+def skip_softmax_rows(sc, v, skip_log2: float, q_group: int = 32, k_block: int = 64) -> np.ndarray:
+    """One segment and head under the rule above: sc [n, n] scores in log2
+    units (query row i of the segment against key j), v [n, D].  Returns the
+    n output rows, each a base-2 softmax over the keys its group keeps."""
+    n = sc.shape[0]
+    out = np.zeros((n, v.shape[1]))
+    for g0 in range(0, n, q_group):
+        rows = slice(g0, min(g0 + q_group, n))
+        keep = np.zeros(n, dtype=bool)
+        m_run = None
+        for b0 in range(0, n, k_block):
+            blk = slice(b0, min(b0 + k_block, n))
+            bmax = sc[rows, blk].max(axis=1)
+            if m_run is not None and np.all(bmax < m_run + skip_log2):
+                continue
+            keep[blk] = True
+            m_run = bmax if m_run is None else np.maximum(m_run, bmax)
+        ss = sc[rows][:, keep]
+        p = np.exp2(ss - ss.max(axis=1, keepdims=True))
+        out[rows] = (p @ v[keep]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def varlen_attention_skip(q, k, v, cu_slots, valid_len, skip_log2: float,
                           scale: Optional[float] = None, q_group: int = 32,
                           k_block: int = 64) -> np.ndarray:
@@ -577,20 +606,9 @@ def varlen_attention_skip(q, k, v, cu_slots, valid_len, skip_log2: float,
     vl = np.asarray(valid_len) if valid_len is not None else np.diff(cu)
     for s in range(len(cu) - 1):
         lo, n = int(cu[s]), int(vl[s])
+        if n == 0:
+            continue
         for head in range(h):
             sc = (q[lo:lo + n, head] @ k[lo:lo + n, head].T) * c   # log2 units
-            for g0 in range(0, n, q_group):
-                rows = slice(g0, min(g0 + q_group, n))
-                keep = np.zeros(n, dtype=bool)
-                m_run = None
-                for b0 in range(0, n, k_block):
-                    blk = slice(b0, min(b0 + k_block, n))
-                    bmax = sc[rows, blk].max(axis=1)
-                    if m_run is not None and np.all(bmax < m_run + skip_log2):
-                        continue
-                    keep[blk] = True
-                    m_run = bmax if m_run is None else np.maximum(m_run, bmax)
-                ss = sc[rows][:, keep]
-                p = np.exp2(ss - ss.max(axis=1, keepdims=True))
-                out[lo + g0:lo + min(g0 + q_group, n), head] = (p @ v[lo:lo + n, head][keep]) / p.sum(axis=1, keepdims=True)
+            out[lo:lo + n, head] = skip_softmax_rows(sc, v[lo:lo + n, head], skip_log2, q_group, k_block)
     return out

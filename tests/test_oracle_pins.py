@@ -836,3 +836,31 @@ def test_skip_softmax_first_block_and_group_rule():
     exact2 = O.varlen_attention(q2, k2, v2, cu, vl)
     np.testing.assert_allclose(got2[:32], exact2[:32], rtol=1e-10, atol=1e-12)   # group 0 keeps block 2
     assert np.abs(got2[32:64] - exact2[32:64]).max() > 0                     # group 1 skips it
+
+
+def test_fp8_skip_softmax_on_grid_operands_is_the_skip_rule():
+    """On operands already on the MX-e4m3 grid the FP8 oracle quantizes nothing
+    away, so with a threshold it must be the Skip-Softmax oracle itself."""
+    q, k, v = _blocky_case()
+    n, h, d = q.shape
+    # far blocks at ~-12 log2 units (not -40), so that dropping them shows at t = -6
+    k[64:128, :, 0] += 38.0
+    k[192:256, :, 0] += 38.0
+    cu, vl = np.array([0, n]), np.array([n])
+    c = O.fp8_fold(d)
+    # grid values of the folded Q (scores in log2 units), and a Q that folds onto them
+    qd = O.mx_dequantize(*O.mx_quantize(q.astype(np.float32), fold=c))
+    qin = (qd / np.float64(c)).astype(np.float32)
+    # folding the scale back in lands on the same grid values
+    assert np.array_equal(O.mx_dequantize(*O.mx_quantize(qin, fold=c)), qd)
+    kd = O.mx_dequantize(*O.mx_quantize(k.astype(np.float32)))
+    vq, ve = O.mx_quantize(v.astype(np.float32).transpose(1, 2, 0))   # blocks of 32 keys
+    vd = O.mx_dequantize(vq, ve).transpose(2, 0, 1)
+    got = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-6.0)
+    # scores q.k in log2 units: scale 1/log2(e) undoes the oracle's own log2(e)
+    want = O.varlen_attention_skip(qd, kd, vd, cu, vl, -6.0, scale=1.0 / np.log2(np.e))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-9)
+    plain = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl)
+    assert np.abs(got - plain).max() > 1e-6          # the far blocks were dropped
+    np.testing.assert_allclose(O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-1e9),
+                               plain, rtol=0, atol=1e-12)
