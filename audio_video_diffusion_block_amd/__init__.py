@@ -115,6 +115,9 @@ _c_attn8 = _sig("h3_varlen_attn_fp8", ctypes.c_int,
 _c_attn_skip = _sig("h3_varlen_attn_skip", ctypes.c_int,
                     [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32,
                      _f, _f, _p, _sz, _i32, _p])
+_c_attn8_skip = _sig("h3_varlen_attn_fp8_skip", ctypes.c_int,
+                     [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32,
+                      _f, _f, _p, _sz, _i32, _p])
 _c_mxq = _sig("h3_mx_quantize", ctypes.c_int,
               [_p, _i64, _i64, _i32, _p, _i64, _p, _i64, _i32, _p])
 _c_lin8 = _sig("h3_linear_fp8", ctypes.c_int,
@@ -130,7 +133,7 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
-            "h3_swiglu_fp8", "h3_varlen_attn_skip")
+            "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip")
 
 
 def _status_string(st: int) -> str:
@@ -249,6 +252,20 @@ def h3_varlen_attn_fp8(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.
                     n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
                     softmax_scale, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
                     _stream(stream)))
+
+
+def h3_varlen_attn_fp8_skip(q, k, v, o, n_heads: int, head_dim: int, cu_slots, valid_len,
+                            max_valid_len: int, skip_log2: float, softmax_scale: float = 0.0,
+                            ws: Optional[torch.Tensor] = None, stream=None):
+    """h3_varlen_attn_fp8 with the Skip-Softmax rule of h3_varlen_attn_skip."""
+    n_buf = q.shape[0]
+    n_seg = cu_slots.shape[0] - 1
+    if ws is None:
+        ws = _bytes_ws(varlen_attn_fp8_workspace_size(n_buf, n_heads, head_dim, n_seg), q.device)
+    _check(_c_attn8_skip(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
+                         n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
+                         softmax_scale, skip_log2, _ptr(ws), ws.numel() * ws.element_size(),
+                         _dt(q), _stream(stream)))
 
 
 def h3_modulate_residual(x, y=None, gate=None, shift=None, scale=None, h_out=None,

@@ -309,13 +309,13 @@ size_t h3_varlen_attn_fp8_workspace_size(int64_t n_buf, int32_t n_heads, int32_t
   return attn_fp8_workspace_bytes(n_buf, n_heads, head_dim, n_seg);
 }
 
-h3_status h3_varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
-                             const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
-                             int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
-                             const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
-                             float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
-                             void* stream) {
-  g_err[0] = 0;
+namespace {
+h3_status varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
+                          int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf, int32_t n_heads,
+                          int32_t head_dim, const int32_t* cu_slots, const int32_t* valid_len,
+                          int32_t n_seg, int32_t max_valid_len, float softmax_scale,
+                          float skip_log2, void* ws, size_t ws_bytes, h3_dtype dtype,
+                          void* stream) {
   if (dtype != H3_BF16) return fail(H3_ERR_UNSUPPORTED, "the FP8 attention takes bf16 operands");
   TRY(validate_attn(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, head_dim, cu_slots, n_seg,
                     max_valid_len, ws, ws_bytes, dtype, true));
@@ -324,8 +324,35 @@ h3_status h3_varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   return hip_status(launch_varlen_attn_fp8(head_dim, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf,
                                            n_heads, cu_slots, valid_len, n_seg, max_valid_len,
-                                           scale, ws, (hipStream_t)stream),
+                                           scale, skip_log2, ws, (hipStream_t)stream),
                     "varlen_attn_fp8 launch");
+}
+}  // namespace
+
+h3_status h3_varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                             const void* v, int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf,
+                             int32_t n_heads, int32_t head_dim, const int32_t* cu_slots,
+                             const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
+                             float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
+                             void* stream) {
+  g_err[0] = 0;
+  return varlen_attn_fp8(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, head_dim, cu_slots,
+                         valid_len, n_seg, max_valid_len, softmax_scale, 0.f, ws, ws_bytes, dtype,
+                         stream);
+}
+
+h3_status h3_varlen_attn_fp8_skip(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                                  const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                                  int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                  const int32_t* cu_slots, const int32_t* valid_len,
+                                  int32_t n_seg, int32_t max_valid_len, float softmax_scale,
+                                  float skip_log2, void* ws, size_t ws_bytes, h3_dtype dtype,
+                                  void* stream) {
+  g_err[0] = 0;
+  CHECK(skip_log2 < 0.f, "skip_log2 must be negative (-inf: never skip)");
+  return varlen_attn_fp8(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, head_dim, cu_slots,
+                         valid_len, n_seg, max_valid_len, softmax_scale, skip_log2, ws, ws_bytes,
+                         dtype, stream);
 }
 
 h3_status h3_modulate_residual(void* x, int64_t ld_x, const void* y, int64_t ld_y,
@@ -548,8 +575,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   CHECK(cfg->gemm_fp8 == 0 || cfg->gemm_fp8 == 1, "gemm_fp8 must be 0 or 1");
   CHECK(cfg->attn_skip_log2 <= 0.f, "attn_skip_log2 must be 0 (off) or negative");
   const bool skip = cfg->attn_skip_log2 < 0.f;
-  CHECK(!skip || (dt == H3_BF16 && !cfg->attn_fp8),
-        "Skip-Softmax attention needs bf16 storage and attn_fp8 = 0");
+  CHECK(!skip || dt == H3_BF16, "Skip-Softmax attention needs bf16 storage");
   const bool f8 = cfg->gemm_fp8 == 1;
   if (f8) {
     CHECK(dt == H3_BF16, "the FP8 projections need bf16 storage");
@@ -636,8 +662,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                        int64_t ldv, void* o, int64_t ldo, int64_t rows, int heads) {
     if (cfg->attn_fp8)
       return launch_varlen_attn_fp8(D, q, ldq, k, ldk, v, ldv, o, ldo, rows, heads, io->cu_slots,
-                                    io->valid_len, io->n_seg, io->max_valid_len, scale, attn_ws,
-                                    s);
+                                    io->valid_len, io->n_seg, io->max_valid_len, scale,
+                                    skip ? cfg->attn_skip_log2 : 0.f, attn_ws, s);
     if (skip)
       return launch_varlen_attn_skip(D, q, ldq, k, ldk, v, ldv, o, ldo, rows, heads,
                                      io->cu_slots, io->valid_len, io->n_seg, io->max_valid_len,

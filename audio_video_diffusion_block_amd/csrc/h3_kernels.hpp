@@ -77,13 +77,14 @@ hipError_t launch_varlen_attn_skip(int head_dim, const void* q, int64_t ld_q, co
                                    float skip_log2, void* ws, hipStream_t s);
 
 // FP8 (MX-scaled e4m3) attention: bf16 q, k, v, o as above; workspace holds
-// the quantized operands and their block scales
+// the quantized operands and their block scales.  skip_log2 < 0: with the
+// Skip-Softmax rule at that threshold; 0: without it
 size_t attn_fp8_workspace_bytes(int64_t n_buf, int n_heads, int head_dim, int n_seg);
 hipError_t launch_varlen_attn_fp8(int head_dim, const void* q, int64_t ld_q, const void* k,
                                   int64_t ld_k, const void* v, int64_t ld_v, void* o,
                                   int64_t ld_o, int64_t n_buf, int n_heads, const int* cu,
-                                  const int* valid, int n_seg, int max_len, float scale, void* ws,
-                                  hipStream_t s);
+                                  const int* valid, int n_seg, int max_len, float scale,
+                                  float skip_log2, void* ws, hipStream_t s);
 
 // strides and group sizes in BYTES (multiples of 16)
 hipError_t launch_copy_rows(const void* src, int64_t ld_src, int64_t gs_src, void* dst,

@@ -934,13 +934,17 @@ __device__ __forceinline__ i32x8_t frag32(const uint8_t* p0, const uint8_t* p1) 
 }
 }  // namespace
 
-template <int D, int NW>
+// SKIP (Skip-Softmax): as in the bf16 kernel, a wave leaves out the softmax
+// slots and the P.V and row-sum MFMAs of a key tile when every valid row's
+// tile max is more than |skip_log2| below its exact running max.  Here the
+// softmax is most of the VALU work, so the skipped slots are branched around.
+template <int D, int NW, bool SKIP = false>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qs,
     const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ks, int64_t n_buf,
     const uint8_t* __restrict__ vt8, const uint8_t* __restrict__ vts, int64_t vt_cols,
     bf16_t* __restrict__ o, int64_t ld_o, const int* __restrict__ cu,
-    const int* __restrict__ valid) {
+    const int* __restrict__ valid, float skip_log2 = 0.f) {
   constexpr int BMQ = NW * 32;
   constexpr int NTH = NW * 64;
   constexpr int NT = D / 64;          // 64-deep steps of S (1 or 2)
@@ -1079,6 +1083,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   // Scores are kept relative to m_ref = m_run - 8: each score chain starts from
   // negm (= -m_ref in all 16 registers), so exp2 of a score is 256 p.
   float m_ref = 0.f;
+  float mt_rel = 8.f;        // SKIP: exact running max, relative to m_ref
   f32x16_t negm;
   f32x16_t lacc;             // row sums of the stored weights (register 0 is used)
 #pragma unroll
@@ -1096,16 +1101,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       for (int r = 0; r < 16; ++r)
         if (base + kb * 32 + 16 * hf + r >= len) sc[kb][r] = -INFINITY;
   };
-  auto update_max = [&](float mx, f32x16_t (&sc)[2]) {
+  auto update_max = [&](float mx, f32x16_t (&sc)[2]) -> bool {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    bool skip = false;
+    if constexpr (SKIP) {
+      skip = __all(!q_ok || mx < mt_rel + skip_log2);
+      mt_rel = fmaxf(mt_rel, mx);
+    }
     const bool raise = mx > 8.75f;  // tile max above the running max + 0.75
     if (__any(raise)) {
       scaled_mfma_drain();
       const float delta = raise ? mx - 8.0f : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       m_ref += delta;
+      if constexpr (SKIP) mt_rel -= delta;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sc[0][r] -= delta;
@@ -1118,6 +1129,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    return skip;
   };
   auto compute_s = [&](int stage, f32x16_t (&sc)[2]) {
     const uint8_t* st = smem + stage * STAGE;
@@ -1138,7 +1150,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   constexpr int SPS = 32 / NA;     // scores per phase-A slot (multiple of 4)
   static_assert(SPS % 4 == 0, "slot holds whole packed words");
   // phase A: S(next) MFMAs, each followed by 1/NA of the softmax of S(cur)
-  auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], f32x16_t (&cur)[2], int jt) {
+  auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], f32x16_t (&cur)[2], int jt,
+                     bool skip) {
     const uint8_t* sk = smem + stage_k * STAGE;
     __builtin_amdgcn_s_setprio(2);
     uint32_t ksc[2];
@@ -1154,6 +1167,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       if (i + 1 < NA) kf = kfrag(sk, (i + 1) & 1, (i + 1) >> 1);
       if (t == 0) nxt[kb] = mfma_e4m3<0>(a, qf[0], nxt[kb], ksc[kb], qsc);
       else nxt[kb] = mfma_e4m3<1>(a, qf[NT - 1], nxt[kb], ksc[kb], qsc);
+      if (!(SKIP && skip)) {
 #pragma unroll
       for (int w4 = 0; w4 < SPS / 4; ++w4) {
         const int word = i * (SPS / 4) + w4;  // packed word 0..7: scores 4*word .. 4*word+3
@@ -1167,6 +1181,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pw[word], false);
         pw[word] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], lo, true);
       }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -1176,7 +1191,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     }
   };
   // phase B: P.V MFMAs, each followed by part of the row max of S(next)
-  auto phase_b = [&](int stage_v, f32x16_t (&nxt)[2], int jt, bool last = false) {
+  // returns whether tile jt+1 is skipped (SKIP)
+  auto phase_b = [&](int stage_v, f32x16_t (&nxt)[2], int jt, bool skip,
+                     bool last = false) -> bool {
     const uint8_t* sv = smem + stage_v * STAGE;
     float mx = -INFINITY;
     i32x8_t vf[NBM];
@@ -1186,10 +1203,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       vf[db] = vfrag(sv, db);
       vsc[db] = vscale(sv, db);
     }
-    lacc = mfma_e4m3<0>(ones8, pw, lacc, 127u, PSC);
+    // a skipped tile issues no MFMA here, so the row max below would read
+    // S(next) right behind phase A's last scaled MFMA: wait it out
+    if (SKIP && skip) scaled_mfma_drain();
+    if (!(SKIP && skip)) lacc = mfma_e4m3<0>(ones8, pw, lacc, 127u, PSC);
 #pragma unroll
     for (int db = 0; db < NBM; ++db) {
-      oacc[db] = mfma_e4m3<0>(vf[db], pw, oacc[db], vsc[db], PSC);
+      if (!(SKIP && skip)) oacc[db] = mfma_e4m3<0>(vf[db], pw, oacc[db], vsc[db], PSC);
 #pragma unroll
       for (int e = 0; e < 32 / NBM; ++e) {
         const int idx = db * (32 / NBM) + e;
@@ -1199,7 +1219,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     }
     // after the last tile's P.V the epilogue reads O: let these MFMAs finish
     if (last || jt + 1 >= n_tiles) scaled_mfma_drain();
-    if (jt + 1 < n_tiles) update_max(mx, nxt);
+    if (jt + 1 < n_tiles) return update_max(mx, nxt);
+    return false;
   };
 
   // tiles 0 .. 3 in flight; 0 and 1 must land before the first step
@@ -1232,10 +1253,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   // is waited for before the barrier that ends the step, and tile jt+4 goes
   // into the stage of tile jt-1 right after it.
   const bool lag = wv >= NW / 2;
+  // SKIP flags: sk_cur for the tile whose softmax runs in this step, sk_prev
+  // for the lagging half's P.V of the tile before it
+  bool sk_cur = false, sk_prev = false;
   auto step = [&](int jt, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
-    if (lag && jt > 0) phase_b((jt - 1) % NSTAGE, cur, jt - 1);
-    phase_a((jt + 1) % NSTAGE, nxt, cur, jt);
-    if (!lag) phase_b(jt % NSTAGE, nxt, jt);
+    if (lag && jt > 0) {
+      sk_prev = sk_cur;
+      sk_cur = phase_b((jt - 1) % NSTAGE, cur, jt - 1, sk_prev);
+    }
+    phase_a((jt + 1) % NSTAGE, nxt, cur, jt, sk_cur);
+    if (!lag) sk_cur = phase_b(jt % NSTAGE, nxt, jt, sk_cur);
     wait_dma(jt + 3 < n_tiles ? 1 : 0);
     __syncthreads();
     if (jt + 4 < n_tiles) issue_tile(jt + 4);
@@ -1246,7 +1273,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     step(jt + 1, sb, sa);
   }
   // the lagging half's last P.V (its score argument is unused: no max follows)
-  if (lag) phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1, true);
+  if (lag) phase_b((n_tiles - 1) % NSTAGE, sa, n_tiles - 1, sk_cur, true);
 
   const float l_tot = lacc[0];  // every accumulator row holds the query's sum
   if (!q_ok) return;
@@ -1279,8 +1306,8 @@ template <int D>
 static hipError_t launch_attn_fp8_d(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
                                     const void* v, int64_t ld_v, void* o, int64_t ld_o,
                                     int64_t n_buf, int n_heads, const int* cu, const int* valid,
-                                    int n_seg, int max_len, float scale, void* ws,
-                                    hipStream_t s) {
+                                    int n_seg, int max_len, float scale, float skip_log2,
+                                    void* ws, hipStream_t s) {
   if (n_buf == 0) return hipSuccess;
   const unsigned zblocks = (unsigned)ceil_div(n_buf, 4);
   hipLaunchKernelGGL((zero_pad_rows_kernel<bf16_t>), dim3(zblocks), dim3(256), 0, s,
@@ -1302,22 +1329,26 @@ static hipError_t launch_attn_fp8_d(const void* q, int64_t ld_q, const void* k, 
   hipLaunchKernelGGL((transpose_quant_v_kernel<D>), dim3((unsigned)ceil_div(max_len, 64), n_seg, n_heads),
                      dim3(256), 0, s, (const bf16_t*)v, ld_v, vt8, vts, cols, cu, valid);
   constexpr int NW = 8;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW>),
-                     dim3((unsigned)ceil_div(max_len, NW * 32), n_seg, n_heads), dim3(NW * 64), 0,
-                     s, q8, qs, k8, ks, n_buf, vt8, vts, cols, (bf16_t*)o, ld_o, cu, valid);
+  const dim3 grid((unsigned)ceil_div(max_len, NW * 32), n_seg, n_heads);
+  if (skip_log2 < 0.f)
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, true>), grid, dim3(NW * 64), 0, s, q8, qs, k8,
+                       ks, n_buf, vt8, vts, cols, (bf16_t*)o, ld_o, cu, valid, skip_log2);
+  else
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW>), grid, dim3(NW * 64), 0, s, q8, qs, k8, ks,
+                       n_buf, vt8, vts, cols, (bf16_t*)o, ld_o, cu, valid, 0.f);
   return hipGetLastError();
 }
 
 hipError_t launch_varlen_attn_fp8(int head_dim, const void* q, int64_t ld_q, const void* k,
                                   int64_t ld_k, const void* v, int64_t ld_v, void* o,
                                   int64_t ld_o, int64_t n_buf, int n_heads, const int* cu,
-                                  const int* valid, int n_seg, int max_len, float scale, void* ws,
-                                  hipStream_t s) {
+                                  const int* valid, int n_seg, int max_len, float scale,
+                                  float skip_log2, void* ws, hipStream_t s) {
   if (head_dim == 128)
     return launch_attn_fp8_d<128>(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu, valid,
-                                  n_seg, max_len, scale, ws, s);
+                                  n_seg, max_len, scale, skip_log2, ws, s);
   return launch_attn_fp8_d<64>(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, cu, valid,
-                               n_seg, max_len, scale, ws, s);
+                               n_seg, max_len, scale, skip_log2, ws, s);
 }
 
 }  // namespace h3

@@ -405,12 +405,13 @@ def main():
     o8 = torch.empty_like(o_v)
     ops["attention_fp8"] = timer.time(lambda: h3.h3_varlen_attn_fp8(
         q_v, k_v, v_v, o8, hc, D, cu, vl, max_len, ws=ws8), reps)
-    del ws8, o8
     # Skip-Softmax on the same operands (t = -20: random scores leave no key
     # block that far below the running max, so this is the rule's overhead)
     o_sk = torch.empty_like(o_v)
     ops["attention_skip_random"] = timer.time(lambda: h3.h3_varlen_attn_skip(
         q_v, k_v, v_v, o_sk, hc, D, cu, vl, max_len, -20.0, ws=attn_ws), reps)
+    ops["attention_fp8_skip_random"] = timer.time(lambda: h3.h3_varlen_attn_fp8_skip(
+        q_v, k_v, v_v, o8, hc, D, cu, vl, max_len, -20.0, ws=ws8), reps)
     # ... and on operands where attention is concentrated: every query is
     # 4 e0 + noise and 3 of 4 key blocks (after the first) score ~4.5 log2
     # units below the others, so with t = -3 they are skipped
@@ -429,8 +430,12 @@ def main():
         qs, ks, v_v, o_sk, hc, D, cu, vl, max_len, ws=attn_ws), reps)
     ops["attention_concentrated_skip"] = timer.time(lambda: h3.h3_varlen_attn_skip(
         qs, ks, v_v, o_sk, hc, D, cu, vl, max_len, -3.0, ws=attn_ws), reps)
+    ops["attention_fp8_concentrated"] = timer.time(lambda: h3.h3_varlen_attn_fp8(
+        qs, ks, v_v, o8, hc, D, cu, vl, max_len, ws=ws8), reps)
+    ops["attention_fp8_concentrated_skip"] = timer.time(lambda: h3.h3_varlen_attn_fp8_skip(
+        qs, ks, v_v, o8, hc, D, cu, vl, max_len, -3.0, ws=ws8), reps)
     skip_frac = float(far.float().mean())
-    del qs, ks, o_sk, far, far_rows
+    del qs, ks, o_sk, far, far_rows, ws8, o8
     o_in = share["o_local"] if wl.share_mode else o_v
     ops["out_gemm_residual"] = timer.time(lambda: h3.h3_linear(o_in, wd["w_o"], xs, gate=mod[:, 2]), reps)
     sw_ws = torch.empty(h3.swiglu_workspace_size(wl.n_loc, wl.ffn_dim, bf), dtype=torch.uint8, device="cuda")
@@ -496,8 +501,14 @@ def main():
                            "concentrated_skip_ms": ops["attention_concentrated_skip"],
                            "concentrated_speedup": ops["attention_concentrated_exact"] / ops["attention_concentrated_skip"],
                            "concentrated_far_block_frac": skip_frac,
-                           "note": "Skip-Softmax; random operands t=-20 (no block skipped), concentrated "
-                                   "operands t=-3 (the far key blocks skipped)"},
+                           "fp8_random_ms": ops["attention_fp8_skip_random"],
+                           "fp8_random_vs_fp8": ops["attention_fp8_skip_random"] / ops["attention_fp8"],
+                           "fp8_concentrated_ms": ops["attention_fp8_concentrated"],
+                           "fp8_concentrated_skip_ms": ops["attention_fp8_concentrated_skip"],
+                           "fp8_concentrated_speedup": ops["attention_fp8_concentrated"] / ops["attention_fp8_concentrated_skip"],
+                           "fp8_skip_vs_bf16_exact": ops["attention_concentrated_exact"] / ops["attention_fp8_concentrated_skip"],
+                           "note": "Skip-Softmax on the bf16 and FP8 paths; random operands t=-20 (no block "
+                                   "skipped), concentrated operands t=-3 (the far key blocks skipped)"},
         "block_fp8_attention": {"ms": ops["block_fp8_attention"],
                                 "TFLOP/s": total_flop / ops["block_fp8_attention"] / 1e9,
                                 "note": "the same block with attention on the FP8 path"},

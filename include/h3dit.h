@@ -176,6 +176,23 @@ h3_status h3_varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t
                              void* stream);
 
 /*
+ * h3_varlen_attn_fp8_skip -- h3_varlen_attn_fp8 with the Skip-Softmax rule of
+ * h3_varlen_attn_skip (same page and section: SAGE FP8 and Skip-Softmax are
+ * named together).  The rule is applied to the scores of the quantized
+ * operands (log2 units: q already carries softmax_scale * log2 e).
+ * skip_log2 < 0 (H3_ERR_ARG otherwise, NaN included); -inf skips nothing and
+ * gives h3_varlen_attn_fp8's result.  Arguments, workspace and errors as
+ * h3_varlen_attn_fp8.
+ */
+h3_status h3_varlen_attn_fp8_skip(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                                  const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                                  int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                  const int32_t* cu_slots, const int32_t* valid_len,
+                                  int32_t n_seg, int32_t max_valid_len, float softmax_scale,
+                                  float skip_log2, void* ws, size_t ws_bytes, h3_dtype dtype,
+                                  void* stream);
+
+/*
  * h3_modulate_residual -- one pass over rows of width dim:
  *   if y != NULL:     x <- x + gate * y                       (gated residual)
  *   if h_out != NULL: h_out <- norm(x) * (1 + scale) + shift  (modulated norm)
@@ -299,8 +316,9 @@ typedef struct {
   h3_dtype dtype;
   int32_t attn_fp8;   /* 1: attention through h3_varlen_attn_fp8 (bf16 only); 0: exact path */
   int32_t gemm_fp8;   /* 1: the four projections on MX operands (bf16 only, weights.mx); 0: bf16 */
-  float attn_skip_log2; /* < 0: attention through h3_varlen_attn_skip with this threshold t
-                           (bf16 only, not with attn_fp8; -inf never skips); 0: exact path */
+  float attn_skip_log2; /* < 0: attention with the Skip-Softmax rule at this threshold t
+                           (h3_varlen_attn_skip, or h3_varlen_attn_fp8_skip with attn_fp8;
+                           bf16 only; -inf never skips); 0: without it */
 } h3_block_config;
 
 typedef struct {

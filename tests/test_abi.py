@@ -272,7 +272,6 @@ def test_block_skip_softmax_argument_checks():
     io = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 480, 0, 0, 4, None, None, None)
     cases = [(dict(attn_skip_log2=1.0), "attn_skip_log2"),
              (dict(attn_skip_log2=float("nan")), "attn_skip_log2"),
-             (dict(attn_skip_log2=-3.0, attn_fp8=True), "attn_fp8"),
              (dict(attn_skip_log2=-3.0, dtype=torch.float32), "bf16")]
     for kw, word in cases:
         cfg = h3.block_config(256, 4, 64, 704, (16, 24, 24), **kw)
@@ -282,3 +281,13 @@ def test_block_skip_softmax_argument_checks():
     on = h3.block_config(256, 4, 64, 704, (16, 24, 24), attn_skip_log2=-3.0)
     off = h3.block_config(256, 4, 64, 704, (16, 24, 24))
     assert h3.block_workspace_size(on, 480, 480, 1) == h3.block_workspace_size(off, 480, 480, 1)
+
+
+def test_fp8_skip_softmax_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    args = lambda t, dt: (FAKE, 256, FAKE, 256, FAKE, 256, FAKE, 256, 64, 4, 64, FAKE, None, 1, 64,
+                          0.0, t, FAKE, 1 << 24, dt, None)
+    assert h3._c_attn8_skip(*args(-10.0, h3.H3_F32)) == h3.H3_ERR_UNSUPPORTED
+    assert h3._c_attn8_skip(*args(0.0, h3.H3_BF16)) == h3.H3_ERR_ARG
+    assert "negative" in h3.last_error()
+    assert h3._c_attn8_skip(*args(float("nan"), h3.H3_BF16)) == h3.H3_ERR_ARG

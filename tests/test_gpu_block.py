@@ -219,22 +219,25 @@ def test_block_fp8_projections(lib, case):
     assert not np.array_equal(got, bf16_path)  # the FP8 projections really ran
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16_attn", "fp8_attn"])
 @pytest.mark.parametrize("case", ["world1", "share_r2", "peer_r3"])
-def test_block_skip_softmax_option(lib, case):
+def test_block_skip_softmax_option(lib, case, fp8):
     """The block's Skip-Softmax option reaches the attention step with the
     block's own layouts.  On these random-weight inputs every key block has a
     score within 0.4 log2 units of its group's running max (checked on the
-    oracle's q and k), so no block is skipped at t = -20 or t = -2 and the block
-    must equal the exact block bit for bit; the skip rule itself is checked
-    against the oracle in the attention tests."""
+    oracle's q and k, and on their FP8-quantized values), so no block is
+    skipped at t = -20 or t = -2 and the block must equal
+    the block without the option bit for bit, on either attention path; the
+    skip rule itself is checked against the oracle in the attention tests."""
     rank = {"world1": None, "share_r2": 2, "peer_r3": 3}[case]
     wl = W.TINY if rank is None else W.TINY.replace(sp_degree=4, rank=rank)
     w = W.block_weights(wl, 4, "bf16")
     bi = W.block_inputs(wl, 4, "bf16")
     x, mod = _update_dominant(bi)
     peer = case.startswith("peer")
-    base = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer)
+    base = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
+                     attn_fp8=fp8)
     for t in (-20.0, -2.0):
         got = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
-                        attn_skip_log2=t)
+                        attn_fp8=fp8, attn_skip_log2=t)
         assert np.array_equal(got, base), (case, t)

@@ -16,14 +16,16 @@ from _util import assert_close, dev, dev_i32, host
 pytestmark = pytest.mark.gpu
 
 
-def _blocky(lengths, n_buf, H, D, far_frac, seed):
+def _blocky(lengths, n_buf, H, D, far_frac, seed, v_far=None):
     """q = 4 e0 + N(0, 0.05^2); keys N(0, 1), except in a seeded subset of each
     segment's 64-key blocks (never the first), whose keys are -c e0 + N(0,
     0.05^2) with c set so that their scores sit at -4.5 log2 units.  The kept
     blocks' maxima are near +1.3, so with t = -3 the far blocks are skipped
     with a margin of ~3 and the others kept with a margin of ~4, while the
     skipped weight (2^-4.5 per key relative to the row max) is large enough to
-    see in the output."""
+    see in the output.  v_far: the far blocks' values are v_far + N(0, 0.05^2),
+    which makes the skipped weight move the output by far more than the FP8
+    path's rounding."""
     g = np.random.default_rng(seed)
     e0 = np.zeros(D, np.float32)
     e0[0] = 1.0
@@ -45,6 +47,8 @@ def _blocky(lengths, n_buf, H, D, far_frac, seed):
                 lo = cu[s] + 64 * b
                 hi = min(lo + 64, cu[s] + n)
                 k[lo:hi] = -c * e0 + 0.05 * g.standard_normal((hi - lo, H, D))
+                if v_far is not None:
+                    v[lo:hi] = v_far + 0.05 * g.standard_normal((hi - lo, H, D))
                 far_blocks += 1
     r = lambda a: W.round_to_bf16(a)
     return r(q), r(k), r(v), cu, np.asarray(lengths), far_blocks
@@ -104,5 +108,71 @@ def test_skip_10s_share_random_inputs_skip_nothing(lib):
     o2 = torch.empty_like(o1)
     lib.h3_varlen_attn(q, k, v, o1, hc, D, cu, vl, wl.n_valid)
     lib.h3_varlen_attn_skip(q, k, v, o2, hc, D, cu, vl, wl.n_valid, -20.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------ FP8 path
+
+# the FP8 attention bar against the quantized-operand oracle: the e4m3 rounding
+# of 256 p (up to 2^-4 relative per weight) leaves a few percent relative L2
+TOL_Q = dict(max_abs=6e-2, mean_abs=4e-3, rel_l2=6e-2)
+
+
+def _run8(lib, q, k, v, cu, vl, H, D, skip_log2):
+    n_buf = q.shape[0]
+    qd, kd, vd = (dev(a.reshape(n_buf, H * D), "bf16") for a in (q, k, v))
+    o = torch.full((n_buf, H * D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if skip_log2 is None:
+        lib.h3_varlen_attn_fp8(qd, kd, vd, o, H, D, dev_i32(cu), dev_i32(vl), int(vl.max()))
+    else:
+        lib.h3_varlen_attn_fp8_skip(qd, kd, vd, o, H, D, dev_i32(cu), dev_i32(vl), int(vl.max()),
+                                    skip_log2)
+    torch.cuda.synchronize()
+    return host(o).reshape(n_buf, H, D)
+
+
+@pytest.mark.parametrize("lengths,n_buf,H,D", [((700, 333, 64), 1200, 2, 128), ((500, 40), 640, 3, 64)])
+def test_fp8_skip_matches_oracle_rule(lib, lengths, n_buf, H, D):
+    """FP8 attention with the rule, against the oracle's FP8 attention with the
+    rule applied to the scores of its quantized operands (margins of >= 1.8
+    log2 units on those scores on these seeds).  The far blocks' values are
+    offset by 8, so dropping them moves the output by 0.07-0.28 on average,
+    far above the FP8 path's own rounding."""
+    q, k, v, cu, vl, far = _blocky(lengths, n_buf, H, D, 0.5, seed=3, v_far=8.0)
+    assert far > 0
+    got = _run8(lib, q, k, v, cu, vl, H, D, -3.0)
+    ref = O.varlen_attention_fp8_operands(q, k, v, cu, vl, skip_log2=-3.0)
+    plain = O.varlen_attention_fp8_operands(q, k, v, cu, vl)
+    valid = np.zeros(n_buf, bool)
+    for s in range(len(vl)):
+        valid[cu[s]:cu[s] + vl[s]] = True
+    assert_close(got[valid], ref[valid], "bf16", f"fp8 skip {lengths}", **TOL_Q)
+    assert np.all(got[~valid] == 0)
+    to_ref = np.abs(got[valid] - ref[valid]).mean()
+    to_plain = np.abs(got[valid] - plain[valid]).mean()
+    assert to_plain > 10 * to_ref, (to_ref, to_plain)
+
+
+@pytest.mark.parametrize("lengths,n_buf,H,D", [((700, 333, 64), 1200, 2, 128), ((500, 40), 640, 3, 64)])
+def test_fp8_skip_without_skips_is_the_fp8_kernel(lib, lengths, n_buf, H, D):
+    q, k, v, cu, vl, _ = _blocky(lengths, n_buf, H, D, 0.0, seed=4)
+    base = _run8(lib, q, k, v, cu, vl, H, D, None)
+    assert np.array_equal(_run8(lib, q, k, v, cu, vl, H, D, float("-inf")), base)
+    assert np.array_equal(_run8(lib, q, k, v, cu, vl, H, D, -30.0), base)
+
+
+def test_fp8_skip_10s_share_random_inputs_skip_nothing(lib):
+    wl = W.SHARE_10S
+    N, hc, D = wl.n_pad_total, wl.head_count, wl.head_dim
+    g = torch.Generator(device="cuda").manual_seed(6)
+    qa = torch.randn((N, 3 * hc * D), generator=g, device="cuda").to(torch.bfloat16)
+    q, k, v = qa[:, :hc * D], qa[:, hc * D:2 * hc * D], qa[:, 2 * hc * D:]
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    vl = torch.tensor([wl.n_valid], dtype=torch.int32, device="cuda")
+    o1 = torch.empty((N, hc * D), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    lib.h3_varlen_attn_fp8(q, k, v, o1, hc, D, cu, vl, wl.n_valid)
+    lib.h3_varlen_attn_fp8_skip(q, k, v, o2, hc, D, cu, vl, wl.n_valid, -20.0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
