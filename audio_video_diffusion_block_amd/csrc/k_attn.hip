@@ -934,10 +934,11 @@ __device__ __forceinline__ i32x8_t frag32(const uint8_t* p0, const uint8_t* p1) 
 }
 }  // namespace
 
-// SKIP (Skip-Softmax): as in the bf16 kernel, a wave leaves out the softmax
-// slots and the P.V and row-sum MFMAs of a key tile when every valid row's
-// tile max is more than |skip_log2| below its exact running max.  Here the
-// softmax is most of the VALU work, so the skipped slots are branched around.
+// SKIP (Skip-Softmax): as in the bf16 kernel, a wave gives a key tile zero
+// weight when every valid row's tile max is more than |skip_log2| below its
+// exact running max.  Here the softmax is most of the VALU work, so a skipped
+// tile branches around its softmax slots; its packed P is zeroed instead, and
+// its P.V and row-sum MFMAs then add exact zeros (no branch in phase B).
 template <int D, int NW, bool SKIP = false>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qs,
@@ -1160,6 +1161,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
     i32x8_t kf = kfrag(sk, 0, 0);
     nxt[0] = negm;
     nxt[1] = negm;
+    if constexpr (SKIP) {
+      // a skipped tile's P.V and row sums then add exact zeros
+      if (skip)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pw[w] = 0;
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int kb = i & 1, t = i >> 1;
@@ -1180,6 +1187,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
         // the first conversion's upper half is overwritten by the second
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pw[word], false);
         pw[word] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], lo, true);
+        // keep this slice next to its MFMA (no sinking past the mask branch)
+        asm volatile("" ::"v"(pw[word]));
       }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1203,13 +1212,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       vf[db] = vfrag(sv, db);
       vsc[db] = vscale(sv, db);
     }
-    // a skipped tile issues no MFMA here, so the row max below would read
-    // S(next) right behind phase A's last scaled MFMA: wait it out
-    if (SKIP && skip) scaled_mfma_drain();
-    if (!(SKIP && skip)) lacc = mfma_e4m3<0>(ones8, pw, lacc, 127u, PSC);
+    lacc = mfma_e4m3<0>(ones8, pw, lacc, 127u, PSC);
 #pragma unroll
     for (int db = 0; db < NBM; ++db) {
-      if (!(SKIP && skip)) oacc[db] = mfma_e4m3<0>(vf[db], pw, oacc[db], vsc[db], PSC);
+      oacc[db] = mfma_e4m3<0>(vf[db], pw, oacc[db], vsc[db], PSC);
 #pragma unroll
       for (int e = 0; e < 32 / NBM; ++e) {
         const int idx = db * (32 / NBM) + e;
