@@ -118,6 +118,7 @@ _c_attn_skip = _sig("h3_varlen_attn_skip", ctypes.c_int,
 _c_attn8_skip = _sig("h3_varlen_attn_fp8_skip", ctypes.c_int,
                      [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32,
                       _f, _f, _p, _sz, _i32, _p])
+_c_mfma_probe = _sig("h3_mfma_rate_probe", ctypes.c_int, [_i32, _i32, _p, _i64, _p])
 _c_mxq = _sig("h3_mx_quantize", ctypes.c_int,
               [_p, _i64, _i64, _i32, _p, _i64, _p, _i64, _i32, _p])
 _c_lin8 = _sig("h3_linear_fp8", ctypes.c_int,
@@ -133,7 +134,8 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_dit_block_forward", "h3_timestep_workspace_size", "h3_timestep_modulation",
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
-            "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip")
+            "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip",
+            "h3_mfma_rate_probe")
 
 
 def _status_string(st: int) -> str:
@@ -444,3 +446,12 @@ def h3_frames_to_u8(frames, out, layout: int = 0, stream=None):
     if tuple(out.shape) != want:
         raise ValueError(f"out must have shape {want}")
     _check(_c_frames(_ptr(frames), B, T, H, W, _ptr(out), layout, _stream(stream)))
+
+
+def h3_mfma_rate_probe(out: torch.Tensor, iters: int, zero_operands: bool = False,
+                       stream=None) -> float:
+    """Launch the matrix-core rate probe into `out` (float32, a multiple of 512
+    elements: one 8-wave work-group per 512); returns the flop it performs."""
+    assert out.dtype == torch.float32 and out.is_contiguous()
+    _check(_c_mfma_probe(iters, int(bool(zero_operands)), _ptr(out), out.numel(), _stream(stream)))
+    return (out.numel() // 64) * iters * 4 * 32768.0

@@ -891,4 +891,18 @@ h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, i
                     "frames launch");
 }
 
+h3_status h3_mfma_rate_probe(int32_t iters, int32_t zero_operands, float* out, int64_t out_len,
+                             void* stream) {
+  g_err[0] = 0;
+  CHECK(iters >= 1 && iters <= 10000000, "iters must be in [1, 10^7]");
+  CHECK(zero_operands == 0 || zero_operands == 1, "zero_operands must be 0 or 1");
+  CHECK(out_len > 0 && out_len % 512 == 0 && out_len / 512 <= 65535,
+        "out_len must be a positive multiple of 512, at most 65535 * 512");
+  CHECK(out && aligned16(out), "out must be non-NULL, 16-byte aligned");
+  TRY(check_device());
+  return hip_status(launch_mfma_rate((int)(out_len / 512), iters, zero_operands, out,
+                                     (hipStream_t)stream),
+                    "mfma rate launch");
+}
+
 }  // extern "C"

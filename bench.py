@@ -117,6 +117,23 @@ class EventTimer:
         return s.elapsed_time(e) / reps  # ms per call
 
 
+def mfma_ceiling(h3, timer):
+    """bf16 matrix-core rate with no memory traffic (h3_mfma_rate_probe), one
+    8-wave work-group per CU as the attention kernel runs, for random and for
+    zero operands: the chip's clock, and so this rate, falls with operand
+    switching activity."""
+    import torch
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(n_cu * 512, dtype=torch.float32, device="cuda")
+    res = {}
+    for zero in (False, True):
+        h3.h3_mfma_rate_probe(out, 1000, zero)                     # warm
+        flop = h3.h3_mfma_rate_probe(out, 40000, zero)
+        ms = timer.time(lambda: h3.h3_mfma_rate_probe(out, 40000, zero), 3)
+        res["zero" if zero else "random"] = flop / ms / 1e9
+    return res
+
+
 def traffic_record():
     """HBM bytes per attention launch from committed rocprof counters, if they were
     taken on the current attention source."""
@@ -551,6 +568,12 @@ def main():
                 "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "attn_fwd_bf16_pipe_kernel<128,8> (+ V transpose pass)",
                 "algorithmic_flop_per_launch": work["attn_flop"]}
+    ceil = mfma_ceiling(h3, timer)
+    mfma_ceiling_rec = {"bf16_random_operands_tflops": ceil["random"], "bf16_zero_operands_tflops": ceil["zero"],
+                        "attention_frac_of_random": attn_tflops / ceil["random"],
+                        "note": "h3_mfma_rate_probe: 8 waves per CU, four 32x32x16 bf16 MFMAs per round, no "
+                                "memory traffic; the published peak assumes 2.4 GHz, which the chip does not "
+                                "hold under switching operands"}
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -563,7 +586,7 @@ def main():
                    "ffn_dim": wl.ffn_dim, "head_slice": hc, "parallelism": "1 GPU (rank-share stand-in)"},
         "block_ms": step_ms, "attn_tflops": attn_tflops,
         "fused_op_gbps": {k: breakdown[k]["GB/s"] for k in ("modnorm", "qk_norm_rope", "frames_u8")},
-        "breakdown": breakdown, "roofline": roofline,
+        "breakdown": breakdown, "roofline": roofline, "mfma_ceiling": mfma_ceiling_rec,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, w, bi, work)

@@ -441,6 +441,24 @@ h3_status h3_euler_update(void* z, const void* u, void* x_next, int64_t n, float
 h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, int64_t W,
                           void* out, int32_t layout, void* stream);
 
+/* ------------------------------------------------------- measurement aid */
+
+/*
+ * h3_mfma_rate_probe -- not a step of the method: the bf16 matrix-core rate
+ * the chip sustains with no memory traffic, for reading the attention and
+ * GEMM rates against.  Launches out_len / 512 work-groups of 8 waves (one per
+ * CU is the attention kernel's occupancy); each wave runs `iters` rounds of
+ * four independent 32x32x16 bf16 MFMAs, so the launch does
+ * (out_len / 64) * iters * 4 * 32768 flop.  zero_operands = 1 multiplies
+ * zeros (least switching), 0 fixed pseudo-random values in [-2, 2).
+ *   out: device float [out_len], out_len a positive multiple of 512 and at
+ *        most 65535 * 512; receives per-lane sums (their values carry no meaning).
+ *   iters in [1, 10^7].  The caller times the launch on `stream`.
+ *   Errors: H3_ERR_ARG on a bad size or pointer (nothing launched).
+ */
+h3_status h3_mfma_rate_probe(int32_t iters, int32_t zero_operands, float* out, int64_t out_len,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

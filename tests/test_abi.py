@@ -291,3 +291,12 @@ def test_fp8_skip_softmax_argument_checks():
     assert h3._c_attn8_skip(*args(0.0, h3.H3_BF16)) == h3.H3_ERR_ARG
     assert "negative" in h3.last_error()
     assert h3._c_attn8_skip(*args(float("nan"), h3.H3_BF16)) == h3.H3_ERR_ARG
+
+
+def test_mfma_rate_probe_argument_checks():
+    import audio_video_diffusion_block_amd as h3
+    assert h3._c_mfma_probe(0, 0, FAKE, 512, None) == h3.H3_ERR_ARG
+    assert h3._c_mfma_probe(10, 2, FAKE, 512, None) == h3.H3_ERR_ARG
+    assert h3._c_mfma_probe(10, 0, FAKE, 500, None) == h3.H3_ERR_ARG
+    assert h3._c_mfma_probe(10, 0, FAKE, 512 * 65536, None) == h3.H3_ERR_ARG
+    assert h3._c_mfma_probe(10, 0, None, 512, None) == h3.H3_ERR_ARG

@@ -201,3 +201,16 @@ def test_varlen_attention_edge_segments(lib):
     assert_close(got, ref, "bf16", "attn edges")
     assert np.all(got[0:10] == 0)
     assert np.allclose(got[10], v[10], atol=0)  # one-row segment: o = v exactly (p = 1)
+
+
+def test_mfma_rate_probe_runs(lib):
+    """The measurement probe: zero operands give zero sums, random ones finite
+    sums; the flop count follows the launch shape."""
+    out = torch.full((2 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    flop = lib.h3_mfma_rate_probe(out, 10, zero_operands=True)
+    torch.cuda.synchronize()
+    assert flop == 16 * 10 * 4 * 32768.0
+    assert torch.all(out == 0)
+    lib.h3_mfma_rate_probe(out, 10, zero_operands=False)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out)) and torch.any(out != 0)
