@@ -176,3 +176,33 @@ def test_fp8_skip_10s_share_random_inputs_skip_nothing(lib):
     lib.h3_varlen_attn_fp8_skip(q, k, v, o2, hc, D, cu, vl, wl.n_valid, -20.0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("D,seed", [(128, 7), (64, 8)])
+def test_skip_edge_segments(lib, D, seed, fp8):
+    """Segments of 65 (a one-key tail block), 0, 1, 129 and 300 keys with 70% far
+    blocks: on these seeds the rule skips 66 (D = 128) and 106 (D = 64) group
+    blocks with margins >= 1.9 log2 units below the threshold and keeps the rest
+    >= 1.08 above it, on exact and on FP8-quantized scores."""
+    lengths, n_buf, H = (65, 0, 1, 129, 300), 720, 2
+    q, k, v, cu, vl, far = _blocky(lengths, n_buf, H, D, 0.7, seed=seed, v_far=8.0)
+    assert far > 0
+    valid = np.zeros(n_buf, bool)
+    for s in range(len(vl)):
+        valid[cu[s]:cu[s] + vl[s]] = True
+    if fp8:
+        got = _run8(lib, q, k, v, cu, vl, H, D, -3.0)
+        ref = O.varlen_attention_fp8_operands(q, k, v, cu, vl, skip_log2=-3.0)
+        plain = O.varlen_attention_fp8_operands(q, k, v, cu, vl)
+        assert_close(got[valid], ref[valid], "bf16", f"fp8 skip edges D={D}", **TOL_Q)
+    else:
+        got = _run(lib, q, k, v, cu, vl, H, D, -3.0)
+        ref = O.varlen_attention_skip(q, k, v, cu, vl, -3.0)
+        plain = O.varlen_attention(q, k, v, cu, vl)
+        assert_close(got[valid], ref[valid], "bf16", f"skip edges D={D}")
+    assert np.all(got[~valid] == 0)
+    # the length-1 segment attends to itself only: its row is its (quantized) value, exactly
+    one = cu[2]
+    np.testing.assert_array_equal(got[one], W.round_to_bf16(ref[one].astype(np.float32)))
+    assert np.abs(got[valid] - plain[valid]).mean() > 10 * np.abs(got[valid] - ref[valid]).mean()
