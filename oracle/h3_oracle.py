@@ -488,8 +488,8 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, ski
     query rows q_rows (buffer rows).  Q is quantized after folding scale * log2(e); the scores are then
     in log2 units, and softmax uses base 2.  The FP8 kernel differs from this
     only by rounding 256 * p to e4m3 and by fp32 accumulation.
-    skip_log2: apply the Skip-Softmax rule (skip_softmax_rows) to the scores
-    of the quantized operands; q must then hold every buffer row."""
+    skip_log2: apply the Skip-Softmax rule to the scores of the quantized
+    operands; q_rows must then be whole query groups of each segment."""
     q = np.asarray(q, dtype=np.float32)
     D = q.shape[-1]
     c = float(fp8_fold(D))
@@ -515,6 +515,11 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, ski
         vdq[lo:lo + n] = mx_dequantize(vq, ve).transpose(2, 0, 1)[:n]
     qd = mx_dequantize(*mx_quantize(qsel, fold=c))
     kd = mx_dequantize(kq, ke)
+    if skip_log2 is not None:
+        # the scores qd.kd are already in log2 units: scale 1/log2(e) cancels
+        # the log2(e) the Skip-Softmax oracle applies
+        return varlen_attention_skip(qd, kd, vdq, cu, vl, skip_log2, scale=1.0 / np.log2(np.e),
+                                     q_rows=None if q_rows is None else rows)
     out = np.zeros((len(rows), h, D))
     for s in range(len(cu) - 1):
         lo, n = int(cu[s]), int(vl[s])
@@ -523,10 +528,6 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, ski
             continue
         for hh in range(h):
             sc = qd[sel, hh] @ kd[lo:lo + n, hh].T                  # log2 units
-            if skip_log2 is not None:
-                assert sel.size == n and np.all(rows[sel] == np.arange(lo, lo + n))
-                out[sel, hh] = skip_softmax_rows(sc, vdq[lo:lo + n, hh], skip_log2)
-                continue
             sc -= sc.max(axis=1, keepdims=True)
             p = np.exp2(sc)
             out[sel, hh] = (p @ vdq[lo:lo + n, hh]) / p.sum(axis=1, keepdims=True)
@@ -568,13 +569,16 @@ def linear_fp8_operands(x, w) -> np.ndarray:
 # skipped key's weight is at most 2^t times the row's largest weight.
 
 def skip_softmax_rows(sc, v, skip_log2: float, q_group: int = 32, k_block: int = 64) -> np.ndarray:
-    """One segment and head under the rule above: sc [n, n] scores in log2
-    units (query row i of the segment against key j), v [n, D].  Returns the
-    n output rows, each a base-2 softmax over the keys its group keeps."""
-    n = sc.shape[0]
-    out = np.zeros((n, v.shape[1]))
-    for g0 in range(0, n, q_group):
-        rows = slice(g0, min(g0 + q_group, n))
+    """Query rows of one segment and head under the rule above: sc [r, n]
+    scores in log2 units of r consecutive query rows against the segment's n
+    keys, v [n, D].  The rows start at a multiple of q_group from the segment
+    start and hold whole groups (the segment's last group may be shorter).
+    Returns the r output rows, each a base-2 softmax over the keys its group
+    keeps."""
+    r, n = sc.shape
+    out = np.zeros((r, v.shape[1]))
+    for g0 in range(0, r, q_group):
+        rows = slice(g0, min(g0 + q_group, r))
         keep = np.zeros(n, dtype=bool)
         m_run = None
         for b0 in range(0, n, k_block):
@@ -592,23 +596,40 @@ def skip_softmax_rows(sc, v, skip_log2: float, q_group: int = 32, k_block: int =
 
 def varlen_attention_skip(q, k, v, cu_slots, valid_len, skip_log2: float,
                           scale: Optional[float] = None, q_group: int = 32,
-                          k_block: int = 64) -> np.ndarray:
-    """Attention with the Skip-Softmax rule above; q, k, v [n_buf, H, D].
+                          k_block: int = 64, q_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Attention with the Skip-Softmax rule above; k, v [n_buf, H, D].
     Returns [n_buf, H, D] (rows outside every segment are 0) and applies the
-    rule exactly in float64: a block is skipped or kept whole."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    rule exactly in float64: a block is skipped or kept whole.
+    q_rows: if given, q holds only those buffer rows, in increasing order, and
+    the result has q's shape; within each segment they must be whole query
+    groups (the rule is decided per group)."""
+    k, v = _f64(k), _f64(v)
     n_buf, h, d = k.shape
+    rows = np.arange(n_buf) if q_rows is None else np.asarray(q_rows)
+    q = _f64(q)
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     c = scale * np.log2(np.e)
-    out = np.zeros((n_buf, h, d))
+    out = np.zeros((len(rows), h, d))
     cu = np.asarray(cu_slots)
     vl = np.asarray(valid_len) if valid_len is not None else np.diff(cu)
     for s in range(len(cu) - 1):
         lo, n = int(cu[s]), int(vl[s])
         if n == 0:
             continue
-        for head in range(h):
-            sc = (q[lo:lo + n, head] @ k[lo:lo + n, head].T) * c   # log2 units
-            out[lo:lo + n, head] = skip_softmax_rows(sc, v[lo:lo + n, head], skip_log2, q_group, k_block)
+        sel = np.nonzero((rows >= lo) & (rows < lo + n))[0]
+        if sel.size == 0:
+            continue
+        rel = rows[sel] - lo
+        # whole groups, in order: each run starts at a group boundary and is
+        # contiguous up to its group's end (or the segment's end)
+        starts = np.nonzero(np.diff(np.concatenate([[-2], rel])) != 1)[0]
+        ends = np.concatenate([starts[1:], [len(rel)]])
+        for a, b in zip(starts, ends):
+            end = int(rel[b - 1]) + 1
+            assert int(rel[a]) % q_group == 0 and (end % q_group == 0 or end == n), \
+                "q_rows must be whole query groups"
+            for head in range(h):
+                sc = (q[sel[a:b], head] @ k[lo:lo + n, head].T) * c   # log2 units
+                out[sel[a:b], head] = skip_softmax_rows(sc, v[lo:lo + n, head], skip_log2, q_group, k_block)
     return out

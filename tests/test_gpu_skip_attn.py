@@ -206,3 +206,94 @@ def test_skip_edge_segments(lib, D, seed, fp8):
     one = cu[2]
     np.testing.assert_array_equal(got[one], W.round_to_bf16(ref[one].astype(np.float32)))
     assert np.abs(got[valid] - plain[valid]).mean() > 10 * np.abs(got[valid] - ref[valid]).mean()
+
+
+# ------------------------------------------------ full size, sampled groups
+
+def _concentrated_10s(seed=11, v_far=8.0):
+    """The 10 s share's head slice with concentrated attention: q = 4 e0 +
+    N(0, 0.05^2); keys N(0, 1) except in 75% of the 64-key blocks after the
+    first, whose keys are -c e0 + N(0, 0.05^2) (scores near -4.5 log2 units)
+    and whose values are v_far + N(0, 0.05^2).  Device bf16 [N, 5 * 128]."""
+    wl = W.SHARE_10S
+    N, hc, D = wl.n_pad_total, wl.head_count, wl.head_dim
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn((N, hc, D), generator=g, device="cuda") * 0.05
+    q[:, :, 0] += 4.0
+    k = torch.randn((N, hc, D), generator=g, device="cuda")
+    v = torch.randn((N, hc, D), generator=g, device="cuda")
+    far = torch.rand((N + 63) // 64, generator=g, device="cuda") < 0.75
+    far[0] = False
+    rows = far.repeat_interleave(64)[:N]
+    nf = int(rows.sum())
+    k[rows] = torch.randn((nf, hc, D), generator=g, device="cuda") * 0.05
+    k[rows, :, 0] -= 4.5 / (4.0 * np.log2(np.e) / np.sqrt(D))
+    v[rows] = v_far + torch.randn((nf, hc, D), generator=g, device="cuda") * 0.05
+    bf = torch.bfloat16
+    return wl, (q.reshape(N, -1).to(bf), k.reshape(N, -1).to(bf), v.reshape(N, -1).to(bf))
+
+
+def _min_margin(sc, t, q_group=32, k_block=64):
+    """Smallest distance (log2 units) between a group's decision statistic
+    max_row(block max - running max) and the threshold t, over the blocks
+    after the first, following the decisions as they fall."""
+    r, n = sc.shape
+    best = np.inf
+    for g0 in range(0, r, q_group):
+        rows = sc[g0:g0 + q_group]
+        m = rows[:, :k_block].max(axis=1)
+        for b0 in range(k_block, n, k_block):
+            bm = rows[:, b0:b0 + k_block].max(axis=1)
+            d = (bm - m - t).max()
+            best = min(best, abs(d))
+            if d >= 0:
+                m = np.maximum(m, bm)
+    return best
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_skip_10s_share_concentrated_sampled(lib, fp8):
+    """Full size, in the bench's launch configuration: the concentrated operands
+    of breakdown.attention_skip with t = -3, three sampled query groups (the
+    first, one in the middle and the shorter last one) against the oracle's
+    rule, whose decisions on these rows are checked to lie >= 0.3 log2 units
+    from the threshold."""
+    wl, (qd, kd, vd) = _concentrated_10s()
+    N, hc, D, nv = wl.n_pad_total, wl.head_count, wl.head_dim, wl.n_valid
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    vl = torch.tensor([nv], dtype=torch.int32, device="cuda")
+    o = torch.full_like(qd, float("nan"))
+    t = -3.0
+    if fp8:
+        lib.h3_varlen_attn_fp8_skip(qd, kd, vd, o, hc, D, cu, vl, nv, t)
+    else:
+        lib.h3_varlen_attn_skip(qd, kd, vd, o, hc, D, cu, vl, nv, t)
+    torch.cuda.synchronize()
+    last = (nv // 32) * 32
+    rows = np.r_[0:32, 123008:123040, last:nv]
+    ridx = torch.from_numpy(rows).cuda()
+    got = host(o[ridx]).reshape(len(rows), hc, D)
+    h = lambda x: x.float().cpu().numpy().reshape(N, hc, D)
+    k, v = h(kd), h(vd)
+    q = qd[ridx].float().cpu().numpy().reshape(len(rows), hc, D)
+    cu_h, vl_h = np.array([0, N]), np.array([nv])
+    if fp8:
+        c = O.fp8_fold(D)
+        qq = O.mx_dequantize(*O.mx_quantize(q, fold=c))
+        kq = O.mx_dequantize(*O.mx_quantize(k[:nv]))
+        margins = [_min_margin(qq[a:b, hh] @ kq[:, hh].T, t)
+                   for a, b in ((0, 32), (32, 64), (64, len(rows))) for hh in range(hc)]
+        ref = O.varlen_attention_fp8_operands(q, k, v, cu_h, vl_h, q_rows=rows, skip_log2=t)
+        plain = O.varlen_attention_fp8_operands(q, k, v, cu_h, vl_h, q_rows=rows)
+        assert min(margins) >= 0.3, margins
+        assert_close(got, ref, "bf16", "fp8 skip 10s sampled", **TOL_Q)
+    else:
+        cl = np.log2(np.e) / np.sqrt(D)
+        margins = [_min_margin((q[a:b, hh].astype(np.float64) @ k[:nv, hh].T.astype(np.float64)) * cl, t)
+                   for a, b in ((0, 32), (32, 64), (64, len(rows))) for hh in range(hc)]
+        ref = O.varlen_attention_skip(q, k, v, cu_h, vl_h, t, q_rows=rows)
+        plain = O.varlen_attention(q, k, v, cu_h, vl_h, q_rows=rows)
+        assert min(margins) >= 0.3, margins
+        assert_close(got, ref, "bf16", "skip 10s sampled")
+    # the skips were taken: far from attention without the rule
+    assert np.abs(got - plain).mean() > 10 * np.abs(got - ref).mean()

@@ -864,3 +864,15 @@ def test_fp8_skip_softmax_on_grid_operands_is_the_skip_rule():
     assert np.abs(got - plain).max() > 1e-6          # the far blocks were dropped
     np.testing.assert_allclose(O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-1e9),
                                plain, rtol=0, atol=1e-12)
+
+
+def test_skip_softmax_sampled_groups_equal_the_full_result():
+    q, k, v = _blocky_case(n=400)
+    k[64:128, :, 0] += 38.0            # far blocks near -12 log2 units, skipped at t = -6
+    cu, vl = np.array([0, 400]), np.array([400])
+    full = O.varlen_attention_skip(q, k, v, cu, vl, -6.0)
+    rows = np.r_[32:96, 384:400]        # groups 1-2 and the last, shorter group
+    part = O.varlen_attention_skip(q[rows], k, v, cu, vl, -6.0, q_rows=rows)
+    np.testing.assert_allclose(part, full[rows], rtol=0, atol=1e-13)
+    with pytest.raises(AssertionError):
+        O.varlen_attention_skip(q[40:60], k, v, cu, vl, -6.0, q_rows=np.arange(40, 60))
