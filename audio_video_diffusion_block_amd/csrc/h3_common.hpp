@@ -44,6 +44,22 @@ struct Vec8<float> {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }
+  // streaming forms: non-temporal hint, for data touched once per pass
+  __device__ __forceinline__ static void load_nt(const float* p, float (&v)[8]) {
+    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+  __device__ __forceinline__ static void store_nt(float* p, const float (&v)[8]) {
+    const f32x4_t a = {v[0], v[1], v[2], v[3]};
+    const f32x4_t b = {v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(p + 4));
+  }
 };
 
 template <>
@@ -64,6 +80,19 @@ struct Vec8<bf16_t> {
     a.z = pack_bf16x2(v[4], v[5]);
     a.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = a;
+  }
+  __device__ __forceinline__ static void load_nt(const bf16_t* p, float (&v)[8]) {
+    const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(a[i] << 16);
+      v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ __forceinline__ static void store_nt(bf16_t* p, const float (&v)[8]) {
+    const u32x4_t a = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(p));
   }
 };
 

@@ -10,7 +10,8 @@
 // the D/8 lanes with DPP.  A lane always owns the same 4 RoPE pairs; it derives
 // their inverse frequencies once and recomputes cos/sin only when its token
 // changes (each work-group walks a contiguous run of rows, so that happens
-// every 2H/(256/(D/8)) rows).
+// every 2H/(256/(D/8)) rows).  Row loads and stores carry the non-temporal
+// hint (each byte is read and written once).
 #include "h3_common.hpp"
 #include "h3_kernels.hpp"
 
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     if (kind != 0 && kind != 1) continue;  // pad row: untouched
     T* ptr = (is_k ? k + tok * ld_k : q + tok * ld_q) + (int64_t)head * D + 8 * lane;
     float v[8];
-    Vec8<T>::load(ptr, v);
+    Vec8<T>::load_nt(ptr, v);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
       v[2 * j] = a * cs[j] - b * sn[j];
       v[2 * j + 1] = a * sn[j] + b * cs[j];
     }
-    Vec8<T>::store(ptr, v);
+    Vec8<T>::store_nt(ptr, v);
   }
 }
 

@@ -105,10 +105,12 @@ class EventTimer:
         self.torch = torch
         self.stream = stream
 
-    def time(self, fn, reps):
+    def time(self, fn, reps, warm=0):
         torch = self.torch
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
+        for _ in range(warm):
+            fn()
         s.record(self.stream)
         for _ in range(reps):
             fn()
@@ -132,6 +134,24 @@ def mfma_ceiling(h3, timer):
         ms = timer.time(lambda: h3.h3_mfma_rate_probe(out, 40000, zero), 3)
         res["zero" if zero else "random"] = flop / ms / 1e9
     return res
+
+
+def hbm_ceiling(h3, timer, n_rows, row_bytes, touch_bytes):
+    """HBM rates of the elementwise passes' two access patterns (h3_hbm_rate_probe):
+    a 1 GiB copy, and read-modify-write in place of the first `touch_bytes` of
+    each of `n_rows` rows of `row_bytes` (the q and k thirds of the QKV buffer,
+    the Q/K norm + RoPE pattern)."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    nb = h3.h3_hbm_rate_probe(b, a)
+    copy_ms = timer.time(lambda: h3.h3_hbm_rate_probe(b, a), 20, warm=2)
+    del a, b
+    buf = torch.zeros(n_rows * row_bytes, dtype=torch.uint8, device="cuda")
+    nr = h3.h3_hbm_rate_probe(buf, row_chunks=row_bytes // 16, touch_chunks=touch_bytes // 16)
+    rmw_ms = timer.time(lambda: h3.h3_hbm_rate_probe(buf, row_chunks=row_bytes // 16,
+                                                     touch_chunks=touch_bytes // 16), 20, warm=2)
+    return {"copy": nb / copy_ms / 1e6, "qk_rmw": nr / rmw_ms / 1e6}
 
 
 def traffic_record():
@@ -405,16 +425,17 @@ def main():
 
     # ---- per-step breakdown: each C entry alone, HIP events on the launch stream
     reps = args.op_reps
+    reps_short = max(reps, 20)  # sub-millisecond passes: more calls per event pair
     h1 = torch.empty((wl.n_loc, C), dtype=bf, device="cuda")
     qkv = torch.empty((wl.n_loc, 3 * H * D), dtype=bf, device="cuda")
     xs = x0.clone()
     ops = {}
     ops["modnorm"] = timer.time(lambda: h3.h3_modulate_residual(
-        xs, shift=mod[:, 0], scale=mod[:, 1], h_out=h1), reps)
+        xs, shift=mod[:, 0], scale=mod[:, 1], h_out=h1), reps_short, warm=1)
     ops["qkv_gemm"] = timer.time(lambda: h3.h3_linear(h1, wd["w_qkv"], qkv), reps)
     ops["qk_norm_rope"] = timer.time(lambda: h3.h3_qk_norm_rope(
         qkv[:, :H * D], qkv[:, H * D:2 * H * D], H, D, wd["g_q"], wd["g_k"], pos, wl.sections,
-        wl.theta, wl.eps_qk), reps)
+        wl.theta, wl.eps_qk), reps_short, warm=1)
     ops["attention"] = timer.time(attn, reps)
     # the MX-scaled e4m3 attention on the same operands, with its own workspace
     ws8 = torch.empty(max(h3.varlen_attn_fp8_workspace_size(n_buf, hc, D, 1), 16),
@@ -473,7 +494,7 @@ def main():
     # FP8 projections on MX operands: weights quantized once, activations on the fly
     wmx = h3.block_weights_mx(wd)
     h1m = h3.h3_mx_quantize(h1)
-    ops["act_quant"] = timer.time(lambda: h3.h3_mx_quantize(h1, h1m), reps)
+    ops["act_quant"] = timer.time(lambda: h3.h3_mx_quantize(h1, h1m), reps_short, warm=1)
     ops["qkv_gemm_fp8"] = timer.time(lambda: h3.h3_linear_fp8(h1m, wmx[0], qkv), reps)
     om = h3.h3_mx_quantize(o_in)
     ops["out_gemm_residual_fp8"] = timer.time(lambda: h3.h3_linear_fp8(om, wmx[1], xs, gate=mod[:, 2]), reps)
@@ -498,7 +519,7 @@ def main():
     fr = W.FRAMES_10S
     frames = torch.rand((fr["B"], 3, fr["T"], fr["H"], fr["W"]), device="cuda") * 2.1 - 1.05
     fout = torch.empty((fr["B"], fr["T"], fr["H"], fr["W"], 3), dtype=torch.uint8, device="cuda")
-    ops["frames_u8"] = timer.time(lambda: h3.h3_frames_to_u8(frames, fout, 0), reps)
+    ops["frames_u8"] = timer.time(lambda: h3.h3_frames_to_u8(frames, fout, 0), reps_short, warm=1)
     frames_bytes = frames.numel() * 5  # 4 bytes read + 1 byte written per value
     del frames, fout
     torch.cuda.synchronize()
@@ -575,6 +596,16 @@ def main():
                                 "memory traffic; the published peak assumes 2.4 GHz, which the chip does not "
                                 "hold under switching operands"}
 
+    hbm = hbm_ceiling(h3, timer, wl.n_loc, 3 * H * D * 2, 2 * H * D * 2)
+    hbm_ceiling_rec = {
+        "copy_gbps": hbm["copy"], "qk_inplace_rmw_gbps": hbm["qk_rmw"],
+        "modnorm_frac_of_copy": breakdown["modnorm"]["GB/s"] / hbm["copy"],
+        "frames_u8_frac_of_copy": breakdown["frames_u8"]["GB/s"] / hbm["copy"],
+        "qk_norm_rope_frac_of_inplace_rmw": breakdown["qk_norm_rope"]["GB/s"] / hbm["qk_rmw"],
+        "note": "h3_hbm_rate_probe: 1 GiB copy with non-temporal accesses, and read-modify-write in place "
+                "of the q and k thirds of a bf16 [n_loc, 3, H, D] buffer (the Q/K norm + RoPE pattern); "
+                "bytes = read + written"}
+
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
@@ -587,6 +618,7 @@ def main():
         "block_ms": step_ms, "attn_tflops": attn_tflops,
         "fused_op_gbps": {k: breakdown[k]["GB/s"] for k in ("modnorm", "qk_norm_rope", "frames_u8")},
         "breakdown": breakdown, "roofline": roofline, "mfma_ceiling": mfma_ceiling_rec,
+        "hbm_ceiling": hbm_ceiling_rec,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, w, bi, work)

@@ -214,3 +214,22 @@ def test_mfma_rate_probe_runs(lib):
     lib.h3_mfma_rate_probe(out, 10, zero_operands=False)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out)) and torch.any(out != 0)
+
+
+def test_hbm_rate_probe_runs(lib):
+    """The HBM probe copies exactly, and its in-place form increments the first
+    32-bit word of each touched chunk and nothing else (ragged grid: 37 rows)."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    src = torch.randint(0, 2**31 - 1, (1000 * 4 + 4,), generator=g, dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    assert lib.h3_hbm_rate_probe(dst, src) == 2.0 * src.numel() * 4
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    rows, row, touch = 37, 30, 20
+    buf0 = torch.randint(0, 2**30, (rows * row * 4,), generator=g, dtype=torch.int32, device="cuda")
+    buf = buf0.clone()
+    assert lib.h3_hbm_rate_probe(buf, row_chunks=row, touch_chunks=touch) == 2.0 * 16 * rows * touch
+    torch.cuda.synchronize()
+    want = buf0.view(rows, row, 4).clone()
+    want[:, :touch, 0] += 1
+    assert torch.equal(buf.view(rows, row, 4), want)
