@@ -7,17 +7,20 @@
 // HBM-bound pass.  A head row (D values) is owned by D/8 adjacent lanes, 8
 // values (16 bytes of bf16) per lane, so four consecutive head rows of a token
 // are one contiguous 1 KiB wave access.  The sum of squares is reduced across
-// the D/8 lanes with DPP.  A lane always owns the same 4 RoPE pairs; it derives
-// their inverse frequencies once and recomputes cos/sin only when its token
-// changes (each work-group walks a contiguous run of rows, so that happens
-// every 2H/(256/(D/8)) rows).  Row loads and stores carry the non-temporal
-// hint (each byte is read and written once).
+// the D/8 lanes with DPP.  A lane always owns the same 4 RoPE pairs; the
+// work-group derives the pairs' inverse frequencies once, and a lane
+// recomputes cos/sin only when its token changes (each work-group walks a
+// contiguous run of rows, so that happens every 2H/(256/(D/8)) rows).  A lane
+// takes U rows per step (SLOTS rows apart) and issues their loads before
+// processing the first; loads and stores carry the non-temporal hint.  On a
+// [n, 3, H, D] bf16 buffer this runs at the rate of a plain in-place
+// read-modify-write of the same q and k regions.
 #include "h3_common.hpp"
 #include "h3_kernels.hpp"
 
 namespace h3 {
 
-template <typename T, int D>
+template <typename T, int D, int U>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     T* __restrict__ q, int64_t ld_q, T* __restrict__ k, int64_t ld_k, int64_t n_tok, int n_heads,
     const T* __restrict__ g_q, const T* __restrict__ g_k, const int4* __restrict__ pos, int sec_t,
@@ -27,24 +30,40 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   const int lane = threadIdx.x % L;
   const int slot = threadIdx.x / L;
 
-  // this lane's 4 pairs are pair indices 4*lane .. 4*lane+3 (dims 8*lane .. 8*lane+7)
+  // Inverse frequency of every rotation pair, in double and rounded once to
+  // float, computed once per work-group (one thread per pair) and shared
+  // through LDS.  This lane's 4 pairs are 4*lane .. 4*lane+3 (dims 8*lane ..
+  // 8*lane+7).
+  __shared__ float f_tab[2][D / 2];  // [0] video (per-axis sections), [1] audio
+  auto axis_of = [&](int p, int& jj, int& width) {
+    if (p < sec_t / 2) {
+      jj = p; width = sec_t;
+      return 0;
+    }
+    if (p < (sec_t + sec_h) / 2) {
+      jj = p - sec_t / 2; width = sec_h;
+      return 1;
+    }
+    jj = p - (sec_t + sec_h) / 2; width = D - sec_t - sec_h;
+    return 2;
+  };
+  if (threadIdx.x < D / 2) {
+    const int p = threadIdx.x;
+    int jj, width;
+    axis_of(p, jj, width);
+    f_tab[0][p] = (float)exp2(-2.0 * jj / width * log2_theta);
+    f_tab[1][p] = (float)exp2(-2.0 * p / D * log2_theta);
+  }
+  __syncthreads();
   float f_vid[4], f_aud[4];
   int axis[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int p = 4 * lane + j;
-    int a, jj, width;
-    if (p < sec_t / 2) {
-      a = 0; jj = p; width = sec_t;
-    } else if (p < (sec_t + sec_h) / 2) {
-      a = 1; jj = p - sec_t / 2; width = sec_h;
-    } else {
-      a = 2; jj = p - (sec_t + sec_h) / 2; width = D - sec_t - sec_h;
-    }
-    axis[j] = a;
-    // frequencies in double, rounded once to float
-    f_vid[j] = (float)exp2(-2.0 * jj / width * log2_theta);
-    f_aud[j] = (float)exp2(-2.0 * p / D * log2_theta);
+    int jj, width;
+    axis[j] = axis_of(p, jj, width);
+    f_vid[j] = f_tab[0][p];
+    f_aud[j] = f_tab[1][p];
   }
   float gq[8], gk[8];
   Vec8<T>::load(g_q + 8 * lane, gq);
@@ -58,41 +77,55 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   int64_t cur_tok = -1;
   int kind = 2;
   float cs[4], sn[4];
-  for (int64_t r = begin + slot; r < end; r += SLOTS) {
-    const int64_t tok = r / rows_per_tok;
-    const int rr = (int)(r - tok * rows_per_tok);
-    const bool is_k = rr >= n_heads;
-    const int head = is_k ? rr - n_heads : rr;
-    if (tok != cur_tok) {
-      cur_tok = tok;
-      const int4 p = pos[tok];
-      kind = p.x;
+  // U rows per step, SLOTS rows apart: all U loads are issued before the first
+  // row is processed, and its stores follow
+  for (int64_t r0 = begin + slot; r0 < end; r0 += U * SLOTS) {
+    T* ptr[U];
+    int64_t tok[U];
+    bool is_k[U];
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + u * SLOTS;
+      const int64_t rc = r < end ? r : r0;  // past the end: a harmless re-read of row r0
+      tok[u] = rc / rows_per_tok;
+      const int rr = (int)(rc - tok[u] * rows_per_tok);
+      is_k[u] = rr >= n_heads;
+      const int head = is_k[u] ? rr - n_heads : rr;
+      ptr[u] = (is_k[u] ? k + tok[u] * ld_k : q + tok[u] * ld_q) + (int64_t)head * D + 8 * lane;
+      Vec8<T>::load_nt(ptr[u], v[u]);  // pad rows are read too (in the buffer), never written
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (r0 + u * SLOTS >= end) break;
+      if (tok[u] != cur_tok) {
+        cur_tok = tok[u];
+        const int4 p = pos[cur_tok];
+        kind = p.x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pv = axis[j] == 0 ? p.y : (axis[j] == 1 ? p.z : p.w);
+          const float ang = kind == 1 ? (float)p.y * f_aud[j] : (float)pv * f_vid[j];
+          sincosf(ang, &sn[j], &cs[j]);
+        }
+      }
+      if (kind != 0 && kind != 1) continue;  // pad row: untouched
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += v[u][i] * v[u][i];
+      ss = group_sum<L>(ss);
+      const float rinv = rsqrtf(ss * (1.0f / D) + eps);
+      const float* g = is_k[u] ? gk : gq;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] * rinv * g[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pv = axis[j] == 0 ? p.y : (axis[j] == 1 ? p.z : p.w);
-        const float ang = kind == 1 ? (float)p.y * f_aud[j] : (float)pv * f_vid[j];
-        sincosf(ang, &sn[j], &cs[j]);
+        const float a = v[u][2 * j], b = v[u][2 * j + 1];
+        v[u][2 * j] = a * cs[j] - b * sn[j];
+        v[u][2 * j + 1] = a * sn[j] + b * cs[j];
       }
+      Vec8<T>::store_nt(ptr[u], v[u]);
     }
-    if (kind != 0 && kind != 1) continue;  // pad row: untouched
-    T* ptr = (is_k ? k + tok * ld_k : q + tok * ld_q) + (int64_t)head * D + 8 * lane;
-    float v[8];
-    Vec8<T>::load_nt(ptr, v);
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
-    ss = group_sum<L>(ss);
-    const float rinv = rsqrtf(ss * (1.0f / D) + eps);
-    const float* g = is_k ? gk : gq;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = v[i] * rinv * g[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = v[2 * j], b = v[2 * j + 1];
-      v[2 * j] = a * cs[j] - b * sn[j];
-      v[2 * j + 1] = a * sn[j] + b * cs[j];
-    }
-    Vec8<T>::store_nt(ptr, v);
   }
 }
 
@@ -105,7 +138,7 @@ static hipError_t launch_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_
   const int64_t total = n_tok * 2 * (int64_t)n_heads;
   const int64_t rows_per_block = (int64_t)SLOTS * 16;
   const int64_t blocks = ceil_div(total, rows_per_block);
-  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, 4>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (T*)q, ld_q, (T*)k, ld_k, n_tok, n_heads, (const T*)g_q, (const T*)g_k,
                      (const int4*)pos, sec_t, sec_h, log2((double)theta), eps, rows_per_block);
   return hipGetLastError();
