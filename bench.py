@@ -412,6 +412,15 @@ def main():
         print(json.dumps({"kernel": args.only, "attn_ms": ms, "attn_tflops": work["attn_flop"] / ms / 1e9}))
         return
 
+    if args.only == "block":
+        # the block's kernels alone (for per-kernel counters)
+        for _ in range(args.warmup):
+            block()
+        torch.cuda.synchronize()
+        ms = timer.time(block, max(args.steps, 1))
+        print(json.dumps({"kernel": "block", "block_ms": ms}))
+        return
+
     # ---- timed block steps
     log(f"warmup {args.warmup}, steps {args.steps}")
     for _ in range(args.warmup):
