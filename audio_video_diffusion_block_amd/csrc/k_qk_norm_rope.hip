@@ -136,7 +136,7 @@ static hipError_t launch_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_
   constexpr int L = D / 8;
   constexpr int SLOTS = 256 / L;
   const int64_t total = n_tok * 2 * (int64_t)n_heads;
-  const int64_t rows_per_block = (int64_t)SLOTS * 16;
+  const int64_t rows_per_block = (int64_t)SLOTS * 8;  // two steps of four rows per lane
   const int64_t blocks = ceil_div(total, rows_per_block);
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, 4>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (T*)q, ld_q, (T*)k, ld_k, n_tok, n_heads, (const T*)g_q, (const T*)g_k,
