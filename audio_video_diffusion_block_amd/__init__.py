@@ -120,6 +120,7 @@ _c_attn8_skip = _sig("h3_varlen_attn_fp8_skip", ctypes.c_int,
                       _f, _f, _p, _sz, _i32, _p])
 _c_mfma_probe = _sig("h3_mfma_rate_probe", ctypes.c_int, [_i32, _i32, _p, _i64, _p])
 _c_hbm_probe = _sig("h3_hbm_rate_probe", ctypes.c_int, [_i32, _p, _p, _i64, _i64, _i64, _p])
+_c_check_segments = _sig("h3_check_segments", ctypes.c_int, [_p, _p, _i32, _i64, _i32])
 _c_mxq = _sig("h3_mx_quantize", ctypes.c_int,
               [_p, _i64, _i64, _i32, _p, _i64, _p, _i64, _i32, _p])
 _c_lin8 = _sig("h3_linear_fp8", ctypes.c_int,
@@ -136,7 +137,7 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
             "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip",
-            "h3_mfma_rate_probe", "h3_hbm_rate_probe")
+            "h3_mfma_rate_probe", "h3_hbm_rate_probe", "h3_check_segments")
 
 
 def _status_string(st: int) -> str:
@@ -456,6 +457,19 @@ def h3_mfma_rate_probe(out: torch.Tensor, iters: int, zero_operands: bool = Fals
     assert out.dtype == torch.float32 and out.is_contiguous()
     _check(_c_mfma_probe(iters, int(bool(zero_operands)), _ptr(out), out.numel(), _stream(stream)))
     return (out.numel() // 64) * iters * 4 * 32768.0
+
+
+def h3_check_segments(cu_slots, valid_len, n_buf: int, max_valid_len: int) -> None:
+    """Check segment metadata given as host int32 arrays (numpy or CPU tensors);
+    raises H3Error (H3_ERR_ARG) naming the first violated rule."""
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_slots), dtype=np.int32)
+    vl = None if valid_len is None else np.ascontiguousarray(np.asarray(valid_len), dtype=np.int32)
+    n_seg = cu.size - 1
+    if vl is not None and vl.size != n_seg:
+        raise ValueError("valid_len must have one entry per segment")
+    _check(_c_check_segments(cu.ctypes.data, None if vl is None else vl.ctypes.data, n_seg, n_buf,
+                             max_valid_len))
 
 
 def h3_hbm_rate_probe(dst: torch.Tensor, src: torch.Tensor = None, row_chunks: int = 0,

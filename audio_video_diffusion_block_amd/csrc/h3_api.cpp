@@ -7,7 +7,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "../../include/h3dit.h"
 #include "h3_common.hpp"
@@ -147,6 +149,44 @@ h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k
   return H3_OK;
 }
 
+// Segment metadata in host memory: 0 <= cu[0] <= ... <= cu[n_seg] <= n_buf, and every valid
+// length (the slot length where valid is NULL) in [0, slot length] and at most max_len.
+h3_status check_segments_host(const int32_t* cu, const int32_t* valid, int32_t n_seg,
+                              int64_t n_buf, int32_t max_len) {
+  CHECK(cu, "cu_slots is NULL");
+  CHECK(n_seg >= 1 && n_seg <= 65535, "n_seg must be in [1, 65535]");
+  CHECK(n_buf >= 0 && n_buf < (int64_t)INT32_MAX, "n_buf out of range");
+  CHECK(cu[0] >= 0, "cu_slots[0] = %d is negative", cu[0]);
+  for (int32_t i = 0; i < n_seg; ++i)
+    CHECK(cu[i + 1] >= cu[i], "cu_slots decreases at %d (%d -> %d)", i, cu[i], cu[i + 1]);
+  CHECK((int64_t)cu[n_seg] <= n_buf, "cu_slots[n_seg] = %d exceeds n_buf = %lld", cu[n_seg],
+        (long long)n_buf);
+  for (int32_t i = 0; i < n_seg; ++i) {
+    const int32_t slot = cu[i + 1] - cu[i];
+    const int32_t len = valid ? valid[i] : slot;
+    CHECK(len >= 0 && len <= slot, "valid_len[%d] = %d outside [0, %d]", i, len, slot);
+    CHECK(len <= max_len, "valid length %d of segment %d exceeds max_valid_len = %d", len, i,
+          max_len);
+  }
+  return H3_OK;
+}
+
+// H3_DEBUG_VALIDATE=1: copy the device segment metadata to the host (this synchronises the
+// stream) and check it before anything is launched.
+h3_status debug_check_segments(const int32_t* cu_dev, const int32_t* valid_dev, int32_t n_seg,
+                               int64_t n_buf, int32_t max_len, hipStream_t s) {
+  const char* e = getenv("H3_DEBUG_VALIDATE");
+  if (!e || strcmp(e, "1") != 0) return H3_OK;
+  std::vector<int32_t> cu((size_t)n_seg + 1), vl(valid_dev ? (size_t)n_seg : 0);
+  TRY(hip_status(hipMemcpyAsync(cu.data(), cu_dev, cu.size() * 4, hipMemcpyDeviceToHost, s),
+                 "H3_DEBUG_VALIDATE copy of cu_slots"));
+  if (valid_dev)
+    TRY(hip_status(hipMemcpyAsync(vl.data(), valid_dev, vl.size() * 4, hipMemcpyDeviceToHost, s),
+                   "H3_DEBUG_VALIDATE copy of valid_len"));
+  TRY(hip_status(hipStreamSynchronize(s), "H3_DEBUG_VALIDATE synchronisation"));
+  return check_segments_host(cu.data(), valid_dev ? vl.data() : nullptr, n_seg, n_buf, max_len);
+}
+
 h3_status validate_modres(void* x, int64_t ld_x, const void* y, int64_t ld_y, const void* gate,
                           const void* shift, const void* scale, int64_t ld_mod, void* h,
                           int64_t ld_h, int64_t n_tok, int32_t dim, int32_t norm_kind, float eps,
@@ -259,6 +299,12 @@ h3_status h3_qk_norm_rope(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t 
                     "qk_norm_rope launch");
 }
 
+h3_status h3_check_segments(const int32_t* cu_slots, const int32_t* valid_len, int32_t n_seg,
+                            int64_t n_buf, int32_t max_valid_len) {
+  g_err[0] = 0;
+  return check_segments_host(cu_slots, valid_len, n_seg, n_buf, max_valid_len);
+}
+
 size_t h3_varlen_attn_workspace_size(int64_t n_buf, int32_t n_heads, int32_t head_dim,
                                      int32_t n_seg, h3_dtype dtype) {
   if (n_buf <= 0 || n_heads <= 0 || head_dim <= 0 || n_seg <= 0) return 0;
@@ -276,6 +322,7 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
                     max_valid_len, ws, ws_bytes, dtype));
   if (n_buf == 0) return H3_OK;
   TRY(check_device());
+  TRY(debug_check_segments(cu_slots, valid_len, n_seg, n_buf, max_valid_len, (hipStream_t)stream));
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   return hip_status(launch_varlen_attn(dtype == H3_BF16, head_dim, q, ld_q, k, ld_k, v, ld_v, o,
                                        ld_o, n_buf, n_heads, cu_slots, valid_len, n_seg,
@@ -296,6 +343,7 @@ h3_status h3_varlen_attn_skip(const void* q, int64_t ld_q, const void* k, int64_
                     max_valid_len, ws, ws_bytes, dtype));
   if (n_buf == 0) return H3_OK;
   TRY(check_device());
+  TRY(debug_check_segments(cu_slots, valid_len, n_seg, n_buf, max_valid_len, (hipStream_t)stream));
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   return hip_status(launch_varlen_attn_skip(head_dim, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf,
                                             n_heads, cu_slots, valid_len, n_seg, max_valid_len,
@@ -321,6 +369,7 @@ h3_status varlen_attn_fp8(const void* q, int64_t ld_q, const void* k, int64_t ld
                     max_valid_len, ws, ws_bytes, dtype, true));
   if (n_buf == 0) return H3_OK;
   TRY(check_device());
+  TRY(debug_check_segments(cu_slots, valid_len, n_seg, n_buf, max_valid_len, (hipStream_t)stream));
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   return hip_status(launch_varlen_attn_fp8(head_dim, q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf,
                                            n_heads, cu_slots, valid_len, n_seg, max_valid_len,
@@ -639,6 +688,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
     return fail(H3_ERR_WORKSPACE, "block workspace %zu bytes, need %zu", ws_bytes, L.total);
   CHECK(ws && aligned16(ws), "workspace is NULL or not 16-byte aligned");
   TRY(check_device());
+  TRY(debug_check_segments(io->cu_slots, io->valid_len, io->n_seg, io->n_buf, io->max_valid_len,
+                           (hipStream_t)stream));
 
   const bool bf = dt == H3_BF16;
   const int64_t es = (int64_t)esize(dt);

@@ -441,6 +441,25 @@ h3_status h3_euler_update(void* z, const void* u, void* x_next, int64_t n, float
 h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, int64_t W,
                           void* out, int32_t layout, void* stream);
 
+/* --------------------------------------------- segment metadata check */
+
+/*
+ * h3_check_segments -- checks segment metadata held in HOST memory against the
+ * rules the attention entry points assume ([RT-H3] Key takeaways: attention
+ * runs over each segment's valid length, suffix padding removed):
+ *   0 <= cu_slots[0] <= cu_slots[1] <= ... <= cu_slots[n_seg] <= n_buf, and
+ *   for each segment s: 0 <= valid_len[s] <= cu_slots[s+1] - cu_slots[s] (the
+ *   slot length itself when valid_len is NULL) and valid_len[s] <= max_valid_len.
+ *   cu_slots [n_seg + 1], valid_len [n_seg] or NULL: host arrays, read only.
+ * The attention entry points and h3_dit_block_forward run the same check on
+ * their device copies when the environment variable H3_DEBUG_VALIDATE is "1"
+ * (a device-to-host copy that synchronises the stream, before any launch);
+ * otherwise they trust the device metadata.
+ * Errors: H3_ERR_ARG with the first violated rule in h3_last_error().
+ */
+h3_status h3_check_segments(const int32_t* cu_slots, const int32_t* valid_len, int32_t n_seg,
+                            int64_t n_buf, int32_t max_valid_len);
+
 /* ------------------------------------------------------- measurement aid */
 
 /*

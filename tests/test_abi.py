@@ -315,3 +315,29 @@ def test_hbm_rate_probe_argument_checks():
     assert h3._c_hbm_probe(0, None, other, 1, 16, 16, None) == h3.H3_ERR_ARG
     assert h3._c_hbm_probe(1, None, None, 1, 16, 16, None) == h3.H3_ERR_ARG
     assert h3._c_hbm_probe(1, None, FAKE + 8, 1, 16, 16, None) == h3.H3_ERR_ARG
+
+
+def test_check_segments_rules():
+    """The host segment checker accepts well-formed metadata and names each rule it rejects."""
+    import numpy as np
+    import audio_video_diffusion_block_amd as h3
+    ok = dict(cu_slots=[0, 4032, 5600, 5700], valid_len=[4032, 1500, 17], n_buf=8192, max_valid_len=4032)
+    h3.h3_check_segments(**ok)
+    h3.h3_check_segments([0, 10, 10, 30], None, 30, 20)         # empty slot, full slots
+    h3.h3_check_segments(np.array([0, 64]), np.array([0]), 64, 0)  # zero valid rows
+    bad = [
+        (dict(ok, cu_slots=[-1, 4032, 5600, 5700]), "negative"),
+        (dict(ok, cu_slots=[0, 5600, 4032, 5700]), "decreases"),
+        (dict(ok, cu_slots=[0, 4032, 5600, 8193]), "exceeds n_buf"),
+        (dict(ok, valid_len=[4033, 1500, 17]), "outside"),
+        (dict(ok, valid_len=[4032, -1, 17]), "outside"),
+        (dict(ok, max_valid_len=4031), "max_valid_len"),
+        (dict(ok, cu_slots=[0, 70], valid_len=None, n_buf=70, max_valid_len=64), "max_valid_len"),
+    ]
+    for args, word in bad:
+        with pytest.raises(h3.H3Error) as ei:
+            h3.h3_check_segments(**args)
+        assert ei.value.status == h3.H3_ERR_ARG and word in str(ei.value), (args, str(ei.value))
+    assert h3._c_check_segments(None, None, 1, 10, 10) == h3.H3_ERR_ARG
+    cu = np.array([0, 10], dtype=np.int32)
+    assert h3._c_check_segments(cu.ctypes.data, None, 0, 10, 10) == h3.H3_ERR_ARG
