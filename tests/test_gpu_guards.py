@@ -145,6 +145,24 @@ def test_debug_validate_accepts_good_and_rejects_malformed_metadata(lib, debug_v
         assert torch.all(o == 3.0), "nothing may be launched after a failed check"
 
 
+@pytest.mark.parametrize("entry", ["fp8", "skip", "fp8_skip"])
+def test_debug_validate_on_the_other_attention_paths(lib, debug_validate, entry):
+    case = W.varlen_case(seed=2, lengths=(100, 100), n_buf=256, n_heads=2, head_dim=128)
+    q, k, v = (dev(a.reshape(case.n_buf, -1), "bf16") for a in (case.q, case.k, case.v))
+    fn = {"fp8": lambda *a: lib.h3_varlen_attn_fp8(*a),
+          "skip": lambda *a: lib.h3_varlen_attn_skip(*a, -20.0),
+          "fp8_skip": lambda *a: lib.h3_varlen_attn_fp8_skip(*a, -20.0)}[entry]
+    o = torch.full((256, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lib.H3Error) as ei:   # the grid hint is below a valid length
+        fn(q, k, v, o, 2, 128, dev_i32(case.cu_slots), dev_i32(case.valid_len), 99)
+    assert ei.value.status == lib.H3_ERR_ARG and "max_valid_len" in str(ei.value)
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0), "nothing may be launched after a failed check"
+    fn(q, k, v, o, 2, 128, dev_i32(case.cu_slots), dev_i32(case.valid_len), 100)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_debug_validate_in_the_block(lib, debug_validate):
     wl = W.TINY
     w = W.block_weights(wl, 0, "bf16")
