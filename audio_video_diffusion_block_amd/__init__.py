@@ -121,6 +121,8 @@ _c_attn8_skip = _sig("h3_varlen_attn_fp8_skip", ctypes.c_int,
 _c_mfma_probe = _sig("h3_mfma_rate_probe", ctypes.c_int, [_i32, _i32, _p, _i64, _p])
 _c_hbm_probe = _sig("h3_hbm_rate_probe", ctypes.c_int, [_i32, _p, _p, _i64, _i64, _i64, _p])
 _c_check_segments = _sig("h3_check_segments", ctypes.c_int, [_p, _p, _i32, _i64, _i32])
+_c_modmx = _sig("h3_modulate_mx", ctypes.c_int,
+                [_p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _f, _p])
 _c_mxq = _sig("h3_mx_quantize", ctypes.c_int,
               [_p, _i64, _i64, _i32, _p, _i64, _p, _i64, _i32, _p])
 _c_lin8 = _sig("h3_linear_fp8", ctypes.c_int,
@@ -137,7 +139,7 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
             "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip",
-            "h3_mfma_rate_probe", "h3_hbm_rate_probe", "h3_check_segments")
+            "h3_mfma_rate_probe", "h3_hbm_rate_probe", "h3_check_segments", "h3_modulate_mx")
 
 
 def _status_string(st: int) -> str:
@@ -335,6 +337,20 @@ def h3_mx_quantize(x, out: Optional[MxTensor] = None, stream=None) -> MxTensor:
         out = MxTensor.empty(rows, cols, x.device)
     _check(_c_mxq(_ptr(x), _ld(x), rows, cols, _ptr(out.q), _ld(out.q), _ptr(out.s), _ld(out.s),
                   _dt(x), _stream(stream)))
+    return out
+
+
+def h3_modulate_mx(x, shift, scale, out: Optional[MxTensor] = None, ld_mod: Optional[int] = None,
+                   norm_kind: int = 0, eps: float = 1e-6, stream=None) -> MxTensor:
+    """Modulated norm of bf16 x [n, C] written as an MxTensor (C % 128 == 0); the
+    same bytes as h3_mx_quantize of h3_modulate_residual's bf16 h."""
+    n, c = x.shape
+    if out is None:
+        out = MxTensor.empty(n, c, x.device)
+    if ld_mod is None:
+        ld_mod = 0 if shift.shape[0] == 1 else _ld(shift)
+    _check(_c_modmx(_ptr(x), _ld(x), _ptr(shift), _ptr(scale), ld_mod, _ptr(out.q), _ld(out.q),
+                    _ptr(out.s), _ld(out.s), n, c, norm_kind, eps, _stream(stream)))
     return out
 
 

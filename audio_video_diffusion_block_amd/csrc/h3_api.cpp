@@ -489,6 +489,27 @@ h3_status h3_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int32_t cols
                     "mx_quantize launch");
 }
 
+h3_status h3_modulate_mx(const void* x, int64_t ld_x, const void* shift, const void* scale,
+                         int64_t ld_mod, void* q, int64_t ld_q, void* q_scale, int64_t ld_scale,
+                         int64_t n_tok, int32_t dim, int32_t norm_kind, float eps, void* stream) {
+  g_err[0] = 0;
+  CHECK(n_tok >= 0 && n_tok <= (int64_t)INT32_MAX, "n_tok out of range");
+  CHECK(dim > 0 && dim % 128 == 0 && dim <= 16384, "dim must be a positive multiple of 128, <= 16384");
+  CHECK(norm_kind == 0 || norm_kind == 1, "norm_kind must be 0 or 1");
+  CHECK(eps >= 0.f, "eps < 0");
+  if (n_tok == 0) return H3_OK;
+  TRY(check_rows("x", x, ld_x, dim, n_tok, H3_BF16));
+  CHECK(ld_x > 0, "x row stride must be positive");
+  TRY(check_rows("shift", shift, ld_mod, dim, n_tok, H3_BF16));
+  TRY(check_rows("scale", scale, ld_mod, dim, n_tok, H3_BF16));
+  h3_mx_operand o{q, ld_q, q_scale, ld_scale};
+  TRY(check_mx("q", &o, dim, n_tok));
+  TRY(check_device());
+  return hip_status(launch_modulate_mx(x, ld_x, shift, scale, ld_mod, q, ld_q, q_scale, ld_scale,
+                                       n_tok, dim, norm_kind, eps, (hipStream_t)stream),
+                    "modulate_mx launch");
+}
+
 h3_status h3_linear_fp8(const h3_mx_operand* a, const h3_mx_operand* w, void* out,
                         int64_t ld_out, int64_t m, int32_t n_out, int32_t k_in,
                         const void* gate, int64_t ld_gate, void* stream) {
@@ -703,11 +724,21 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   const int64_t ldm = io->ld_mod;
   auto mslot = [&](int i) { return (const void*)(mod + (int64_t)i * C * es); };
 
+  // FP8 projections with C % 128 == 0: the modulated norms write the MX operand
+  // of h1 / h2 directly (the same bytes as storing bf16 h and quantizing it)
+  const bool mx_norm = f8 && C % 128 == 0;
   // A1 h1 = norm(x)(1 + scale1) + shift1
-  TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(0),
-                                          mslot(1), ldm, h1, C, n, C, cfg->norm_kind,
-                                          cfg->eps_mod, s),
-                 "modulate-1"));
+  if (mx_norm) {
+    TRY(hip_status(launch_modulate_mx(io->x, io->ld_x, mslot(0), mslot(1), ldm, wsb + L.xq, L.xkp,
+                                      wsb + L.xs, L.xkp / 32, n, C, cfg->norm_kind, cfg->eps_mod,
+                                      s),
+                   "modulate-1 (mx)"));
+  } else {
+    TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(0),
+                                            mslot(1), ldm, h1, C, n, C, cfg->norm_kind,
+                                            cfg->eps_mod, s),
+                   "modulate-1"));
+  }
   const float scale = 1.0f / std::sqrt((float)D);
   auto attention = [&](const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                        int64_t ldv, void* o, int64_t ldo, int64_t rows, int heads) {
@@ -747,7 +778,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
     scatter.peer_hc = hc;
     scatter.peer_D = D;
     if (f8) {
-      TRY(quant_act(h1, C, C));
+      if (!mx_norm) TRY(quant_act(h1, C, C));
       TRY(hip_status(launch_gemm_mx8(EPI_STORE, xq, wmx(0), MxOperand{}, send, 3 * hd, nullptr, 0,
                                      n, (int)(3 * hd), C, s, scatter),
                      "qkv projection (peer-major, fp8)"));
@@ -796,7 +827,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   } else {
   // A2 qkv = h1 w_qkv^T
   if (f8) {
-    TRY(quant_act(h1, C, C));
+    if (!mx_norm) TRY(quant_act(h1, C, C));
     TRY(hip_status(launch_gemm_mx8(EPI_STORE, xq, wmx(0), MxOperand{}, qkv, 3 * hd, nullptr, 0, n,
                                    (int)(3 * hd), C, s),
                    "qkv projection (fp8)"));
@@ -850,14 +881,21 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   }
   }
   // A8 h2 = norm(x)(1 + scale2) + shift2   (h2 reuses h1's scratch)
-  TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(3),
-                                          mslot(4), ldm, h1, C, n, C, cfg->norm_kind,
-                                          cfg->eps_mod, s),
-                 "modulate-2"));
+  if (mx_norm) {
+    TRY(hip_status(launch_modulate_mx(io->x, io->ld_x, mslot(3), mslot(4), ldm, wsb + L.xq, L.xkp,
+                                      wsb + L.xs, L.xkp / 32, n, C, cfg->norm_kind, cfg->eps_mod,
+                                      s),
+                   "modulate-2 (mx)"));
+  } else {
+    TRY(hip_status(launch_modulate_residual(bf, io->x, io->ld_x, nullptr, 0, nullptr, mslot(3),
+                                            mslot(4), ldm, h1, C, n, C, cfg->norm_kind,
+                                            cfg->eps_mod, s),
+                   "modulate-2"));
+  }
   // A9 g = silu(h2 w1^T) * (h2 w3^T)
   void* g = wsb + L.g;
   if (f8) {
-    TRY(quant_act(h1, C, C));
+    if (!mx_norm) TRY(quant_act(h1, C, C));
     TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, xq, wmx(2), wmx(3), g, F, nullptr, 0, n, F, C, s),
                    "swiglu up-projection (fp8)"));
     // A10 x <- x + gate2 * (g w2^T), g quantized on the fly

@@ -20,6 +20,10 @@ hipError_t launch_modulate_residual(bool bf16, void* x, int64_t ld_x, const void
                                     const void* scale, int64_t ld_mod, void* h, int64_t ld_h,
                                     int64_t n_tok, int dim, int norm_kind, float eps,
                                     hipStream_t s);
+// modulated norm of x written as an MX e4m3 operand instead of bf16 (dim % 32 == 0)
+hipError_t launch_modulate_mx(const void* x, int64_t ld_x, const void* shift, const void* scale,
+                              int64_t ld_mod, void* q, int64_t ld_q, void* qs, int64_t ld_s,
+                              int64_t n_tok, int dim, int norm_kind, float eps, hipStream_t s);
 
 // Optional operand layouts of the bf16 K % 64 == 0 GEMM (sequence-parallel
 // exchange buffers).  All zero: plain row-major A and C.

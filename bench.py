@@ -504,6 +504,8 @@ def main():
     wmx = h3.block_weights_mx(wd)
     h1m = h3.h3_mx_quantize(h1)
     ops["act_quant"] = timer.time(lambda: h3.h3_mx_quantize(h1, h1m), reps_short, warm=1)
+    ops["modnorm_mx"] = timer.time(lambda: h3.h3_modulate_mx(xs, mod[:, 0], mod[:, 1], out=h1m),
+                                   reps_short, warm=1)
     ops["qkv_gemm_fp8"] = timer.time(lambda: h3.h3_linear_fp8(h1m, wmx[0], qkv), reps)
     om = h3.h3_mx_quantize(o_in)
     ops["out_gemm_residual_fp8"] = timer.time(lambda: h3.h3_linear_fp8(om, wmx[1], xs, gate=mod[:, 2]), reps)
@@ -572,6 +574,11 @@ def main():
         "swiglu_residual_fp8": {"ms": ops["swiglu_residual_fp8"],
                                 "TFLOP/s": (work["w13_flop"] + work["w2_flop"]) / ops["swiglu_residual_fp8"] / 1e9,
                                 "note": "includes quantizing g"},
+        "modnorm_mx": {"ms": ops["modnorm_mx"],
+                       "GB/s": wl.n_loc * C * (3 * 2 + 1 + 1 / 32) / ops["modnorm_mx"] / 1e6,
+                       "frac_hbm": wl.n_loc * C * (3 * 2 + 1 + 1 / 32) / ops["modnorm_mx"] / 1e6 / HBM_PEAK_GBS,
+                       "note": "modulated norm written as the MX e4m3 operand of the FP8 projections "
+                               "(x, shift, scale read; e4m3 bytes and scales written)"},
         "act_quant": {"ms": ops["act_quant"], "GB/s": wl.n_loc * C * (2 + 1 + 1 / 32) / ops["act_quant"] / 1e6,
                       "note": "h1 bf16 -> MX e4m3 (one per projection input)"},
         "qkv_gemm": {"ms": ops["qkv_gemm"], "TFLOP/s": work["qkv_flop"] / ops["qkv_gemm"] / 1e9},

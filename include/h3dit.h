@@ -278,6 +278,22 @@ h3_status h3_mx_quantize(const void* x, int64_t ld_x, int64_t rows, int32_t cols
                          void* stream);
 
 /*
+ * h3_modulate_mx -- the modulated norm of h3_modulate_residual (no residual),
+ * written as an MX operand instead of bf16 h ([RT-H3] Key takeaways:
+ * modulation and normalisation fused; [FH3-zh] 超出 FastH3 配置的扩展能力:
+ * online FP8 GEMMs): q, q_scale receive exactly the bytes that
+ * h3_modulate_residual(h_out = h) followed by h3_mx_quantize(h) would give.
+ *   x [n_tok][dim] bf16 (read only), shift/scale rows of stride ld_mod (0:
+ *   broadcast), norm_kind and eps as in h3_modulate_residual.
+ *   (q, ld_q, q_scale, ld_scale): MX operand of dim columns, as above.
+ *   dim % 128 == 0 (no zero padding columns), dim <= 16384; bf16 only.
+ * Errors: H3_ERR_ARG for shapes, strides or alignment.
+ */
+h3_status h3_modulate_mx(const void* x, int64_t ld_x, const void* shift, const void* scale,
+                         int64_t ld_mod, void* q, int64_t ld_q, void* q_scale, int64_t ld_scale,
+                         int64_t n_tok, int32_t dim, int32_t norm_kind, float eps, void* stream);
+
+/*
  * h3_linear_fp8 -- out = a w^T over MX operands a [m][k_in] and w [n_out][k_in]
  * (k_in % 32 == 0), fp32 accumulation, bf16 out [m][n_out] (row stride ld_out).
  * gate != NULL: out = out + gate * (a w^T) in place (gate bf16 [m][n_out]).

@@ -341,3 +341,27 @@ def test_check_segments_rules():
     assert h3._c_check_segments(None, None, 1, 10, 10) == h3.H3_ERR_ARG
     cu = np.array([0, 10], dtype=np.int32)
     assert h3._c_check_segments(cu.ctypes.data, None, 0, 10, 10) == h3.H3_ERR_ARG
+
+
+def test_modulate_mx_argument_checks():
+    """The modulated norm to an MX operand: dim a multiple of 128, operand strides, pointers."""
+    import audio_video_diffusion_block_amd as h3
+    # x, ld_x, shift, scale, ld_mod, q, ld_q, q_scale, ld_scale, n, dim, norm_kind, eps, stream
+    ok = [FAKE, 256, FAKE, FAKE, 6 * 256, FAKE, 256, FAKE, 8, 10, 256, 0, 1e-6, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x", "ld_x", "shift", "scale", "ld_mod", "q", "ld_q", "qs", "ld_s", "n", "dim", "nk", "eps", "st"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return h3._c_modmx(*a)
+
+    st = call(dim=192, ld_x=192, ld_q=256)
+    assert st == h3.H3_ERR_ARG and "128" in h3.last_error()
+    assert call(ld_q=128) == h3.H3_ERR_ARG and "ld" in h3.last_error()
+    assert call(ld_s=6) == h3.H3_ERR_ARG and "ld_scale" in h3.last_error()
+    assert call(q=None) == h3.H3_ERR_ARG
+    assert call(shift=None) == h3.H3_ERR_ARG
+    assert call(nk=2) == h3.H3_ERR_ARG
+    assert call(x=FAKE + 8) == h3.H3_ERR_ARG
+    assert call(n=0, x=None, q=None) == h3.H3_OK

@@ -179,3 +179,25 @@ def test_fp8_projections_10s_shapes_sampled(lib):
     torch.cuda.synchronize()
     got = host(out[torch.from_numpy(rows).cuda()])
     assert_close(got, _swiglu_ref(h, w1, w3, w2, rows), "bf16", "swiglu_fp8 10 s sampled", max_abs=4e-2)
+
+
+@pytest.mark.parametrize("rows,dim,per_token,norm_kind", [(333, 256, True, 0), (70, 384, False, 0),
+                                                         (129, 5120, True, 0), (65, 1024, True, 1)])
+def test_modulate_mx_equals_norm_then_quantize(lib, rows, dim, per_token, norm_kind):
+    """The fused modulated norm -> MX operand gives the bytes of the two passes it
+    replaces: the bf16 modulated norm, then the MX quantizer (each pinned to the
+    oracle on its own); per-token and broadcast modulation, LayerNorm and RMSNorm,
+    ragged row counts."""
+    g = torch.Generator(device="cuda").manual_seed(rows + dim)
+    bf = torch.bfloat16
+    x = (3 * torch.randn((rows, dim), generator=g, device="cuda")).to(bf)
+    mod = (0.5 * torch.randn((rows if per_token else 1, 6, dim), generator=g, device="cuda")).to(bf)
+    x[rows // 2] = 0  # a constant row: zero variance
+    h = torch.empty_like(x)
+    xs = x.clone()
+    lib.h3_modulate_residual(xs, shift=mod[:, 0], scale=mod[:, 1], h_out=h, norm_kind=norm_kind)
+    ref = lib.h3_mx_quantize(h)
+    got = lib.h3_modulate_mx(x, mod[:, 0], mod[:, 1], norm_kind=norm_kind)
+    torch.cuda.synchronize()
+    assert torch.equal(x, xs), "x is read only"
+    assert torch.equal(got.q, ref.q) and torch.equal(got.s, ref.s)
