@@ -16,6 +16,7 @@
 #include "h3_kernels.hpp"
 
 namespace h3 {
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(NT) void modres_kernel(
         uint2 wq;
         wq.x = fp8::pack4_e4m3(o[0], o[1], o[2], o[3], s);
         wq.y = fp8::pack4_e4m3(o[4], o[5], o[6], o[7], s);
-        *reinterpret_cast<uint2*>(mq + row * ld_mq + 8 * c) = wq;
+        __builtin_nontemporal_store(u32x2_t{wq.x, wq.y}, reinterpret_cast<u32x2_t*>(mq + row * ld_mq + 8 * c));
         if ((threadIdx.x & 3) == 0) ms[row * ld_ms + c / 4] = (uint8_t)(ex + 127);
       } else {
         Vec8<T>::store_nt(h + row * ld_h + 8 * c, o);
