@@ -565,12 +565,22 @@ h3_status h3_swiglu_fp8(const h3_mx_operand* h, const h3_mx_operand* w1,
   g8.ld = fp;
   g8.scale = wsb + gs_off;
   g8.ld_scale = fp / 32;
+  // with ffn_dim % 128 == 0 the up-projection's epilogue also writes g's MX
+  // operand (no padding columns); otherwise a separate pass quantizes g
+  GemmMap gmx;
+  if (ffn_dim % 128 == 0) {
+    gmx.mx_q = (uint8_t*)(wsb + gq_off);
+    gmx.mx_ld = fp;
+    gmx.mx_s = (uint8_t*)(wsb + gs_off);
+    gmx.mx_lds = fp / 32;
+  }
   TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, mx_of(h), mx_of(w1), mx_of(w3), wsb, ffn_dim,
-                                 nullptr, 0, n_tok, ffn_dim, dim, s),
+                                 nullptr, 0, n_tok, ffn_dim, dim, s, gmx),
                  "swiglu_fp8 up-projection launch"));
-  TRY(hip_status(launch_mx_quantize(wsb, ffn_dim, n_tok, ffn_dim, wsb + gq_off, fp, wsb + gs_off,
-                                    fp / 32, s),
-                 "swiglu_fp8 gate quantization launch"));
+  if (!gmx.mx_q)
+    TRY(hip_status(launch_mx_quantize(wsb, ffn_dim, n_tok, ffn_dim, wsb + gq_off, fp,
+                                      wsb + gs_off, fp / 32, s),
+                   "swiglu_fp8 gate quantization launch"));
   return hip_status(launch_gemm_mx8(gate ? EPI_RESIDUAL : EPI_STORE, g8, mx_of(w2), MxOperand{},
                                     out, ld_out, gate, ld_gate, n_tok, dim, ffn_dim, s),
                     "swiglu_fp8 down-projection launch");
@@ -896,11 +906,21 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   void* g = wsb + L.g;
   if (f8) {
     if (!mx_norm) TRY(quant_act(h1, C, C));
-    TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, xq, wmx(2), wmx(3), g, F, nullptr, 0, n, F, C, s),
+    // g's MX operand comes from the up-projection's epilogue when F % 128 == 0
+    GemmMap gmx;
+    if (F % 128 == 0) {
+      gmx.mx_q = (uint8_t*)(wsb + L.gq);
+      gmx.mx_ld = L.fkp;
+      gmx.mx_s = (uint8_t*)(wsb + L.gs);
+      gmx.mx_lds = L.fkp / 32;
+    }
+    TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, xq, wmx(2), wmx(3), g, F, nullptr, 0, n, F, C, s,
+                                   gmx),
                    "swiglu up-projection (fp8)"));
     // A10 x <- x + gate2 * (g w2^T), g quantized on the fly
-    TRY(hip_status(launch_mx_quantize(g, F, n, F, wsb + L.gq, L.fkp, wsb + L.gs, L.fkp / 32, s),
-                   "gate-product quantization"));
+    if (!gmx.mx_q)
+      TRY(hip_status(launch_mx_quantize(g, F, n, F, wsb + L.gq, L.fkp, wsb + L.gs, L.fkp / 32, s),
+                     "gate-product quantization"));
     MxOperand gq;
     gq.data = wsb + L.gq;
     gq.ld = L.fkp;

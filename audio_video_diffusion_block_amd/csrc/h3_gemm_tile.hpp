@@ -3,6 +3,7 @@
 #pragma once
 
 #include "h3_common.hpp"
+#include "h3_fp8.hpp"
 #include "h3_kernels.hpp"
 
 namespace h3 {
@@ -124,6 +125,30 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
       }
       if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
       else for (int e = 0; col + e < N; ++e) po[e] = src[e];
+      if (EPI == EPI_SWIGLU && map.mx_q) {
+        // MX e4m3 copy: a 32-column block is the chunks of 4 adjacent lanes (N % 32 == 0,
+        // so a quad is active or skipped as a whole)
+        const uint4 raw = *reinterpret_cast<const uint4*>(src);
+        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+        float v[8], am = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(u[e] << 16);
+          v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+        am = fmaxf(am, dpp<0xB1>(am));  // quad_perm [1,0,3,2]
+        am = fmaxf(am, dpp<0x4E>(am));  // quad_perm [2,3,0,1]
+        const int ex = fp8::e8m0_exp(am);
+        const float sc = __builtin_ldexpf(1.0f, -ex);
+        const uint32_t w0 = fp8::pack4_e4m3(v[0], v[1], v[2], v[3], sc);
+        const uint32_t w1 = fp8::pack4_e4m3(v[4], v[5], v[6], v[7], sc);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32x2_t{w0, w1},
+                                    reinterpret_cast<u32x2_t*>(map.mx_q + (int64_t)row * map.mx_ld + col));
+        if ((tid & 3) == 0) map.mx_s[(int64_t)row * map.mx_lds + col / 32] = (uint8_t)(ex + 127);
+      }
     }
   }
 }

@@ -35,7 +35,14 @@ struct GemmMap {
   // EPI_STORE scatter: output column n = (which*H + h)*D + d of row m goes to
   // C + ((p*M + m)*3 + which)*hc*D + j*D + d with h = p*hc + j (peer-major)
   int peer_H = 0, peer_hc = 0, peer_D = 0;
-  bool empty() const { return a_kgroup == 0 && peer_hc == 0; }
+  // EPI_SWIGLU (N % 32 == 0): the bf16 output is also written as an MX e4m3
+  // operand (mx_q bytes, row stride mx_ld; one E8M0 byte per 32 columns at mx_s,
+  // row stride mx_lds), the same bytes as quantizing the stored bf16 output
+  uint8_t* mx_q = nullptr;
+  int64_t mx_ld = 0;
+  uint8_t* mx_s = nullptr;
+  int64_t mx_lds = 0;
+  bool empty() const { return a_kgroup == 0 && peer_hc == 0 && mx_q == nullptr; }
 };
 
 // out = A @ B^T with epilogue; for EPI_SWIGLU, B = W1, B3 = W3 and N = features

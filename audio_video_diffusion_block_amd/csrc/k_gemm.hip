@@ -414,7 +414,8 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
   if (M == 0 || N == 0) return hipSuccess;
   // operand maps exist only on the bf16 K % 64 kernel (and a scatter only for plain stores)
   if (!map.empty() && (!bf16 || K < BK || K % BK != 0 || (map.a_kgroup % BK) != 0 ||
-                       (map.peer_hc && epi != EPI_STORE)))
+                       (map.peer_hc && epi != EPI_STORE) ||
+                       (map.mx_q && (epi != EPI_SWIGLU || N % 32 != 0))))
     return hipErrorInvalidValue;
   if (bf16) {
     const int tiles_m = (int)ceil_div(M, BM);

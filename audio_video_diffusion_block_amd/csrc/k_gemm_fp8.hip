@@ -289,7 +289,9 @@ hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, cons
                            int N, int K, hipStream_t s, const GemmMap& map) {
   if (M == 0 || N == 0) return hipSuccess;
   // only the store epilogue's peer-major scatter applies here (A is an MX operand)
-  if (map.a_kgroup != 0 || (map.peer_hc && epi != EPI_STORE)) return hipErrorInvalidValue;
+  if (map.a_kgroup != 0 || (map.peer_hc && epi != EPI_STORE) ||
+      (map.mx_q && (epi != EPI_SWIGLU || N % 32 != 0)))
+    return hipErrorInvalidValue;
   const int kp = (int)round_up((int64_t)K, 128);
   const int tiles_m = (int)ceil_div(M, F8_BM);
   const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : F8_BN);

@@ -138,6 +138,17 @@ def test_swiglu_fp8_parity(lib, n, C, F):
     # g = silu(a) b: errors in a and b enter through |silu'(a)| <= 1.1 and |silu(a)|
     S = 1.1 * np.abs(b) * _abs_products(h, w1) + np.abs(O.silu(a)) * _abs_products(h, w3)
     _close_bf16_product(g_got, g_ref, S, f"swiglu_fp8 gate product {n}x{C}x{F}")
+    # g's MX operand (from the up-projection's epilogue when F % 128 == 0, else a
+    # separate pass) is the MX quantization of the stored bf16 g, byte for byte
+    fp = -(-F // 128) * 128
+    up = lambda b: -(-b // 256) * 256
+    gq_off = up(n * F * 2)
+    gs_off = gq_off + up(n * fp)
+    g_dev = ws[:n * F * 2].view(torch.bfloat16).reshape(n, F)
+    ref_mx = lib.h3_mx_quantize(g_dev.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(ws[gq_off:gq_off + n * fp].reshape(n, fp), ref_mx.q)
+    assert torch.equal(ws[gs_off:gs_off + n * (fp // 32)].reshape(n, fp // 32), ref_mx.s)
     ref = x.astype(np.float64) + g.astype(np.float64) * _swiglu_ref(h, w1, w3, w2)
     got = host(out)
     # g is rounded to bf16 on both sides from values that differ in the last
