@@ -30,12 +30,20 @@ def _qk_case(wl, dtype, seed, n_rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", ["tiny", "tiny_pad", "h40d128"])
+@pytest.mark.parametrize("shape", ["tiny", "tiny_pad", "h40d128", "h16d64", "h3d128", "h24d128"])
 def test_qk_norm_rope_parity(lib, dtype, shape):
+    """Row walk (tokens of fewer than 256 16-byte chunks) and one work-group per
+    token (256 and more: 1, 3 and 5 chunks per thread)."""
     if shape == "tiny":
         wl, rows = W.TINY, None
     elif shape == "tiny_pad":
         wl, rows = W.TINY.replace(pad_to=520), None
+    elif shape == "h16d64":
+        wl, rows = W.TINY.replace(n_heads=16, dim=1024, pad_to=500), None
+    elif shape == "h3d128":
+        wl, rows = W.SHARE_10S.replace(n_heads=3), 700
+    elif shape == "h24d128":
+        wl, rows = W.SHARE_10S.replace(n_heads=24, dim=3072), 1000
     else:  # the 10 s share's head layout on the tail of the sequence (video, audio, pad rows)
         wl, rows = W.SHARE_10S, 3000
     pos, qkv, gq, gk = _qk_case(wl, dtype, seed=11, n_rows=rows)
