@@ -421,8 +421,13 @@ def frames_to_u8(frames, layout: int = 0) -> np.ndarray:
 # loss.  The pages give no algorithm.  Reading: Q (with the softmax scale and
 # log2 e folded in), K and V are stored as OCP e4m3 with one power-of-two
 # (E8M0) scale per 32 consecutive elements along the contraction (head dim
-# for Q and K, keys for V); the softmax probabilities are rounded to e4m3 on
-# the same grid as 256 * p.  Everything else is exact.
+# for Q and K, keys for V).  The softmax weights enter P.V as e4m3 values
+# too: with scores s in log2 units and M the smallest integer >= the row's
+# largest score, key j carries w_j = e4m3(2^(8 + s_j - M)) (nearest, ties to
+# even), and the output row is sum_j w_j v_j / sum_j w_j.  Because M is an
+# integer, w_j is 2^(8 - M) times the e4m3 rounding of 2^(s_j) wherever that
+# value is an e4m3 normal (w_j >= 2^-6), so any integer reference gives the
+# same weights there.  Everything else is exact.
 
 E4M3_MAX = 448.0
 
@@ -481,28 +486,52 @@ def fp8_fold(head_dim: int) -> np.float32:
     return np.float32(inv * np.float32(1.4426950408889634))
 
 
-def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, skip_log2=None):
-    """Attention over the MX-e4m3-quantized operands of the FP8 path, exact
-    otherwise (no rounding of the probabilities).  k, v [N, h, D] float32
-    values; q is [N, h, D], or [len(q_rows), h, D] already restricted to the
-    query rows q_rows (buffer rows).  Q is quantized after folding scale * log2(e); the scores are then
-    in log2 units, and softmax uses base 2.  The FP8 kernel differs from this
-    only by rounding 256 * p to e4m3 and by fp32 accumulation.
+def fp8_weights(sc) -> np.ndarray:
+    """The softmax weights of the FP8 path for score rows sc [r, n] (log2
+    units): w = e4m3(2^(8 + s - M)), M = ceil(row max) (see above).  The
+    largest weight of a row lies in [128, 256]; the output row is
+    (w @ v) / w.sum()."""
+    sc = _f64(sc)
+    m = np.ceil(sc.max(axis=-1, keepdims=True))
+    return e4m3_round(np.exp2(sc - m + 8.0))
+
+
+def _valid_row_mask(n_buf: int, cu, vl) -> np.ndarray:
+    mask = np.zeros(n_buf, dtype=bool)
+    for s in range(len(cu) - 1):
+        lo = int(cu[s])
+        mask[lo:lo + int(vl[s])] = True
+    return mask
+
+
+def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, skip_log2=None,
+                                  round_p: bool = True):
+    """Attention over the MX-e4m3-quantized operands of the FP8 path.  k, v
+    [N, h, D] float32 values; q is [N, h, D], or [len(q_rows), h, D] already
+    restricted to the query rows q_rows (buffer rows).  Q is quantized after
+    folding scale * log2(e); the scores are then in log2 units, and softmax
+    uses base 2.  round_p: the weights are fp8_weights of the scores (the
+    reading above); False keeps them exact (2^(s - max)), the attention of the
+    quantized operands alone.  Only rows inside a segment's valid range are
+    quantized (pad rows may hold anything, NaN included).
     skip_log2: apply the Skip-Softmax rule to the scores of the quantized
     operands; q_rows must then be whole query groups of each segment."""
     q = np.asarray(q, dtype=np.float32)
     D = q.shape[-1]
     c = float(fp8_fold(D))
+    N, h, _ = np.asarray(k).shape
     rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
-    # Q is quantized row by row: only the rows asked for are needed
-    qsel = q if q_rows is None or q.shape[0] == len(rows) else q[rows]
-    kq, ke = mx_quantize(k)
-    # V is quantized along the keys of each segment slot: blocks of 32 keys from the slot start
-    vt = np.asarray(v, dtype=np.float32)
-    N, h, _ = vt.shape
-    vdq = np.zeros((N, h, D))
     cu = np.asarray(cu_slots)
     vl = np.asarray(valid_len) if valid_len is not None else cu[1:] - cu[:-1]
+    valid = _valid_row_mask(N, cu, vl)
+    # Q is quantized row by row: only the rows asked for are needed, and only valid ones
+    qsel = q if q_rows is None or q.shape[0] == len(rows) else q[rows]
+    qsel = np.where(valid[rows][:, None, None], qsel, np.float32(0))
+    kv = np.where(valid[:, None, None], np.asarray(k, dtype=np.float32), np.float32(0))
+    kq, ke = mx_quantize(kv)
+    # V is quantized along the keys of each segment slot: blocks of 32 keys from the slot start
+    vt = np.asarray(v, dtype=np.float32)
+    vdq = np.zeros((N, h, D))
     for s in range(len(cu) - 1):
         lo, n = int(cu[s]), int(vl[s])
         if n == 0:
@@ -515,11 +544,12 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, ski
         vdq[lo:lo + n] = mx_dequantize(vq, ve).transpose(2, 0, 1)[:n]
     qd = mx_dequantize(*mx_quantize(qsel, fold=c))
     kd = mx_dequantize(kq, ke)
+    weights = fp8_weights if round_p else None
     if skip_log2 is not None:
         # the scores qd.kd are already in log2 units: scale 1/log2(e) cancels
         # the log2(e) the Skip-Softmax oracle applies
         return varlen_attention_skip(qd, kd, vdq, cu, vl, skip_log2, scale=1.0 / np.log2(np.e),
-                                     q_rows=None if q_rows is None else rows)
+                                     q_rows=None if q_rows is None else rows, weights=weights)
     out = np.zeros((len(rows), h, D))
     for s in range(len(cu) - 1):
         lo, n = int(cu[s]), int(vl[s])
@@ -528,8 +558,7 @@ def varlen_attention_fp8_operands(q, k, v, cu_slots, valid_len, q_rows=None, ski
             continue
         for hh in range(h):
             sc = qd[sel, hh] @ kd[lo:lo + n, hh].T                  # log2 units
-            sc -= sc.max(axis=1, keepdims=True)
-            p = np.exp2(sc)
+            p = fp8_weights(sc) if round_p else np.exp2(sc - sc.max(axis=1, keepdims=True))
             out[sel, hh] = (p @ vdq[lo:lo + n, hh]) / p.sum(axis=1, keepdims=True)
     return out
 
@@ -566,15 +595,21 @@ def linear_fp8_operands(x, w) -> np.ndarray:
 # the group, the block's largest score is more than |t| below the row's
 # running maximum over the blocks visited before it (scores in log2 units,
 # i.e. q.k * scale * log2 e; t < 0).  The first block is never skipped.  A
-# skipped key's weight is at most 2^t times the row's largest weight.
+# skipped key's weight is at most 2^t times the row's largest weight.  The
+# pages give no granularity either: the 64-key block and the 32-row group are
+# taken from the GPU kernels' own key tile and wave, so that a decision never
+# splits a tile or a wave (a reading fixed by the implementation, not by the
+# pages).
 
-def skip_softmax_rows(sc, v, skip_log2: float, q_group: int = 32, k_block: int = 64) -> np.ndarray:
+def skip_softmax_rows(sc, v, skip_log2: float, q_group: int = 32, k_block: int = 64,
+                      weights=None) -> np.ndarray:
     """Query rows of one segment and head under the rule above: sc [r, n]
     scores in log2 units of r consecutive query rows against the segment's n
     keys, v [n, D].  The rows start at a multiple of q_group from the segment
     start and hold whole groups (the segment's last group may be shorter).
     Returns the r output rows, each a base-2 softmax over the keys its group
-    keeps."""
+    keeps (weights: a function of the kept score rows giving their weights,
+    default 2^(s - row max))."""
     r, n = sc.shape
     out = np.zeros((r, v.shape[1]))
     for g0 in range(0, r, q_group):
@@ -589,14 +624,15 @@ def skip_softmax_rows(sc, v, skip_log2: float, q_group: int = 32, k_block: int =
             keep[blk] = True
             m_run = bmax if m_run is None else np.maximum(m_run, bmax)
         ss = sc[rows][:, keep]
-        p = np.exp2(ss - ss.max(axis=1, keepdims=True))
+        p = np.exp2(ss - ss.max(axis=1, keepdims=True)) if weights is None else weights(ss)
         out[rows] = (p @ v[keep]) / p.sum(axis=1, keepdims=True)
     return out
 
 
 def varlen_attention_skip(q, k, v, cu_slots, valid_len, skip_log2: float,
                           scale: Optional[float] = None, q_group: int = 32,
-                          k_block: int = 64, q_rows: Optional[np.ndarray] = None) -> np.ndarray:
+                          k_block: int = 64, q_rows: Optional[np.ndarray] = None,
+                          weights=None) -> np.ndarray:
     """Attention with the Skip-Softmax rule above; k, v [n_buf, H, D].
     Returns [n_buf, H, D] (rows outside every segment are 0) and applies the
     rule exactly in float64: a block is skipped or kept whole.
@@ -631,5 +667,6 @@ def varlen_attention_skip(q, k, v, cu_slots, valid_len, skip_log2: float,
                 "q_rows must be whole query groups"
             for head in range(h):
                 sc = (q[sel[a:b], head] @ k[lo:lo + n, head].T) * c   # log2 units
-                out[sel[a:b], head] = skip_softmax_rows(sc, v[lo:lo + n, head], skip_log2, q_group, k_block)
+                out[sel[a:b], head] = skip_softmax_rows(sc, v[lo:lo + n, head], skip_log2, q_group, k_block,
+                                                        weights)
     return out

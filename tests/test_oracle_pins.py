@@ -487,6 +487,42 @@ def test_student_loop_special_cases():
     assert np.allclose(z, bi.x - u, atol=1e-12)
 
 
+def test_timestep_modulation_closed_form():
+    """W_t2 silu(W_t1 e(sigma)) + table on weights chosen so every value has a
+    closed form.  At sigma = 0 the embedding is 128 ones then 128 zeros, so a
+    W_t1 row holding a/128 on the cosine half gives the pre-activation a; with
+    a = ln 3 the SiLU is ln 3 * sigmoid(ln 3) = (3/4) ln 3, with a = -ln 3 it
+    is -(1/4) ln 3, and silu(0) = 0.  W_t2 row (k, c) holds b[k, c] at column c
+    only, so slot k of channel c is b[k, c] silu(a_c) + table[block, k, c]."""
+    C = 6
+    ln3 = math.log(3.0)
+    a = np.array([ln3, -ln3, 0.0, ln3, -ln3, 2 * ln3])
+    silu_a = np.array([0.75 * ln3, -0.25 * ln3, 0.0, 0.75 * ln3, -0.25 * ln3, 2 * ln3 * 9 / 10])
+    w_t1 = np.zeros((C, 256))
+    w_t1[:, :128] = a[:, None] / 128.0
+    b = (np.arange(6 * C).reshape(6, C) + 1.0) * np.where(np.arange(C) % 2, -0.5, 0.25)
+    w_t2 = np.zeros((6 * C, C))
+    for k in range(6):
+        for c in range(C):
+            w_t2[k * C + c, c] = b[k, c]
+    table = rng.standard_normal((2, 6, C))
+    tw = W.TimestepWeights(w_t1=w_t1, w_t2=w_t2, table=table)
+    got = O.timestep_modulation(0.0, tw)
+    assert got.shape == (2, 6, C)
+    want = b[None] * silu_a[None, None, :] + table
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+    # at sigma = 0.75 a unit W_t1 row reads one embedding entry, cos(750) or
+    # sin(750); the SiLU is then torch's (a library routine)
+    w_t1 = np.zeros((C, 256))
+    w_t1[np.arange(C), [0, 128, 1, 129, 0, 128]] = [1.0, 1.0, 1.0, 1.0, -2.0, 3.0]
+    pre = np.array([math.cos(750.0), math.sin(750.0), math.cos(750.0 * 1e4 ** (-1 / 128)),
+                    math.sin(750.0 * 1e4 ** (-1 / 128)), -2 * math.cos(750.0), 3 * math.sin(750.0)])
+    tw = W.TimestepWeights(w_t1=w_t1, w_t2=w_t2, table=table)
+    got = O.timestep_modulation(0.75, tw)
+    want = b[None] * F.silu(t64(pre)).numpy()[None, None, :] + table
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-14)
+
+
 def test_block_gated_branch_enters_linearly():
     """Doubling W3 doubles the MLP update exactly (silu sits on the W1 branch)."""
     import dataclasses
@@ -723,6 +759,85 @@ def test_fp8_operand_attention_close_to_exact():
     assert diff.max() > 1e-4
 
 
+def test_fp8_weights_hand_derived():
+    """The FP8 path's softmax weights, e4m3(2^(8 + s - M)) with M = ceil(row
+    max), on scores whose values are worked out by hand: max 0.5 gives M = 1,
+    2^7.5 = 181.02 -> 176 (grid step 16 in [128, 256)), 2^6.5 = 90.51 -> 88
+    (step 8), 2^4.75 = 26.91 -> 26 (step 2); integer scores give exact powers
+    of two (the row max 256); a score 24 below an integer max lands in the
+    subnormal range (2^-16 -> 0)."""
+    np.testing.assert_array_equal(O.fp8_weights([[0.5, -0.5, -2.25]]), [[176.0, 88.0, 26.0]])
+    np.testing.assert_array_equal(O.fp8_weights([[0.0, -1.0, -3.0, 2.0]]), [[64.0, 32.0, 8.0, 256.0]])
+    np.testing.assert_array_equal(O.fp8_weights([[3.0, -5.0, -13.0, -14.0, -21.0]]),
+                                  [[256.0, 1.0, 2.0 ** -8, 2.0 ** -9, 0.0]])
+
+
+def test_fp8_weights_grid_and_shift_rules():
+    """Every weight is an e4m3 value (decoded from the byte definition) and the
+    nearest one to 2^(8 + s - M); the row's largest weight lies in [128, 256]
+    (2^(8 + max - M) is in (128, 256], and rounding can reach 128);
+    adding an integer to a row leaves its weights unchanged."""
+    grid = np.array(sorted({_e4m3_decode(c) for c in range(0x7F)}))
+    sc = rng.uniform(-12, 6, (40, 50))
+    w = O.fp8_weights(sc)
+    assert np.all(np.isin(w, grid))
+    x = np.exp2(sc - np.ceil(sc.max(1, keepdims=True)) + 8.0)
+    dist = np.abs(grid[None, None, :] - x[..., None])
+    assert np.all(np.abs(w - x) <= dist.min(-1) + 1e-12)
+    assert np.all((w.max(1) >= 128) & (w.max(1) <= 256))
+    np.testing.assert_array_equal(O.fp8_weights(sc + 3.0), w)
+    assert not np.array_equal(O.fp8_weights(sc + 0.37), w)
+
+
+def test_fp8_rounded_weights_attention_bound():
+    """Rounding the weights moves each output by at most
+    2 * 2^-4 / (1 - 2^-4) * max|v| when every weight is an e4m3 normal (each is
+    off by at most 2^-4 relative), and it does move it; the weights of a row
+    whose scores are integers are exact, so there the output is the
+    unrounded one."""
+    case = W.varlen_case(seed=5, lengths=(100, 37), n_buf=160, n_heads=2, head_dim=64, dtype="bf16")
+    args = (case.q, case.k, case.v, case.cu_slots, case.valid_len)
+    r = O.varlen_attention_fp8_operands(*args)
+    e = O.varlen_attention_fp8_operands(*args, round_p=False)
+    bound = 2 * 2.0 ** -4 / (1 - 2.0 ** -4) * np.abs(case.v).max()
+    assert np.abs(r - e).max() <= bound and np.abs(r - e).max() > 1e-4
+    # one query whose folded grid value meets each key in an integer score
+    g = np.random.default_rng(3)
+    d = 64
+    c = float(O.fp8_fold(d))
+    qd = np.zeros((1, 1, d))
+    qd[0, 0, 0] = 1.0
+    kd = np.zeros((9, 1, d))
+    kd[:, 0, 0] = [0, -1, 2, -3, 1, -6, 3, -2, 2]
+    vd = O.mx_dequantize(*O.mx_quantize(g.standard_normal((1, d, 32)).astype(np.float32)))[..., :9].transpose(2, 0, 1)
+    qin = (qd / c).astype(np.float32)
+    assert O.mx_dequantize(*O.mx_quantize(qin, fold=c))[0, 0, 0] == 1.0
+    qb = np.zeros((9, 1, d), np.float32)
+    qb[0] = qin[0]
+    cu, vl = np.array([0, 9]), np.array([9])
+    got = O.varlen_attention_fp8_operands(qb, kd.astype(np.float32), vd.astype(np.float32), cu, vl)
+    np.testing.assert_array_equal(got[0], O.varlen_attention_fp8_operands(
+        qb, kd.astype(np.float32), vd.astype(np.float32), cu, vl, round_p=False)[0])
+
+
+def test_fp8_operands_ignore_pad_rows():
+    """NaN and Inf in pad rows of q, k, v change nothing (only valid rows are
+    quantized), and no invalid cast happens on the way."""
+    case = W.varlen_case(seed=9, lengths=(70, 33), n_buf=128, n_heads=1, head_dim=64, dtype="bf16")
+    args = (case.cu_slots, case.valid_len)
+    base = O.varlen_attention_fp8_operands(case.q, case.k, case.v, *args)
+    valid = np.zeros(case.q.shape[0], bool)
+    for s in range(len(case.valid_len)):
+        valid[case.cu_slots[s]:case.cu_slots[s] + case.valid_len[s]] = True
+    q, k, v = (a.copy() for a in (case.q, case.k, case.v))
+    q[~valid], k[~valid], v[~valid] = np.nan, np.inf, -np.inf
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        got = O.varlen_attention_fp8_operands(q, k, v, *args)
+    np.testing.assert_array_equal(got, base)
+
+
 def test_mx_quantize_exact_on_representable_blocks():
     """Blocks already of the form e4m3 value x 2^E, with the largest magnitude in
     the top binade (224..448], come back unchanged, exponent and all."""
@@ -856,14 +971,22 @@ def test_fp8_skip_softmax_on_grid_operands_is_the_skip_rule():
     kd = O.mx_dequantize(*O.mx_quantize(k.astype(np.float32)))
     vq, ve = O.mx_quantize(v.astype(np.float32).transpose(1, 2, 0))   # blocks of 32 keys
     vd = O.mx_dequantize(vq, ve).transpose(2, 0, 1)
-    got = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-6.0)
+    got = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-6.0, round_p=False)
     # scores q.k in log2 units: scale 1/log2(e) undoes the oracle's own log2(e)
     want = O.varlen_attention_skip(qd, kd, vd, cu, vl, -6.0, scale=1.0 / np.log2(np.e))
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-9)
-    plain = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl)
+    plain = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, round_p=False)
     assert np.abs(got - plain).max() > 1e-6          # the far blocks were dropped
-    np.testing.assert_allclose(O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-1e9),
-                               plain, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-1e9,
+                                                               round_p=False), plain, rtol=0, atol=1e-12)
+    # with the weights rounded as the FP8 path stores them: the same rule, on the
+    # kept keys only, each row's weights e4m3(2^(8 + s - M)) of its kept scores
+    got_r = O.varlen_attention_fp8_operands(qin, kd, vd, cu, vl, skip_log2=-6.0)
+    keep = np.ones(n, bool)
+    keep[64:128] = keep[192:256] = False
+    sc = qd[:, 0] @ kd[keep, 0].T
+    wts = O.fp8_weights(sc)
+    np.testing.assert_allclose(got_r[:, 0], (wts @ vd[keep, 0]) / wts.sum(1, keepdims=True), rtol=0, atol=1e-12)
 
 
 def test_skip_softmax_sampled_groups_equal_the_full_result():
