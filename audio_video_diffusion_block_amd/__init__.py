@@ -118,8 +118,6 @@ _c_attn_skip = _sig("h3_varlen_attn_skip", ctypes.c_int,
 _c_attn8_skip = _sig("h3_varlen_attn_fp8_skip", ctypes.c_int,
                      [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32,
                       _f, _f, _p, _sz, _i32, _p])
-_c_mfma_probe = _sig("h3_mfma_rate_probe", ctypes.c_int, [_i32, _i32, _p, _i64, _p])
-_c_hbm_probe = _sig("h3_hbm_rate_probe", ctypes.c_int, [_i32, _p, _p, _i64, _i64, _i64, _p])
 _c_check_segments = _sig("h3_check_segments", ctypes.c_int, [_p, _p, _i32, _i64, _i32])
 _c_modmx = _sig("h3_modulate_mx", ctypes.c_int,
                 [_p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _f, _p])
@@ -139,7 +137,7 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
             "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip",
-            "h3_mfma_rate_probe", "h3_hbm_rate_probe", "h3_check_segments", "h3_modulate_mx")
+            "h3_check_segments", "h3_modulate_mx")
 
 
 def _status_string(st: int) -> str:
@@ -466,15 +464,6 @@ def h3_frames_to_u8(frames, out, layout: int = 0, stream=None):
     _check(_c_frames(_ptr(frames), B, T, H, W, _ptr(out), layout, _stream(stream)))
 
 
-def h3_mfma_rate_probe(out: torch.Tensor, iters: int, zero_operands: bool = False,
-                       stream=None) -> float:
-    """Launch the matrix-core rate probe into `out` (float32, a multiple of 512
-    elements: one 8-wave work-group per 512); returns the flop it performs."""
-    assert out.dtype == torch.float32 and out.is_contiguous()
-    _check(_c_mfma_probe(iters, int(bool(zero_operands)), _ptr(out), out.numel(), _stream(stream)))
-    return (out.numel() // 64) * iters * 4 * 32768.0
-
-
 def h3_check_segments(cu_slots, valid_len, n_buf: int, max_valid_len: int) -> None:
     """Check segment metadata given as host int32 arrays (numpy or CPU tensors);
     raises H3Error (H3_ERR_ARG) naming the first violated rule."""
@@ -486,23 +475,3 @@ def h3_check_segments(cu_slots, valid_len, n_buf: int, max_valid_len: int) -> No
         raise ValueError("valid_len must have one entry per segment")
     _check(_c_check_segments(cu.ctypes.data, None if vl is None else vl.ctypes.data, n_seg, n_buf,
                              max_valid_len))
-
-
-def h3_hbm_rate_probe(dst: torch.Tensor, src: torch.Tensor = None, row_chunks: int = 0,
-                      touch_chunks: int = 0, stream=None) -> float:
-    """Launch the HBM rate probe; returns the bytes it moves.  With `src`: copy
-    src -> dst (same byte size).  Without: read-modify-write `dst` in place,
-    viewed as rows of `row_chunks` 16-byte chunks of which the first
-    `touch_chunks` are touched."""
-    assert dst.is_contiguous() and (src is None or src.is_contiguous())
-    nbytes = dst.numel() * dst.element_size()
-    if src is not None:
-        if src.numel() * src.element_size() != nbytes or nbytes % 16:
-            raise ValueError("copy needs src and dst of one byte size, a multiple of 16")
-        _check(_c_hbm_probe(0, _ptr(src), _ptr(dst), 1, nbytes // 16, nbytes // 16, _stream(stream)))
-        return 2.0 * nbytes
-    if row_chunks <= 0 or nbytes % (16 * row_chunks):
-        raise ValueError("dst must hold whole rows of row_chunks 16-byte chunks")
-    rows = nbytes // (16 * row_chunks)
-    _check(_c_hbm_probe(1, None, _ptr(dst), rows, row_chunks, touch_chunks, _stream(stream)))
-    return 2.0 * 16 * rows * touch_chunks

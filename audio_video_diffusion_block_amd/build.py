@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libh3dit.so")
 SOURCES = ["h3_api.cpp", "k_qk_norm_rope.hip", "k_modres.hip", "k_gemm.hip", "k_gemm_fp8.hip",
-           "k_attn.hip", "k_misc.hip", "k_frames.hip", "k_probe.hip"]
+           "k_attn.hip", "k_misc.hip", "k_frames.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1000,41 +1000,4 @@ h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, i
                     "frames launch");
 }
 
-h3_status h3_mfma_rate_probe(int32_t iters, int32_t zero_operands, float* out, int64_t out_len,
-                             void* stream) {
-  g_err[0] = 0;
-  CHECK(iters >= 1 && iters <= 10000000, "iters must be in [1, 10^7]");
-  CHECK(zero_operands == 0 || zero_operands == 1, "zero_operands must be 0 or 1");
-  CHECK(out_len > 0 && out_len % 512 == 0 && out_len / 512 <= 65535,
-        "out_len must be a positive multiple of 512, at most 65535 * 512");
-  CHECK(out && aligned16(out), "out must be non-NULL, 16-byte aligned");
-  TRY(check_device());
-  return hip_status(launch_mfma_rate((int)(out_len / 512), iters, zero_operands, out,
-                                     (hipStream_t)stream),
-                    "mfma rate launch");
-}
-
-h3_status h3_hbm_rate_probe(int32_t mode, const void* src, void* dst, int64_t rows,
-                            int64_t row_chunks, int64_t touch_chunks, void* stream) {
-  g_err[0] = 0;
-  CHECK(mode == 0 || mode == 1, "mode must be 0 (copy) or 1 (read-modify-write in place)");
-  CHECK(rows >= 1 && row_chunks >= 1 && touch_chunks >= 1 && touch_chunks <= row_chunks,
-        "need rows >= 1 and 1 <= touch_chunks <= row_chunks");
-  CHECK(mode == 1 || touch_chunks == row_chunks, "copy needs touch_chunks == row_chunks");
-  CHECK((double)rows * (double)row_chunks <= 1.0e10 &&
-            (rows * touch_chunks + 255) / 256 <= 0x7fffffff,
-        "buffer too large");
-  CHECK(dst && aligned16(dst), "dst must be non-NULL, 16-byte aligned");
-  CHECK(mode == 1 || (src && aligned16(src)), "copy needs a non-NULL, 16-byte aligned src");
-  if (mode == 0) {
-    const uintptr_t sa = (uintptr_t)src, da = (uintptr_t)dst;
-    const uintptr_t nb = (uintptr_t)(rows * row_chunks * 16);
-    CHECK(sa + nb <= da || da + nb <= sa, "src and dst overlap");
-  }
-  TRY(check_device());
-  return hip_status(launch_hbm_rate(mode, src, dst, rows, row_chunks, touch_chunks,
-                                    (hipStream_t)stream),
-                    "hbm rate launch");
-}
-
 }  // extern "C"

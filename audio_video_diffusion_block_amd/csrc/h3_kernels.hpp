@@ -97,12 +97,6 @@ hipError_t launch_varlen_attn_fp8(int head_dim, const void* q, int64_t ld_q, con
                                   const int* valid, int n_seg, int max_len, float scale,
                                   float skip_log2, void* ws, hipStream_t s);
 
-// measurement aid: `blocks` work-groups of 8 waves, each wave `iters` rounds of
-// four 32x32x16 bf16 MFMAs; out gets blocks * 512 floats
-hipError_t launch_mfma_rate(int blocks, int iters, int zero, float* out, hipStream_t s);
-hipError_t launch_hbm_rate(int mode, const void* src, void* dst, int64_t rows, int64_t row,
-                           int64_t touch, hipStream_t s);
-
 // strides and group sizes in BYTES (multiples of 16)
 hipError_t launch_copy_rows(const void* src, int64_t ld_src, int64_t gs_src, void* dst,
                             int64_t ld_dst, int64_t gs_dst, int64_t rows, int groups,

@@ -119,39 +119,16 @@ class EventTimer:
         return s.elapsed_time(e) / reps  # ms per call
 
 
-def mfma_ceiling(h3, timer):
-    """bf16 matrix-core rate with no memory traffic (h3_mfma_rate_probe), one
-    8-wave work-group per CU as the attention kernel runs, for random and for
-    zero operands: the chip's clock, and so this rate, falls with operand
-    switching activity."""
-    import torch
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    out = torch.empty(n_cu * 512, dtype=torch.float32, device="cuda")
-    res = {}
-    for zero in (False, True):
-        h3.h3_mfma_rate_probe(out, 1000, zero)                     # warm
-        flop = h3.h3_mfma_rate_probe(out, 40000, zero)
-        ms = timer.time(lambda: h3.h3_mfma_rate_probe(out, 40000, zero), 3)
-        res["zero" if zero else "random"] = flop / ms / 1e9
-    return res
-
-
-def hbm_ceiling(h3, timer, n_rows, row_bytes, touch_bytes):
-    """HBM rates of the elementwise passes' two access patterns (h3_hbm_rate_probe):
-    a 1 GiB copy, and read-modify-write in place of the first `touch_bytes` of
-    each of `n_rows` rows of `row_bytes` (the q and k thirds of the QKV buffer,
-    the Q/K norm + RoPE pattern)."""
+def copy_rate(timer):
+    """HBM rate of a plain 1 GiB device-to-device copy (torch's copy kernel):
+    the practical ceiling the elementwise passes are read against; bytes =
+    read + written."""
     import torch
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
-    nb = h3.h3_hbm_rate_probe(b, a)
-    copy_ms = timer.time(lambda: h3.h3_hbm_rate_probe(b, a), 20, warm=2)
+    ms = timer.time(lambda: b.copy_(a), 20, warm=2)
     del a, b
-    buf = torch.zeros(n_rows * row_bytes, dtype=torch.uint8, device="cuda")
-    nr = h3.h3_hbm_rate_probe(buf, row_chunks=row_bytes // 16, touch_chunks=touch_bytes // 16)
-    rmw_ms = timer.time(lambda: h3.h3_hbm_rate_probe(buf, row_chunks=row_bytes // 16,
-                                                     touch_chunks=touch_bytes // 16), 20, warm=2)
-    return {"copy": nb / copy_ms / 1e6, "qk_rmw": nr / rmw_ms / 1e6}
+    return 2.0 * (1 << 30) / ms / 1e6
 
 
 def traffic_record():
@@ -605,22 +582,13 @@ def main():
                 "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "attn_fwd_bf16_pipe_kernel<128,8> (+ V transpose pass)",
                 "algorithmic_flop_per_launch": work["attn_flop"]}
-    ceil = mfma_ceiling(h3, timer)
-    mfma_ceiling_rec = {"bf16_random_operands_tflops": ceil["random"], "bf16_zero_operands_tflops": ceil["zero"],
-                        "attention_frac_of_random": attn_tflops / ceil["random"],
-                        "note": "h3_mfma_rate_probe: 8 waves per CU, four 32x32x16 bf16 MFMAs per round, no "
-                                "memory traffic; the published peak assumes 2.4 GHz, which the chip does not "
-                                "hold under switching operands"}
-
-    hbm = hbm_ceiling(h3, timer, wl.n_loc, 3 * H * D * 2, 2 * H * D * 2)
+    copy_gbps = copy_rate(timer)
     hbm_ceiling_rec = {
-        "copy_gbps": hbm["copy"], "qk_inplace_rmw_gbps": hbm["qk_rmw"],
-        "modnorm_frac_of_copy": breakdown["modnorm"]["GB/s"] / hbm["copy"],
-        "frames_u8_frac_of_copy": breakdown["frames_u8"]["GB/s"] / hbm["copy"],
-        "qk_norm_rope_frac_of_inplace_rmw": breakdown["qk_norm_rope"]["GB/s"] / hbm["qk_rmw"],
-        "note": "h3_hbm_rate_probe: 1 GiB copy with non-temporal accesses, and read-modify-write in place "
-                "of the q and k thirds of a bf16 [n_loc, 3, H, D] buffer (the Q/K norm + RoPE pattern); "
-                "bytes = read + written"}
+        "copy_gbps": copy_gbps,
+        "modnorm_frac_of_copy": breakdown["modnorm"]["GB/s"] / copy_gbps,
+        "qk_norm_rope_frac_of_copy": breakdown["qk_norm_rope"]["GB/s"] / copy_gbps,
+        "frames_u8_frac_of_copy": breakdown["frames_u8"]["GB/s"] / copy_gbps,
+        "note": "torch's device copy of 1 GiB; bytes = read + written"}
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -633,8 +601,7 @@ def main():
                    "ffn_dim": wl.ffn_dim, "head_slice": hc, "parallelism": "1 GPU (rank-share stand-in)"},
         "block_ms": step_ms, "attn_tflops": attn_tflops,
         "fused_op_gbps": {k: breakdown[k]["GB/s"] for k in ("modnorm", "qk_norm_rope", "frames_u8")},
-        "breakdown": breakdown, "roofline": roofline, "mfma_ceiling": mfma_ceiling_rec,
-        "hbm_ceiling": hbm_ceiling_rec,
+        "breakdown": breakdown, "roofline": roofline, "hbm_ceiling": hbm_ceiling_rec,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, w, bi, work)

@@ -476,44 +476,6 @@ h3_status h3_frames_to_u8(const void* frames, int64_t B, int64_t T, int64_t H, i
 h3_status h3_check_segments(const int32_t* cu_slots, const int32_t* valid_len, int32_t n_seg,
                             int64_t n_buf, int32_t max_valid_len);
 
-/* ------------------------------------------------------- measurement aid */
-
-/*
- * h3_mfma_rate_probe -- not a step of the method: the bf16 matrix-core rate
- * the chip sustains with no memory traffic, for reading the attention and
- * GEMM rates against.  Launches out_len / 512 work-groups of 8 waves (one per
- * CU is the attention kernel's occupancy); each wave runs `iters` rounds of
- * four independent 32x32x16 bf16 MFMAs, so the launch does
- * (out_len / 64) * iters * 4 * 32768 flop.  zero_operands = 1 multiplies
- * zeros (least switching), 0 fixed pseudo-random values in [-2, 2).
- *   out: device float [out_len], out_len a positive multiple of 512 and at
- *        most 65535 * 512; receives per-lane sums (their values carry no meaning).
- *   iters in [1, 10^7].  The caller times the launch on `stream`.
- *   Errors: H3_ERR_ARG on a bad size or pointer (nothing launched).
- */
-h3_status h3_mfma_rate_probe(int32_t iters, int32_t zero_operands, float* out, int64_t out_len,
-                             void* stream);
-
-/*
- * h3_hbm_rate_probe -- not a step of the method: the HBM rate of the access
- * patterns of the elementwise passes, for reading their GB/s against.  Works
- * in 16-byte chunks, one per thread.
- *   mode 0 (copy): dst[i] = src[i] for i < rows * row_chunks, non-temporal
- *          loads and stores; touch_chunks must equal row_chunks; src and dst
- *          must not overlap.  Moves 2 * 16 * rows * row_chunks bytes.
- *   mode 1 (read-modify-write in place): dst is rows x row_chunks chunks; the
- *          first touch_chunks of every row are read, changed (their first
- *          32-bit word is incremented) and written back; src is ignored.
- *          Moves 2 * 16 * rows * touch_chunks bytes.  With row_chunks =
- *          3*H*D*2/16 and touch_chunks = 2*H*D*2/16 this is the traffic
- *          pattern of h3_qk_norm_rope on a bf16 [n, 3, H, D] QKV buffer.
- *   Buffers: device, 16-byte aligned, owned by the caller; contents are
- *   overwritten.  The caller times the launch on `stream`.
- *   Errors: H3_ERR_ARG on a bad mode, size, pointer or overlap (nothing launched).
- */
-h3_status h3_hbm_rate_probe(int32_t mode, const void* src, void* dst, int64_t rows,
-                            int64_t row_chunks, int64_t touch_chunks, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

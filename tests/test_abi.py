@@ -293,30 +293,6 @@ def test_fp8_skip_softmax_argument_checks():
     assert h3._c_attn8_skip(*args(float("nan"), h3.H3_BF16)) == h3.H3_ERR_ARG
 
 
-def test_mfma_rate_probe_argument_checks():
-    import audio_video_diffusion_block_amd as h3
-    assert h3._c_mfma_probe(0, 0, FAKE, 512, None) == h3.H3_ERR_ARG
-    assert h3._c_mfma_probe(10, 2, FAKE, 512, None) == h3.H3_ERR_ARG
-    assert h3._c_mfma_probe(10, 0, FAKE, 500, None) == h3.H3_ERR_ARG
-    assert h3._c_mfma_probe(10, 0, FAKE, 512 * 65536, None) == h3.H3_ERR_ARG
-    assert h3._c_mfma_probe(10, 0, None, 512, None) == h3.H3_ERR_ARG
-
-
-def test_hbm_rate_probe_argument_checks():
-    """Bad mode, sizes, pointers and overlapping copies are refused before any launch."""
-    import audio_video_diffusion_block_amd as h3
-    other = FAKE + (1 << 20)
-    assert h3._c_hbm_probe(2, FAKE, other, 1, 16, 16, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(0, FAKE, other, 0, 16, 16, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(1, None, other, 4, 16, 17, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(1, None, other, 4, 16, 0, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(0, FAKE, other, 4, 16, 8, None) == h3.H3_ERR_ARG  # copy touches all
-    assert h3._c_hbm_probe(0, FAKE, FAKE + 16, 1, 16, 16, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(0, None, other, 1, 16, 16, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(1, None, None, 1, 16, 16, None) == h3.H3_ERR_ARG
-    assert h3._c_hbm_probe(1, None, FAKE + 8, 1, 16, 16, None) == h3.H3_ERR_ARG
-
-
 def test_check_segments_rules():
     """The host segment checker accepts well-formed metadata and names each rule it rejects."""
     import numpy as np
