@@ -905,9 +905,14 @@ __global__ __launch_bounds__(256) void transpose_quant_v_kernel(const bf16_t* __
 //    32 kb + 16 h + r -- exactly the byte (16 kb + r) the P.V MFMA expects in
 //    its B operand.  P never leaves registers.
 //  * The scores come out in log2 units (the softmax scale and log2 e are in
-//    Q).  The running max is raised whenever a tile exceeds it by more than
-//    0.75, so p <= 2^0.75 and 256 p <= 431 stays in e4m3 range.  The kernel
-//    computes 256 p = exp2(s - (m - 8)) directly and stores it as e4m3 with
+//    Q).  They are kept relative to m_ref = M - 8, where the reference M is an
+//    integer: the ceiling of the first tile's max, raised to the ceiling of a
+//    later tile's max whenever that exceeds M by more than 0.75, so every
+//    stored weight 2^(s - m_ref) = 256 * 2^(s - M) is at most 2^8.75 < 448.
+//    Because M is an integer, the e4m3 value of a weight is the same as for
+//    the reference ceil(row max) wherever it is an e4m3 normal, so the stored
+//    weights do not depend on the tiling, and each raise rescales O and the
+//    row sums by an exact power of two.  The weights are stored as e4m3 with
 //    scale byte 127.  The row sums come from the matrix pipe: one more P.V
 //    MFMA whose A operand is all e4m3 ones sums the stored weights of every
 //    query, so numerator and denominator see the same rounded 256 p.
@@ -1081,8 +1086,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  // Scores are kept relative to m_ref = m_run - 8: each score chain starts from
-  // negm (= -m_ref in all 16 registers), so exp2 of a score is 256 p.
+  // Scores are kept relative to m_ref = M - 8 (M an integer): each score chain
+  // starts from negm (= -m_ref in all 16 registers), so exp2 of a score is
+  // 256 * 2^(s - M).
   float m_ref = 0.f;
   float mt_rel = 8.f;        // SKIP: exact running max, relative to m_ref
   f32x16_t negm;
@@ -1111,11 +1117,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       skip = __all(!q_ok || mx < mt_rel + skip_log2);
       mt_rel = fmaxf(mt_rel, mx);
     }
-    const bool raise = mx > 8.75f;  // tile max above the running max + 0.75
+    const bool raise = mx > 8.75f;  // tile max above M + 0.75
     if (__any(raise)) {
       scaled_mfma_drain();
-      const float delta = raise ? mx - 8.0f : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      // M moves up by a whole number (>= 1): to the ceiling of the tile max
+      const float delta = raise ? ceilf(mx - 8.0f) : 0.f;
+      const float alpha = __builtin_ldexpf(1.0f, -(int)delta);
       m_ref += delta;
       if constexpr (SKIP) mt_rel -= delta;
 #pragma unroll
@@ -1237,7 +1244,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
   compute_s(0, sa);
   if (n_tiles == 1) mask_tile(sa, 0);
   {
-    // first reference: the exact max of S(0) minus 8 (finite: a tile has a valid key)
+    // first reference: M = ceil(max of S(0)) (finite: a tile has a valid key)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -1245,7 +1252,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
-    m_ref = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) - 8.0f;
+    mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    m_ref = ceilf(mx) - 8.0f;
+    if constexpr (SKIP) mt_rel = mx - m_ref;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sa[0][r] -= m_ref;

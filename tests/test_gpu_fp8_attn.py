@@ -2,8 +2,9 @@
 
 The quantized operands are compared byte for byte with the oracle's quantizer
 (read back from the documented workspace layout); the output is compared with
-the oracle's attention over the same quantized operands and with the exact
-attention, within tolerances that follow from e4m3's 3-bit mantissa."""
+the oracle's FP8 attention (the same quantized operands, and the softmax
+weights rounded to e4m3 against an integer reference) at the bf16 bar, and
+with exact attention within a bound that follows from e4m3's 3-bit mantissa."""
 import numpy as np
 import pytest
 import torch
@@ -15,12 +16,16 @@ from _util import E4M3_DECODE as _E4M3, dev, dev_i32, host
 pytestmark = pytest.mark.gpu
 
 # tolerances (outputs are O(1) means of unit-variance values):
-#   vs the oracle on the same quantized operands, the kernel differs only by
-#   rounding 256 p to e4m3 (relative 2^-4 per weight, averaged over the keys)
-#   and fp32 accumulation;
-#   vs exact attention, the e4m3 rounding of q, k and v adds relative 2^-4 per
-#   element to scores and values.
-TOL_Q = dict(max_abs=6e-2, mean_abs=4e-3)
+#   vs the oracle's FP8 attention: both store the same e4m3 weights (the
+#   kernel's integer reference gives the oracle's rounding grid), so what
+#   remains is the kernel's fp32 scores (a weight whose 2^(s - M) sits within
+#   ~1e-6 of an e4m3 midpoint can round the other way), the matrix pipe's fp32
+#   accumulation and the final bf16 rounding: the bf16 bar.  A CPU emulation
+#   of the kernel's arithmetic on these cases gives max-abs 4e-3 - 7e-3 and
+#   mean-abs 1e-4 - 2.5e-4;
+#   vs exact attention, the e4m3 rounding of q, k, v and the weights adds
+#   relative 2^-4 per element to scores, values and weights.
+TOL_Q = dict(max_abs=2e-2, mean_abs=2e-3)
 TOL_X = dict(max_abs=1.5e-1, mean_abs=1.5e-2)
 
 
@@ -120,9 +125,12 @@ def test_fp8_attention_8k_three_segments(lib):
         assert np.array_equal(alone, got[lo:lo + n])
 
 
-def test_fp8_attention_10s_share_sampled(lib):
-    """5 heads x 128 over the 246,208-row buffer of the 10 s request, sampled rows."""
-    wl = W.SHARE_10S
+@pytest.mark.parametrize("wl", [W.SHARE_10S, W.LOOP_15S], ids=["share10s", "loop15s"])
+def test_fp8_attention_share_sampled(lib, wl):
+    """5 heads x 128 over the attention buffer of the 10 s request (246,208
+    rows) and of the 15 s request (367,296 rows, the shape the student-loop
+    benchmark times the FP8 path at), sampled rows."""
+    print(f"fp8 attention {wl.name}: n_buf={wl.n_pad_total}", flush=True)
     bi = W.block_inputs(wl, 0, "bf16")
     hc, D = wl.head_count, wl.head_dim
     qa = dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), "bf16")
@@ -137,11 +145,14 @@ def test_fp8_attention_10s_share_sampled(lib):
     # Near-uniform attention over random values: the output is a mean of ~2.5e5
     # terms, and a uniform relative rounding of 2^-4 / sqrt(3) = 3.6% on each
     # weight (P) or value (V) adds the same relative error to it.  Against the
-    # quantized-operand oracle only the P rounding remains (bound 6%); against
-    # exact attention P and V add up (sqrt(2) x 3.6%, plus the scores: bound 8%).
+    # oracle's FP8 attention, which rounds the same weights on the same grid,
+    # none of that remains: the bf16 relative bar (emulating the kernel's
+    # arithmetic on these rows gives 0.22%; leaving the weights unrounded in the
+    # oracle would give 2.6%).  Against exact attention P and V add up
+    # (sqrt(2) x 3.6%, plus the scores: bound 8%).
     ref_q = O.varlen_attention_fp8_operands(q[rows], k, v, bi.cu_slots, bi.valid_len, q_rows=rows)
     rel_q = np.linalg.norm(got - ref_q) / np.linalg.norm(ref_q)
-    assert rel_q < 6e-2, rel_q
+    assert rel_q < 1e-2, rel_q
     ref = O.varlen_attention(q[rows], k, v, bi.cu_slots, bi.valid_len, q_rows=rows)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel < 8e-2, rel

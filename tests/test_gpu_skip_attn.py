@@ -116,7 +116,10 @@ def test_skip_10s_share_random_inputs_skip_nothing(lib):
 
 # the FP8 attention bar against the quantized-operand oracle: the e4m3 rounding
 # of 256 p (up to 2^-4 relative per weight) leaves a few percent relative L2
-TOL_Q = dict(max_abs=6e-2, mean_abs=4e-3, rel_l2=6e-2)
+# FP8 path: against the oracle's FP8 attention with the rule (same e4m3
+# weights on the same grid), the bf16 bar; a CPU emulation of the kernel's
+# arithmetic on these cases gives max-abs 1.5e-3 - 5e-3, relative L2 0.18%
+TOL_Q = dict(max_abs=2e-2, mean_abs=2e-3, rel_l2=1e-2)
 
 
 def _run8(lib, q, k, v, cu, vl, H, D, skip_log2):
