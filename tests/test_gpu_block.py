@@ -154,15 +154,15 @@ def test_block_fp8_attention(lib, case):
     """Block with the MX-e4m3 attention path, update-dominant inputs so that the
     attention branch shows in x2.
 
-    Against the oracle block whose attention quantizes its own float64 q, k, v:
-    elementwise at the bf16 block bar, relative L2 within 5%.  The e4m3 rounding
-    of an operand element is decided by its low bits, so the kernel's bf16 q, k,
-    v (relative 2^-9 from the oracle's) round to the other e4m3 neighbour (a 2^-3
-    relative step) for a few percent of the elements; on these inputs, rounding
-    the oracle's own q, k, v to bf16 before quantizing moves x2 by 2.0% (world 1)
-    and 0.8% (rank share) relative L2, which the 5% bound covers together with
-    the bf16 block error.  Against the exact oracle block: relative L2 within 8%
-    (the quantized-operand oracle itself is 4.0% / 3.1% from it)."""
+    Against the oracle block whose FP8 attention quantizes its own float64 q,
+    k, v: elementwise at the bf16 block bar, relative L2 within 5%.  The e4m3
+    rounding of an operand element is decided by its low bits, so the kernel's
+    bf16 q, k, v (relative 2^-9 from the oracle's) round to the other e4m3
+    neighbour (a 2^-3 relative step) for a few percent of the elements; on these
+    inputs, rounding the oracle's own q, k, v to bf16 before quantizing moves x2
+    by 3.1% (world 1) and 1.7% (rank share) relative L2, which the 5% bound
+    covers together with the bf16 block error.  Against the exact oracle block:
+    relative L2 within 8% (the FP8 oracle block itself is 4.5% / 3.6% from it)."""
     rank = {"world1": None, "share_r2": 2, "peer_r3": 3}[case]
     wl = W.TINY if rank is None else W.TINY.replace(sp_degree=4, rank=rank)
     w = W.block_weights(wl, 4, "bf16")
@@ -241,3 +241,117 @@ def test_block_skip_softmax_option(lib, case, fp8):
         got = run_block(lib, wl, w, bi, "bf16", x_override=x, mod_override=mod, peer=peer,
                         attn_fp8=fp8, attn_skip_log2=t)
         assert np.array_equal(got, base), (case, t)
+
+
+def _skip_share_case(seed=0, t=-3.0):
+    """Rank 2 of a 4-rank tiny share whose other ranks' attention rows follow a
+    concentrated pattern: their queries are 4 e0 + N(0, 0.05^2); keys N(0, 1),
+    except in the 64-key blocks 1, 2 and 6 (other ranks' rows only), whose keys
+    are -c e0 + N(0, 0.05^2), scoring ~4.5 log2 units below the rest, and whose
+    values are 4 + N(0, 0.05^2).  With t = -3 the other ranks' query groups skip
+    those blocks; this rank's own query rows (q and k from the block's own
+    projection, norm and RoPE) keep every block.  Returns the inputs and the
+    oracle's attention buffer: q of every row, and k, v as the block sees them."""
+    wl = W.TINY.replace(sp_degree=4, rank=2)
+    w = W.block_weights(wl, 4, "bf16")
+    bi = W.block_inputs(wl, 4, "bf16")
+    N, hc, D = wl.n_pad_total, wl.head_count, wl.head_dim
+    g = np.random.default_rng(seed)
+    e0 = np.zeros(D)
+    e0[0] = 1.0
+    c = 4.5 / (4.0 * np.log2(np.e) / np.sqrt(D))
+    fill = np.empty((N, 3, hc, D))
+    fill[:, 0] = 4.0 * e0 + 0.05 * g.standard_normal((N, hc, D))
+    fill[:, 1] = g.standard_normal((N, hc, D))
+    fill[:, 2] = g.standard_normal((N, hc, D))
+    for b in (1, 2, 6):
+        fill[b * 64:(b + 1) * 64, 1] = -c * e0 + 0.05 * g.standard_normal((64, hc, D))
+        fill[b * 64:(b + 1) * 64, 2] = 4.0 + 0.05 * g.standard_normal((64, hc, D))
+    bi.qkv_attn = W.round_to_bf16(fill.astype(np.float32))
+    x, mod = _update_dominant(bi)
+    cap = {}
+
+    def capture(q, k, v, cu, vl, q_rows=None):
+        cap.update(k=k, v=v)
+        return O.varlen_attention(q, k, v, cu, vl, q_rows=q_rows)
+
+    it = O.dit_block(x, mod, w, bi.pos, bi.cu_slots, bi.valid_len, O.BlockShape.of(wl), bi.qkv_attn,
+                     bi.o_local, intermediates=True, attention=capture)
+    q = np.asarray(bi.qkv_attn[:, 0], np.float64).copy()
+    q[wl.tok_begin:wl.tok_begin + wl.n_loc] = it["q"]
+    return wl, w, bi, x, mod, q, cap["k"], cap["v"]
+
+
+def _skip_margin(q, k, cu, vl, t, scale_log2):
+    """Smallest distance (log2 units) of any group-block decision of the skip
+    rule from its threshold, and the number of skipped group-blocks."""
+    margin, skipped = np.inf, 0
+    for s in range(len(cu) - 1):
+        lo, n = int(cu[s]), int(vl[s])
+        for h in range(q.shape[1]):
+            sc = (q[lo:lo + n, h] @ k[lo:lo + n, h].T) * scale_log2
+            for g0 in range(0, n, 32):
+                rows = slice(g0, min(g0 + 32, n))
+                m = sc[rows, 0:64].max(1)
+                for b0 in range(64, n, 64):
+                    d = np.max(sc[rows, b0:b0 + 64].max(1) - (m + t))
+                    margin = min(margin, abs(d))
+                    if d < 0:
+                        skipped += 1
+                    else:
+                        m = np.maximum(m, sc[rows, b0:b0 + 64].max(1))
+    return margin, skipped
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16_attn", "fp8_attn"])
+def test_block_skip_softmax_takes_skips(lib, fp8):
+    """The block with Skip-Softmax on inputs where the rule really skips: the
+    block's attention output over the whole exchange buffer (o_attn) against
+    the oracle's R29 rule applied to the oracle block's own q, k, v, and x2
+    against the oracle block.  Every decision sits >= 0.3 log2 units from the
+    threshold (checked on the oracle's scores; on the FP8 path on the scores
+    of the quantized float64 and of the quantized bf16-rounded operands), far
+    beyond the ~0.03 by which the kernel's bf16 q and k move a score."""
+    t = -3.0
+    wl, w, bi, x, mod, q, k, v = _skip_share_case()
+    cu, vl = bi.cu_slots, bi.valid_len
+    r16 = lambda a: W.round_to_bf16(np.asarray(a, np.float32))
+    if fp8:
+        cf = float(O.fp8_fold(wl.head_dim))
+        for src in (lambda a: a, r16):
+            qq = O.mx_dequantize(*O.mx_quantize(np.asarray(src(q), np.float32), fold=cf))
+            kq = O.mx_dequantize(*O.mx_quantize(np.asarray(src(k), np.float32)))
+            margin, skipped = _skip_margin(qq, kq, cu, vl, t, 1.0)
+            assert margin >= 0.3 and skipped >= 20, (margin, skipped)
+        ref = O.varlen_attention_fp8_operands(q, k, v, cu, vl, skip_log2=t)
+        ref16 = O.varlen_attention_fp8_operands(r16(q), r16(k), r16(v), cu, vl, skip_log2=t)
+        plain = O.varlen_attention_fp8_operands(q, k, v, cu, vl)
+    else:
+        margin, skipped = _skip_margin(q, k, cu, vl, t, np.log2(np.e) / np.sqrt(wl.head_dim))
+        assert margin >= 0.3 and skipped >= 20, (margin, skipped)
+        ref = ref16 = O.varlen_attention_skip(q, k, v, cu, vl, t)
+        plain = O.varlen_attention(q, k, v, cu, vl)
+    extra = share_buffers(wl, bi, "bf16")
+    xd = dev(x, "bf16")
+    lib.h3_dit_block_forward(cfg_of(lib, wl, "bf16", attn_fp8=fp8, attn_skip_log2=t),
+                             weights_dev(w, "bf16"), xd, dev(mod, "bf16"), dev_i32(bi.pos),
+                             dev_i32(cu), dev_i32(vl), int(vl.max()), **extra)
+    torch.cuda.synchronize()
+    hc, D = wl.head_count, wl.head_dim
+    got = host(extra["o_attn"]).reshape(-1, hc, D)
+    what = "block skip o_attn " + ("fp8" if fp8 else "bf16")
+    # FP8: the kernel quantizes its own bf16 q, k, v, whose e4m3 rounding can
+    # fall on the other neighbour where the float64 values' does not (the two
+    # oracles differ by max-abs 0.036, relative L2 0.4% here)
+    assert_close(got, ref16, "bf16", what, **(dict(max_abs=4e-2) if fp8 else {}))
+    if fp8:
+        assert_close(got, ref, "bf16", what + " vs float64 sources", max_abs=6e-2, rel_l2=2e-2)
+    # the skips were taken: far closer to the rule's result than to attention without it
+    assert np.abs(got - plain).mean() > 10 * np.abs(got - ref16).mean()
+    x2 = O.dit_block(x, mod, w, bi.pos, cu, vl, O.BlockShape.of(wl), bi.qkv_attn, bi.o_local,
+                     attention=lambda *a, q_rows=None: ref16[q_rows])
+    if fp8:
+        # as in test_block_fp8_attention: elementwise at the bf16 bar, relative L2 within 5%
+        assert_close(host(xd), x2, "bf16", what + " x2", rel_l2=5e-2)
+    else:
+        check_block(host(xd), x2, x, "bf16", what + " x2", update=True)

@@ -162,11 +162,14 @@ def test_swiglu_fp8_parity(lib, n, C, F):
     assert_close(got - x, ref - x, "bf16", "swiglu_fp8 update", max_abs=4e-2, rel_l2=2e-2)
 
 
-def test_fp8_projections_10s_shapes_sampled(lib):
-    """The block's projection shapes at the 10 s share (30,776 rows, C = 5120,
-    F = 13,824): QKV and the SwiGLU MLP, full launches; sampled rows (and, for
-    QKV, sampled output columns, each a weight row quantized on its own) checked."""
-    n, C, F = 30776, 5120, 13824
+@pytest.mark.parametrize("n", [30776, 45912], ids=["share10s", "loop15s"])
+def test_fp8_projections_share_shapes_sampled(lib, n):
+    """The block's projection shapes at the 10 s share (30,776 rows) and the
+    15 s share (45,912 rows, the loop benchmark's), C = 5120, F = 13,824: QKV
+    and the SwiGLU MLP, full launches; sampled rows (and, for QKV, sampled
+    output columns, each a weight row quantized on its own) checked."""
+    print(f"fp8 projections n={n}", flush=True)
+    C, F = 5120, 13824
     rows = np.sort(W.uniform_ints(6, "rows", 0, n - 1, 24))
     rows[-1] = n - 1
     h = _bf16(6, "h", (n, C))
@@ -179,7 +182,7 @@ def test_fp8_projections_10s_shapes_sampled(lib):
     cols = np.unique(np.concatenate([W.uniform_ints(6, "cols", 0, 3 * C - 1, 600), [0, 3 * C - 1]]))
     got = host(qkv[torch.from_numpy(rows).cuda()])[:, cols]
     _close_bf16_product(got, O.linear_fp8_operands(h[rows], wq[cols]), _abs_products(h[rows], wq[cols]),
-                        "qkv 10 s sampled")
+                        f"qkv n={n} sampled")
     del qkv, wqm
     w1 = _bf16(6, "w1", (F, C), std=C ** -0.5)
     w3 = _bf16(6, "w3", (F, C), std=C ** -0.5)
@@ -189,7 +192,7 @@ def test_fp8_projections_10s_shapes_sampled(lib):
     lib.h3_swiglu_fp8(hm, *mx, out)
     torch.cuda.synchronize()
     got = host(out[torch.from_numpy(rows).cuda()])
-    assert_close(got, _swiglu_ref(h, w1, w3, w2, rows), "bf16", "swiglu_fp8 10 s sampled", max_abs=4e-2)
+    assert_close(got, _swiglu_ref(h, w1, w3, w2, rows), "bf16", f"swiglu_fp8 n={n} sampled", max_abs=4e-2)
 
 
 @pytest.mark.parametrize("rows,dim,per_token,norm_kind", [(333, 256, True, 0), (70, 384, False, 0),

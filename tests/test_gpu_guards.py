@@ -78,6 +78,20 @@ def test_canaries_qk_norm_rope_and_attention(lib):
     lib.h3_qk_norm_rope(qkv[:, :H * D], qkv[:, H * D:2 * H * D], H, D, g, g, pos, wl.sections)
     cq("qk_norm_rope")
     assert torch.equal(qkv[:, 2 * H * D:], v_before), "qk_norm_rope wrote into v"
+    # one work-group per token (2 H D / 8 >= 256 chunks): H = 16 and 20 at D = 128,
+    # a window of the 10 s positions with video, audio and pad rows
+    for Hb in (16, 20):
+        wb = W.SHARE_10S.replace(n_heads=Hb, dim=Hb * 128)
+        pb = W.positions(wb)[-300:]
+        nb, Db = len(pb), 128
+        qb, cqb = guarded((nb, 3 * Hb * Db), bf)
+        qb.copy_(rand((nb, 3 * Hb * Db), bf, 12))
+        vb = qb[:, 2 * Hb * Db:].clone()
+        gb = (1 + rand((Db,), bf, 13, 0.02))
+        lib.h3_qk_norm_rope(qb[:, :Hb * Db], qb[:, Hb * Db:2 * Hb * Db], Hb, Db, gb, gb, dev_i32(pb),
+                            wb.sections)
+        cqb(f"qk_norm_rope per-token H={Hb}")
+        assert torch.equal(qb[:, 2 * Hb * Db:], vb), "qk_norm_rope wrote into v"
     case = W.varlen_case(seed=0, lengths=(300, 45, 17), n_buf=512, n_heads=2, head_dim=128)
     q, k, v = (dev(a.reshape(case.n_buf, -1), "bf16") for a in (case.q, case.k, case.v))
     o, co = guarded((case.n_buf, 2 * 128), bf, fill=7.0)
