@@ -76,7 +76,7 @@ def _sig(name, res, args):
 
 _lib.h3_abi_version.restype = ctypes.c_int
 # the ctypes structures below mirror this version of include/h3dit.h
-ABI_VERSION = 5
+ABI_VERSION = 6
 if _lib.h3_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {_lib.h3_abi_version()}, the binding "
                       f"expects {ABI_VERSION}: rebuild it")
@@ -90,6 +90,9 @@ _c_attn_ws = _sig("h3_varlen_attn_workspace_size", _sz, [_i64, _i32, _i32, _i32,
 _c_attn = _sig("h3_varlen_attn", ctypes.c_int,
                [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _f,
                 _p, _sz, _i32, _p])
+_c_attn_na = _sig("h3_varlen_attn_noalloc", ctypes.c_int,
+                  [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _f,
+                   _i32, _p])
 _c_modres = _sig("h3_modulate_residual", ctypes.c_int,
                  [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _i32, _i32, _f, _i32, _p])
 _c_linear = _sig("h3_linear", ctypes.c_int,
@@ -137,7 +140,7 @@ EXPORTED = ("h3_abi_version", "h3_status_string", "h3_last_error", "h3_qk_norm_r
             "h3_euler_update", "h3_frames_to_u8", "h3_varlen_attn_fp8_workspace_size",
             "h3_varlen_attn_fp8", "h3_mx_quantize", "h3_linear_fp8", "h3_swiglu_fp8_workspace_size",
             "h3_swiglu_fp8", "h3_varlen_attn_skip", "h3_varlen_attn_fp8_skip",
-            "h3_check_segments", "h3_modulate_mx")
+            "h3_check_segments", "h3_modulate_mx", "h3_varlen_attn_noalloc")
 
 
 def _status_string(st: int) -> str:
@@ -221,6 +224,21 @@ def h3_varlen_attn(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tens
                    n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
                    softmax_scale, _ptr(ws), ws.numel() * ws.element_size(), _dt(q),
                    _stream(stream)))
+
+
+def h3_varlen_attn_noalloc(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tensor,
+                           valid_len: Optional[torch.Tensor], max_valid_len: int,
+                           softmax_scale: float = 0.0, stream=None):
+    """h3_varlen_attn with the library's own fixed scratch (no workspace, no
+    allocation; NOALLOC_SCRATCH_BYTES per device, shared by every call)."""
+    n_buf = q.shape[0]
+    n_seg = cu_slots.shape[0] - 1
+    _check(_c_attn_na(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
+                      n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
+                      softmax_scale, _dt(q), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def h3_varlen_attn_skip(q, k, v, o, n_heads: int, head_dim: int, cu_slots, valid_len,

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/h3dit.h"
@@ -124,7 +125,8 @@ h3_status validate_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t n_to
 h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k, const void* v,
                         int64_t ld_v, void* o, int64_t ld_o, int64_t n_buf, int32_t H,
                         int32_t D, const int32_t* cu, int32_t n_seg, int32_t max_len,
-                        void* ws, size_t ws_bytes, h3_dtype dt, bool fp8 = false) {
+                        void* ws, size_t ws_bytes, h3_dtype dt, bool fp8 = false,
+                        bool ws_from_library = false) {
   TRY(check_dtype(dt));
   CHECK(n_buf >= 0 && n_buf < (int64_t)INT32_MAX, "n_buf out of range");
   CHECK(H > 0, "n_heads must be positive");
@@ -141,6 +143,7 @@ h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k
   CHECK(ld_q > 0 && ld_k > 0 && ld_v > 0 && ld_o > 0, "row strides must be positive");
   // the bf16 kernel addresses a 64-row key tile and the transposed-V scratch with 32-bit byte offsets
   CHECK(ld_k <= (1 << 23) && n_buf <= (1 << 22), "row stride above 2^23 or n_buf above 2^22");
+  if (ws_from_library) return H3_OK;
   const size_t need = fp8 ? h3::attn_fp8_workspace_bytes(n_buf, H, D, n_seg)
                          : h3::attn_workspace_bytes(dt == H3_BF16, n_buf, H, D, n_seg);
   if (ws_bytes < need)
@@ -265,6 +268,39 @@ int64_t swiglu_fp8_parts(int64_t n_tok, int32_t ffn_dim, int64_t* g_q, int64_t* 
 
 }  // namespace
 
+// Scratch of h3_varlen_attn_noalloc (the transposed copy of v): one copy per
+// device, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel: it is a host-side stand-in for the device variable;
+// its device address comes from hipGetSymbolAddress, once per device.
+static constexpr size_t kNoAllocScratchBytes = (size_t)H3_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::once_flag g_scratch_once[64];
+void* g_scratch_ptr[64];
+hipError_t g_scratch_err[64];
+
+// device address of `scratch` on the current device (looked up on the first
+// call on that device, with the device current)
+h3_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(H3_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return hip_status(g_scratch_err[dev], "hipGetSymbolAddress of the no-allocation scratch");
+  if (!g_scratch_ptr[dev] || ((uintptr_t)g_scratch_ptr[dev] & 255u) != 0)
+    return fail(H3_ERR_HIP, "no-allocation scratch: bad device address");
+  *out = g_scratch_ptr[dev];
+  return H3_OK;
+}
+}  // namespace
+
 using namespace h3;
 
 extern "C" {
@@ -328,6 +364,33 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
                                        ld_o, n_buf, n_heads, cu_slots, valid_len, n_seg,
                                        max_valid_len, scale, ws, (hipStream_t)stream),
                     "varlen_attn launch");
+}
+
+h3_status h3_varlen_attn_noalloc(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                                 const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                                 int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                 const int32_t* cu_slots, const int32_t* valid_len,
+                                 int32_t n_seg, int32_t max_valid_len, float softmax_scale,
+                                 h3_dtype dtype, void* stream) {
+  g_err[0] = 0;
+  TRY(validate_attn(q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_buf, n_heads, head_dim, cu_slots, n_seg,
+                    max_valid_len, nullptr, 0, dtype, false, true));
+  if (n_buf == 0) return H3_OK;
+  const size_t need = attn_workspace_bytes(dtype == H3_BF16, n_buf, n_heads, head_dim, n_seg);
+  if (need > kNoAllocScratchBytes)
+    return fail(H3_ERR_WORKSPACE,
+                "h3_varlen_attn_noalloc: this call needs %zu bytes of scratch, above the fixed "
+                "%zu (n_heads x head_dim x (n_buf + 128 (n_seg + 1)) x 2 bytes); use "
+                "h3_varlen_attn with a workspace",
+                need, kNoAllocScratchBytes);
+  TRY(check_device());
+  void* ws = nullptr;
+  TRY(scratch_of_current_device(&ws));
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  return hip_status(launch_varlen_attn(dtype == H3_BF16, head_dim, q, ld_q, k, ld_k, v, ld_v, o,
+                                       ld_o, n_buf, n_heads, cu_slots, valid_len, n_seg,
+                                       max_valid_len, scale, ws, (hipStream_t)stream),
+                    "varlen_attn_noalloc launch");
 }
 
 h3_status h3_varlen_attn_skip(const void* q, int64_t ld_q, const void* k, int64_t ld_k,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 5
+#define H3_ABI_VERSION 6
 
 typedef enum {
   H3_OK = 0,
@@ -129,6 +129,35 @@ h3_status h3_varlen_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_
                          const int32_t* valid_len, int32_t n_seg, int32_t max_valid_len,
                          float softmax_scale, void* ws, size_t ws_bytes, h3_dtype dtype,
                          void* stream);
+
+/*
+ * h3_varlen_attn_noalloc -- h3_varlen_attn with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and error behaviour as h3_varlen_attn, except:
+ *   - the transposed copy of v lives in a device array inside the library,
+ *     H3_NOALLOC_SCRATCH_BYTES (64 MiB) per device, held until the process
+ *     ends; a call needing more (n_heads * head_dim * (round_up(n_buf, 64) +
+ *     128 (n_seg + 1)) * 2 bytes for bf16; fp32 needs none) returns
+ *     H3_ERR_WORKSPACE and launches nothing;
+ *   - every call on one device shares that array (one per device in each
+ *     process): calls of one process that overlap in time on one device (on
+ *     different streams, or from different threads) race and give undefined
+ *     results; calls in stream order are safe, since each call writes every
+ *     scratch byte it reads before reading it;
+ *   - it never calls hipMalloc, hipFree or another allocating routine; the
+ *     first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress) once;
+ *   - it does not run the H3_DEBUG_VALIDATE check (that check copies to the
+ *     host and synchronises).
+ */
+#define H3_NOALLOC_SCRATCH_BYTES (64ull << 20)
+h3_status h3_varlen_attn_noalloc(const void* q, int64_t ld_q, const void* k, int64_t ld_k,
+                                 const void* v, int64_t ld_v, void* o, int64_t ld_o,
+                                 int64_t n_buf, int32_t n_heads, int32_t head_dim,
+                                 const int32_t* cu_slots, const int32_t* valid_len,
+                                 int32_t n_seg, int32_t max_valid_len, float softmax_scale,
+                                 h3_dtype dtype, void* stream);
 
 /*
  * h3_varlen_attn_skip -- h3_varlen_attn with Skip-Softmax (MiniMax H3 通过

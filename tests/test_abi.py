@@ -341,3 +341,18 @@ def test_modulate_mx_argument_checks():
     assert call(nk=2) == h3.H3_ERR_ARG
     assert call(x=FAKE + 8) == h3.H3_ERR_ARG
     assert call(n=0, x=None, q=None) == h3.H3_OK
+
+
+def test_noalloc_attention_argument_checks():
+    """The no-allocation attention validates like h3_varlen_attn and refuses, on
+    the host, a call whose transposed v exceeds its fixed scratch."""
+    import audio_video_diffusion_block_amd as h3
+
+    def call(n_buf=8192, H=8, D=128, q=FAKE, n_seg=3, dt=1):
+        return h3._c_attn_na(q, H * D, FAKE, H * D, FAKE, H * D, FAKE, H * D, n_buf, H, D, FAKE,
+                             None, n_seg, min(n_buf, 4032), 0.0, dt, None)
+    assert call(q=None) == h3.H3_ERR_ARG and "q is NULL" in h3.last_error()
+    assert call(D=96) == h3.H3_ERR_UNSUPPORTED
+    big = h3.NOALLOC_SCRATCH_BYTES // (8 * 128 * 2) + 64
+    assert call(n_buf=big) == h3.H3_ERR_WORKSPACE and "scratch" in h3.last_error()
+    assert call(n_buf=0) == h3.H3_OK                     # empty call: nothing to do
