@@ -370,6 +370,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   constexpr int K_ELEMS = KT * KS;
   constexpr int STAGE = K_ELEMS + D * VS;
   constexpr int NSTAGE = 4;
+  // The softmax scale and log2(e) are folded into Q once (one fp32 product,
+  // rounded to bf16), and every score chain starts from -m (negm, the running
+  // max in all 16 registers) instead of 0: scores leave the matrix pipe in
+  // log2 units relative to the running max, ready for v_exp_f32, with no VALU
+  // work per score before the exp.
   __shared__ __attribute__((aligned(16))) bf16_t smem[NSTAGE * STAGE];
 
   const int s = blockIdx.y;
@@ -394,7 +399,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       uint4 val = q_ok ? *reinterpret_cast<const uint4*>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, val);
+      bf16x8_t x = __builtin_bit_cast(bf16x8_t, val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * scale_log2);
+      qf[kk] = x;
     }
   }
 
@@ -459,8 +467,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;
-  float m_true = -INFINITY;  // SKIP: exact running max (log2 units)
+  f32x16_t negm;             // -(running max) in every register
+  float mt_rel = 0.f;        // SKIP: exact running max, relative to the running max
   float l_a = 0.f, l_b = 0.f;
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
   const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -482,33 +490,45 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
         if (key >= len) sc[kb][r] = -INFINITY;
       }
   };
-  // raise the running max to the tile max if it exceeds it by more than 8
-  // (log2 units) and rescale O and l; skipped on most tiles
-  auto update_max = [&](float mx) -> float {
+  // mx: the lane's largest score of the tile (sc) relative to the running
+  // max.  SKIP: the tile is skipped when every valid row's max is more than
+  // |skip_log2| below its exact running max (mt_rel); a skipped tile's scores
+  // become -inf, so its weights are exactly 0.  Then the running max is raised
+  // to the tile max when that exceeds it by more than 8 (2^8 bound on the
+  // unnormalised weights), rescaling O and l and shifting sc, negm and mt_rel;
+  // skipped on most tiles.  Returns whether the tile is skipped.
+  auto update_max = [&](float mx, f32x16_t (&sc)[2]) -> bool {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-    const float mx_s = mx * scale_log2;
-    const bool raise = mx_s > m_run + 8.0f;
+    bool skip = false;
+    if constexpr (SKIP) {
+      skip = __all(!q_ok || mx < mt_rel + skip_log2);
+      mt_rel = fmaxf(mt_rel, mx);
+    }
+    const bool raise = mx > 8.0f;
     if (__any(raise)) {
-      const float m_new = raise ? mx_s : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      const float delta = raise ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_a *= alpha;
       l_b *= alpha;
+      if constexpr (SKIP) mt_rel -= delta;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        negm[r] -= delta;
+        sc[0][r] -= delta;
+        sc[1][r] -= delta;
+      }
     }
-    return mx_s;
-  };
-  // SKIP: whether the tile whose row max is mx_s (log2 units) is skipped; the
-  // running max then takes it in
-  auto skip_decision = [&](float mx_s) -> bool {
-    const bool row_skips = !q_ok || mx_s < m_true + skip_log2;
-    const bool skip = __all(row_skips);
-    m_true = fmaxf(m_true, mx_s);
+    if constexpr (SKIP) {
+      if (skip)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = -INFINITY;
+    }
     return skip;
   };
 
@@ -523,12 +543,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   bf16x8_t vf[4];
   constexpr int NA = 2 * (D / 16);  // phase A MFMAs: 2 key blocks x D/16 k-steps
   constexpr int NB = 4 * (D / 32);  // phase B MFMAs: 4 key groups x D/32 d blocks
-  // SKIP: the softmax of a skipped tile runs with +inf in place of the
-  // running max, so its weights are exactly 0 and its row sums unchanged
-  // (branch-free: a branch per slot costs more than the VALU work it saves)
+  // SKIP: the softmax of a skipped tile runs on -inf scores, so its weights
+  // are exactly 0 and its row sums unchanged (branch-free: a branch per slot
+  // costs more than the VALU work it saves)
   auto phase_a = [&](int stage_k, f32x16_t (&nxt)[2], int stage_v, f32x16_t (&cur)[2], int jt,
                      bool skip) {
-    const float m_sub = (SKIP && skip) ? INFINITY : m_run;
     const bf16_t* sk = smem + stage_k * STAGE;
     // the wave in this (VALU-heavy) phase wins issue arbitration against the
     // other wave of its SIMD, whose P.V MFMAs then fill the matrix pipe
@@ -538,15 +557,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     bf16x8_t kf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[i] = kfrag(sk, i >> 1, i & 1);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nxt[0][r] = nxt[1][r] = 0.f;
     // Slot i: one MFMA of S(next), the fma/exp of softmax slice i and the
     // pack/row-sum of slice i-1 (so a pack never waits on the exp it consumes:
     // in-order issue would stall the wave there).
     float pe[2][SL][2];  // exp results in flight, by slot parity
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+      nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1],
+                                                          i < 2 ? negm : nxt[i & 1], 0, 0, 0);
       if (i + 4 < NA) kf[i & 3] = kfrag(sk, (i + 4) >> 1, (i + 4) & 1);
       else {
         const int pidx = i + 4 - NA;  // first P.V fragments of phase B
@@ -556,8 +574,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       for (int sl = 0; sl < SL; ++sl) {
         const int slice = i * SL + sl;
         const int g = slice >> 2, t = slice & 3, kb = g >> 1, half = g & 1;
-        pe[i & 1][sl][0] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t], scale_log2, -m_sub));
-        pe[i & 1][sl][1] = __builtin_amdgcn_exp2f(fmaf(cur[kb][half * 8 + 2 * t + 1], scale_log2, -m_sub));
+        pe[i & 1][sl][0] = __builtin_amdgcn_exp2f(cur[kb][half * 8 + 2 * t]);
+        pe[i & 1][sl][1] = __builtin_amdgcn_exp2f(cur[kb][half * 8 + 2 * t + 1]);
       }
       if (i > 0) {
 #pragma unroll
@@ -610,10 +628,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (jt + 1 < n_tiles) {
-      const float mx_s = update_max(mx);
-      if constexpr (SKIP) return skip_decision(mx_s);
-    }
+    if (jt + 1 < n_tiles) return update_max(mx, nxt);
     return false;
   };
 
@@ -633,7 +648,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[kb][r]);
-    m_true = update_max(mx);  // the first tile is never skipped
+    // the first reference: the exact max of S(0) (finite: a tile has a valid
+    // key); the first tile is never skipped
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    const float m0 = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sa[0][r] -= m0;
+      sa[1][r] -= m0;
+      negm[r] = -m0;
+    }
   }
   if (n_tiles > 2) load_tile(2);
 
