@@ -839,6 +839,19 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                       "activation quantization");
   };
   auto wmx = [&](int i) { return f8 ? mx_of(&w->mx[i]) : MxOperand{}; };
+  // A3 in the QKV projection's store epilogue (bf16 K % 64 and MX kernels):
+  // Q/K RMSNorm + RoPE of the local rows before q and k leave the work-group
+  GemmMap qkv_map;
+  const bool fuse_qk = bf && C % 64 == 0 && (D == 64 || D == 128);
+  if (fuse_qk) {
+    qkv_map.qk_pos = (const int4*)io->pos;
+    qkv_map.qk_gq = (const bf16_t*)w->g_q;
+    qkv_map.qk_gk = (const bf16_t*)w->g_k;
+    qkv_map.qk_H = H;
+    qkv_map.qk_D = D;
+    qkv_map.qk_eps = cfg->eps_qk;
+    qkv_map.qk_tab = make_rope_tab(D, cfg->sec_t, cfg->sec_h, cfg->theta);
+  }
   if (peer) {
     // Peer-major exchange layout: every all-to-all block is contiguous.
     const int P = H / hc, r = hb / hc;
@@ -846,7 +859,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
     char* send = (char*)io->qkv_send;
     const int64_t blk = n * 3 * sd * es;  // bytes of one peer block of qkv_send
     // A2 qkv = h1 w_qkv^T, scattered by its epilogue into [P][n][3][hc][D]
-    GemmMap scatter;
+    GemmMap scatter = qkv_map;
     scatter.peer_H = H;
     scatter.peer_hc = hc;
     scatter.peer_D = D;
@@ -861,7 +874,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
                      "qkv projection (peer-major)"));
     }
     // A3 Q/K RMSNorm + RoPE on the local rows, one launch per peer block
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < P && !fuse_qk; ++p) {
       char* b = send + p * blk;
       TRY(hip_status(launch_qk_norm_rope(bf, D, b, 3 * sd, b + sd * es, 3 * sd, n, hc, w->g_q,
                                          w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
@@ -902,18 +915,20 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   if (f8) {
     if (!mx_norm) TRY(quant_act(h1, C, C));
     TRY(hip_status(launch_gemm_mx8(EPI_STORE, xq, wmx(0), MxOperand{}, qkv, 3 * hd, nullptr, 0, n,
-                                   (int)(3 * hd), C, s),
+                                   (int)(3 * hd), C, s, qkv_map),
                    "qkv projection (fp8)"));
   } else {
     TRY(hip_status(launch_gemm(bf, EPI_STORE, h1, C, w->w_qkv, nullptr, C, qkv, 3 * hd, nullptr,
-                               0, n, (int)(3 * hd), C, s),
+                               0, n, (int)(3 * hd), C, s, qkv_map),
                    "qkv projection"));
   }
-  // A3 Q/K RMSNorm + RoPE on the local rows
-  TRY(hip_status(launch_qk_norm_rope(bf, D, qkv, 3 * hd, qkv + hd * es, 3 * hd, n, H, w->g_q,
-                                     w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
-                                     cfg->eps_qk, s),
-                 "qk_norm_rope"));
+  // A3 Q/K RMSNorm + RoPE on the local rows (a pass of its own where the
+  // projection's epilogue does not take it)
+  if (!fuse_qk)
+    TRY(hip_status(launch_qk_norm_rope(bf, D, qkv, 3 * hd, qkv + hd * es, 3 * hd, n, H, w->g_q,
+                                       w->g_k, io->pos, cfg->sec_t, cfg->sec_h, cfg->theta,
+                                       cfg->eps_qk, s),
+                   "qk_norm_rope"));
   const void* o_for_proj;
   if (!share) {
     // A5 attention straight from the QKV buffer

@@ -108,6 +108,19 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
       }
     __syncthreads();
     constexpr int CPR = OC / 8;  // 16-byte chunks per row
+    // Q/K RMSNorm + RoPE (EPI_STORE of a QKV projection): a thread always
+    // handles the same 8 columns (chunk tid % CPR of its rows), so its gains
+    // and rotation pairs are fixed; the D/8 chunks of a head row sit in
+    // adjacent lanes of one row of 16 lanes, whose DPP sum gives the norm
+    const int qk_hd = map.qk_H * map.qk_D;
+    float qk_gq[8], qk_gk[8];
+    RopeLane qk_rl;
+    if (EPI == EPI_STORE && map.qk_pos) {
+      const int cd = ((tid % CPR) * 8) % map.qk_D;  // first dim of the thread's 8 columns in its head
+      Vec8<bf16_t>::load(map.qk_gq + cd, qk_gq);
+      Vec8<bf16_t>::load(map.qk_gk + cd, qk_gk);
+      qk_rl = rope_lane(map.qk_tab, cd / 8);
+    }
 #pragma unroll 4
     for (int i = 0; i < 256 * CPR / W4_THREADS; ++i) {
       const int chunk = tid + i * W4_THREADS;
@@ -122,6 +135,30 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
         const int h = (col - which * hd) / map.peer_D, d = col - which * hd - h * map.peer_D;
         const int p = h / map.peer_hc, j = h - p * map.peer_hc;
         po = C + (((int64_t)p * M + row) * 3 + which) * map.peer_hc * map.peer_D + j * map.peer_D + d;
+      }
+      if (EPI == EPI_STORE && map.qk_pos && col < 2 * qk_hd) {
+        // a q or k head column: the row's position decides (uniform over the head's lanes)
+        const int4 ps = map.qk_pos[row];
+        if (ps.x == 0 || ps.x == 1) {
+          float v[8], cs[4], sn[4];
+          const uint4 raw = *reinterpret_cast<const uint4*>(src);
+          const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(u[e] << 16);
+            v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+          }
+          rope_cos_sin(qk_rl, ps, cs, sn);
+          if (map.qk_D == 128) qk_norm_rope_lane<16>(v, col < qk_hd ? qk_gq : qk_gk, cs, sn, map.qk_eps);
+          else qk_norm_rope_lane<8>(v, col < qk_hd ? qk_gq : qk_gk, cs, sn, map.qk_eps);
+          uint4 out;
+          out.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+          out.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          out.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+          out.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+          *reinterpret_cast<uint4*>(po) = out;
+          continue;
+        }
       }
       if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
       else for (int e = 0; col + e < N; ++e) po[e] = src[e];

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "h3_rope.hpp"
+
 namespace h3 {
 
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2 };
@@ -42,7 +44,18 @@ struct GemmMap {
   int64_t mx_ld = 0;
   uint8_t* mx_s = nullptr;
   int64_t mx_lds = 0;
-  bool empty() const { return a_kgroup == 0 && peer_hc == 0 && mx_q == nullptr; }
+  // EPI_STORE of a QKV projection (N = 3*qk_H*qk_D, qk_D in {64, 128}): the q
+  // and k head columns (n < 2*qk_H*qk_D) of rows whose qk_pos kind is video or
+  // audio get Q/K RMSNorm (gains qk_gq, qk_gk) and RoPE before they are
+  // stored, from their bf16-rounded values, exactly as the standalone pass
+  // would; other rows and the v columns are stored as computed
+  const int4* qk_pos = nullptr;
+  const bf16_t* qk_gq = nullptr;
+  const bf16_t* qk_gk = nullptr;
+  int qk_H = 0, qk_D = 0;
+  float qk_eps = 0.f;
+  RopeTab qk_tab{};
+  bool empty() const { return a_kgroup == 0 && peer_hc == 0 && mx_q == nullptr && qk_pos == nullptr; }
 };
 
 // out = A @ B^T with epilogue; for EPI_SWIGLU, B = W1, B3 = W3 and N = features

@@ -7,64 +7,33 @@
 // HBM-bound pass.  A head row (D values) is owned by D/8 adjacent lanes, 8
 // values (16 bytes of bf16) per lane, so four consecutive head rows of a token
 // are one contiguous 1 KiB wave access.  The sum of squares is reduced across
-// the D/8 lanes with DPP.  A lane always owns the same 4 RoPE pairs; the
-// work-group derives the pairs' inverse frequencies once, and a lane
+// the D/8 lanes with DPP.  A lane always owns the same 4 RoPE pairs, whose
+// per-position rotations come from the host-computed table (h3_rope.hpp), and
 // recomputes cos/sin only when its token changes (each work-group walks a
-// contiguous run of rows, so that happens every 2H/(256/(D/8)) rows).  A lane
+// contiguous run of rows, so that happens every 2H/(256/(D/8)) rows).  The
+// arithmetic is the one the QKV projection's fused epilogue uses, so both
+// give the same bits.  A lane
 // takes U rows per step (SLOTS rows apart) and issues their loads before
 // processing the first; loads and stores carry the non-temporal hint.  On a
 // [n, 3, H, D] bf16 buffer this runs at the rate of a plain in-place
 // read-modify-write of the same q and k regions.
 #include "h3_common.hpp"
 #include "h3_kernels.hpp"
+#include "h3_rope.hpp"
 
 namespace h3 {
 
 template <typename T, int D, int U>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     T* __restrict__ q, int64_t ld_q, T* __restrict__ k, int64_t ld_k, int64_t n_tok, int n_heads,
-    const T* __restrict__ g_q, const T* __restrict__ g_k, const int4* __restrict__ pos, int sec_t,
-    int sec_h, double log2_theta, float eps, int64_t rows_per_block) {
+    const T* __restrict__ g_q, const T* __restrict__ g_k, const int4* __restrict__ pos,
+    RopeTab tab, float eps, int64_t rows_per_block) {
   constexpr int L = D / 8;          // lanes per head row
   constexpr int SLOTS = 256 / L;    // head rows in flight per work-group
   const int lane = threadIdx.x % L;
   const int slot = threadIdx.x / L;
+  const RopeLane rl = rope_lane(tab, lane);
 
-  // Inverse frequency of every rotation pair, in double and rounded once to
-  // float, computed once per work-group (one thread per pair) and shared
-  // through LDS.  This lane's 4 pairs are 4*lane .. 4*lane+3 (dims 8*lane ..
-  // 8*lane+7).
-  __shared__ float f_tab[2][D / 2];  // [0] video (per-axis sections), [1] audio
-  auto axis_of = [&](int p, int& jj, int& width) {
-    if (p < sec_t / 2) {
-      jj = p; width = sec_t;
-      return 0;
-    }
-    if (p < (sec_t + sec_h) / 2) {
-      jj = p - sec_t / 2; width = sec_h;
-      return 1;
-    }
-    jj = p - (sec_t + sec_h) / 2; width = D - sec_t - sec_h;
-    return 2;
-  };
-  if (threadIdx.x < D / 2) {
-    const int p = threadIdx.x;
-    int jj, width;
-    axis_of(p, jj, width);
-    f_tab[0][p] = (float)exp2(-2.0 * jj / width * log2_theta);
-    f_tab[1][p] = (float)exp2(-2.0 * p / D * log2_theta);
-  }
-  __syncthreads();
-  float f_vid[4], f_aud[4];
-  int axis[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = 4 * lane + j;
-    int jj, width;
-    axis[j] = axis_of(p, jj, width);
-    f_vid[j] = f_tab[0][p];
-    f_aud[j] = f_tab[1][p];
-  }
   float gq[8], gk[8];
   Vec8<T>::load(g_q + 8 * lane, gq);
   Vec8<T>::load(g_k + 8 * lane, gk);
@@ -102,28 +71,10 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
         cur_tok = tok[u];
         const int4 p = pos[cur_tok];
         kind = p.x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int pv = axis[j] == 0 ? p.y : (axis[j] == 1 ? p.z : p.w);
-          const float ang = kind == 1 ? (float)p.y * f_aud[j] : (float)pv * f_vid[j];
-          sincosf(ang, &sn[j], &cs[j]);
-        }
+        rope_cos_sin(rl, p, cs, sn);
       }
       if (kind != 0 && kind != 1) continue;  // pad row: untouched
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ss += v[u][i] * v[u][i];
-      ss = group_sum<L>(ss);
-      const float rinv = rsqrtf(ss * (1.0f / D) + eps);
-      const float* g = is_k[u] ? gk : gq;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] * rinv * g[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = v[u][2 * j], b = v[u][2 * j + 1];
-        v[u][2 * j] = a * cs[j] - b * sn[j];
-        v[u][2 * j + 1] = a * sn[j] + b * cs[j];
-      }
+      qk_norm_rope_lane<L>(v[u], is_k[u] ? gk : gq, cs, sn, eps);
       Vec8<T>::store_nt(ptr[u], v[u]);
     }
   }
@@ -138,8 +89,8 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
 template <typename T, int D, int CPT>
 __global__ __launch_bounds__(256) void qk_norm_rope_tok_kernel(
     T* __restrict__ q, int64_t ld_q, T* __restrict__ k, int64_t ld_k, int n_heads,
-    const T* __restrict__ g_q, const T* __restrict__ g_k, const int4* __restrict__ pos, int sec_t,
-    int sec_h, double log2_theta, float eps) {
+    const T* __restrict__ g_q, const T* __restrict__ g_k, const int4* __restrict__ pos,
+    RopeTab tab, float eps) {
   constexpr int L = D / 8;  // lanes per head row
   const int64_t tok = blockIdx.x;
   const int lane = threadIdx.x % L;
@@ -159,25 +110,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_tok_kernel(
       Vec8<T>::load_nt(ptr[i], v[i]);
     }
   }
-  // this thread's 4 pairs: frequencies in double, rounded once to float
+  // this thread's 4 pairs
   float cs[4], sn[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = 4 * lane + j;
-    int a, jj, width;
-    if (p < sec_t / 2) {
-      a = 0; jj = p; width = sec_t;
-    } else if (p < (sec_t + sec_h) / 2) {
-      a = 1; jj = p - sec_t / 2; width = sec_h;
-    } else {
-      a = 2; jj = p - (sec_t + sec_h) / 2; width = D - sec_t - sec_h;
-    }
-    const float f = ps.x == 1 ? (float)exp2(-2.0 * p / D * log2_theta)
-                              : (float)exp2(-2.0 * jj / width * log2_theta);
-    const int pv = a == 0 ? ps.y : (a == 1 ? ps.z : ps.w);
-    const float ang = ps.x == 1 ? (float)ps.y * f : (float)pv * f;
-    sincosf(ang, &sn[j], &cs[j]);
-  }
+  rope_cos_sin(rope_lane(tab, lane), ps, cs, sn);
   float gq[8], gk[8];
   Vec8<T>::load(g_q + 8 * lane, gq);
   Vec8<T>::load(g_k + 8 * lane, gk);
@@ -186,20 +121,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_tok_kernel(
     const int c = threadIdx.x + i * 256;
     if (c < chunks) {
       const bool is_k = c / L >= n_heads;
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
-      ss = group_sum<L>(ss);
-      const float rinv = rsqrtf(ss * (1.0f / D) + eps);
-      const float* g = is_k ? gk : gq;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * rinv * g[e];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = v[i][2 * j], bb = v[i][2 * j + 1];
-        v[i][2 * j] = a * cs[j] - bb * sn[j];
-        v[i][2 * j + 1] = a * sn[j] + bb * cs[j];
-      }
+      qk_norm_rope_lane<L>(v[i], is_k ? gk : gq, cs, sn, eps);
       Vec8<T>::store_nt(ptr[i], v[i]);
     }
   }
@@ -215,11 +137,12 @@ static hipError_t launch_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_
   const int64_t rows_per_block = (int64_t)SLOTS * 8;  // two steps of four rows per lane
   const int64_t blocks = ceil_div(total, rows_per_block);
   const int64_t chunks = 2 * (int64_t)n_heads * L;
+  const RopeTab tab = make_rope_tab(D, sec_t, sec_h, theta);
   if (chunks >= 256 && chunks <= 8 * 256 && n_tok <= 0x7fffffff) {
 #define H3_QKT(CPT)                                                                             \
   hipLaunchKernelGGL((qk_norm_rope_tok_kernel<T, D, CPT>), dim3((unsigned)n_tok), dim3(256), 0, s, \
                      (T*)q, ld_q, (T*)k, ld_k, n_heads, (const T*)g_q, (const T*)g_k,            \
-                     (const int4*)pos, sec_t, sec_h, log2((double)theta), eps);                  \
+                     (const int4*)pos, tab, eps);                                                \
   return hipGetLastError()
     switch ((int)ceil_div(chunks, 256)) {
       case 1: H3_QKT(1);
@@ -235,7 +158,7 @@ static hipError_t launch_qk(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_
   }
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, 4>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (T*)q, ld_q, (T*)k, ld_k, n_tok, n_heads, (const T*)g_q, (const T*)g_k,
-                     (const int4*)pos, sec_t, sec_h, log2((double)theta), eps, rows_per_block);
+                     (const int4*)pos, tab, eps, rows_per_block);
   return hipGetLastError();
 }
 

@@ -355,3 +355,44 @@ def test_block_skip_softmax_takes_skips(lib, fp8):
         assert_close(host(xd), x2, "bf16", what + " x2", rel_l2=5e-2)
     else:
         check_block(host(xd), x2, x, "bf16", what + " x2", update=True)
+
+
+@pytest.mark.parametrize("case", ["tiny_d64", "d128_padded"])
+def test_block_equals_boundary_composition(lib, case):
+    """The block, whose QKV projection applies Q/K RMSNorm + RoPE in its store
+    epilogue, equals bit for bit the same steps made of the boundary's own
+    calls: modulated norm, QKV projection, the standalone Q/K RMSNorm + RoPE
+    pass, attention, gated output projection, modulated norm, SwiGLU with gated
+    residual.  World 1, bf16; 64-wide heads, and 128-wide heads with suffix pad
+    rows and a partial last row tile (520 rows)."""
+    if case == "tiny_d64":
+        wl = W.TINY
+    else:
+        wl = W.TINY.replace(dim=512, head_dim=128, ffn_dim=1408, sections=(32, 48, 48), pad_to=520)
+    w = W.block_weights(wl, 6, "bf16")
+    bi = W.block_inputs(wl, 6, "bf16")
+    got = run_block(lib, wl, w, bi, "bf16")
+    H, D, n = wl.n_heads, wl.head_dim, wl.n_loc
+    hd = H * D
+    wd = weights_dev(w, "bf16")
+    x = dev(bi.x, "bf16")
+    mod = dev(bi.mod, "bf16")
+    pos, cu, vl = dev_i32(bi.pos), dev_i32(bi.cu_slots), dev_i32(bi.valid_len)
+    h1 = torch.empty_like(x)
+    lib.h3_modulate_residual(x, shift=mod[:, 0], scale=mod[:, 1], h_out=h1, eps=wl.eps_mod)
+    qkv = torch.empty((n, 3 * hd), dtype=torch.bfloat16, device="cuda")
+    lib.h3_linear(h1, wd["w_qkv"], qkv)
+    lib.h3_qk_norm_rope(qkv[:, :hd], qkv[:, hd:2 * hd], H, D, wd["g_q"], wd["g_k"], pos, wl.sections,
+                        wl.theta, wl.eps_qk)
+    o = torch.empty((n, hd), dtype=torch.bfloat16, device="cuda")
+    lib.h3_varlen_attn(qkv[:, :hd], qkv[:, hd:2 * hd], qkv[:, 2 * hd:], o, H, D, cu, vl,
+                       int(bi.valid_len.max()))
+    lib.h3_linear(o, wd["w_o"], x, gate=mod[:, 2])
+    h2 = torch.empty_like(x)
+    lib.h3_modulate_residual(x, shift=mod[:, 3], scale=mod[:, 4], h_out=h2, eps=wl.eps_mod)
+    lib.h3_swiglu(h2, wd["w1"], wd["w3"], wd["w2"], x, gate=mod[:, 5])
+    torch.cuda.synchronize()
+    composed = host(x)
+    assert np.array_equal(got, composed), f"{case}: max diff {np.abs(got - composed).max():.3g}"
+    # and both are the oracle's block at the bf16 bar
+    assert_close(got, oracle_block(wl, w, bi), "bf16", f"block {case}")
