@@ -76,7 +76,7 @@ def _sig(name, res, args):
 
 _lib.h3_abi_version.restype = ctypes.c_int
 # the ctypes structures below mirror this version of include/h3dit.h
-ABI_VERSION = 6
+ABI_VERSION = 7
 if _lib.h3_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {_lib.h3_abi_version()}, the binding "
                       f"expects {ABI_VERSION}: rebuild it")
@@ -101,7 +101,7 @@ _c_swiglu_ws = _sig("h3_swiglu_workspace_size", _sz, [_i64, _i32, _i32])
 _c_swiglu = _sig("h3_swiglu", ctypes.c_int,
                  [_p, _i64, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i32, _i32, _p, _sz, _i32, _p])
 _c_block_ws = _sig("h3_dit_block_workspace_size", _sz,
-                   [ctypes.POINTER(BlockConfig), _i64, _i64, _i32])
+                   [ctypes.POINTER(BlockConfig), _i64, _i64, _i32, _i32])
 _c_block = _sig("h3_dit_block_forward", ctypes.c_int,
                 [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), ctypes.POINTER(BlockIO),
                  _p, _sz, _p])
@@ -411,8 +411,10 @@ def block_weights_mx(weights: dict, stream=None) -> list:
     return [h3_mx_quantize(weights[k], stream=stream) for k in ("w_qkv", "w_o", "w1", "w3", "w2")]
 
 
-def block_workspace_size(cfg: BlockConfig, n_tok_local: int, n_buf: int, n_seg: int) -> int:
-    return _c_block_ws(ctypes.byref(cfg), n_tok_local, n_buf, n_seg)
+def block_workspace_size(cfg: BlockConfig, n_tok_local: int, n_buf: int, n_seg: int,
+                         head_count: int = 0) -> int:
+    """head_count > 0: a rank share with that head slice; 0: world 1 or any share."""
+    return _c_block_ws(ctypes.byref(cfg), n_tok_local, n_buf, n_seg, head_count)
 
 
 def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots, valid_len,
@@ -440,7 +442,7 @@ def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots,
                  n_seg, max_valid_len, n, n_buf, tok_begin, head_begin,
                  head_count if head_count is not None else cfg.n_heads, _ptr(qkv_attn),
                  _ptr(o_attn), _ptr(o_local), _ptr(qkv_send), _ptr(o_recv))
-    need = block_workspace_size(cfg, n, n_buf, n_seg)
+    need = block_workspace_size(cfg, n, n_buf, n_seg, (head_count or cfg.n_heads) if share else 0)
     if ws is None:
         ws = _bytes_ws(need, x.device)
     _check(_c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), _ptr(ws),

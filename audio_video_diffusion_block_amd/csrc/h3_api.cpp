@@ -258,9 +258,11 @@ h3::MxOperand mx_of(const h3_mx_operand* x) {
   return m;
 }
 
+// bf16 g (only where a separate pass quantizes it: ffn_dim % 128 != 0), then
+// its MX operand
 int64_t swiglu_fp8_parts(int64_t n_tok, int32_t ffn_dim, int64_t* g_q, int64_t* g_s) {
   const int64_t fp = h3::round_up(ffn_dim, 128);
-  const int64_t g = h3::round_up(n_tok * ffn_dim * 2, 256);
+  const int64_t g = ffn_dim % 128 == 0 ? 0 : h3::round_up(n_tok * ffn_dim * 2, 256);
   *g_q = g;
   *g_s = g + h3::round_up(n_tok * fp, 256);
   return *g_s + h3::round_up(n_tok * (fp / 32), 256);
@@ -628,14 +630,16 @@ h3_status h3_swiglu_fp8(const h3_mx_operand* h, const h3_mx_operand* w1,
   g8.ld = fp;
   g8.scale = wsb + gs_off;
   g8.ld_scale = fp / 32;
-  // with ffn_dim % 128 == 0 the up-projection's epilogue also writes g's MX
-  // operand (no padding columns); otherwise a separate pass quantizes g
+  // with ffn_dim % 128 == 0 the up-projection's epilogue writes g only as its
+  // MX operand (no padding columns); otherwise g is stored in bf16 and a
+  // separate pass quantizes it
   GemmMap gmx;
   if (ffn_dim % 128 == 0) {
     gmx.mx_q = (uint8_t*)(wsb + gq_off);
     gmx.mx_ld = fp;
     gmx.mx_s = (uint8_t*)(wsb + gs_off);
     gmx.mx_lds = fp / 32;
+    gmx.mx_only = true;
   }
   TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, mx_of(h), mx_of(w1), mx_of(w3), wsb, ffn_dim,
                                  nullptr, 0, n_tok, ffn_dim, dim, s, gmx),
@@ -657,6 +661,17 @@ struct BlockWs {
   int64_t xkp, fkp;  // padded widths of the activation and g MX operands
 };
 
+// FP8 projections with dim % 128 == 0: the modulated norms write h1 / h2 as
+// the MX operand directly (no bf16 h)
+bool block_mx_norm(const h3_block_config* c) { return c->gemm_fp8 && c->dim % 128 == 0; }
+// FP8 projections with ffn_dim % 128 == 0: the up-projection's epilogue writes
+// g only as the MX operand the down-projection reads (no bf16 g)
+bool block_g_mx_only(const h3_block_config* c) { return c->gemm_fp8 && c->ffn_dim % 128 == 0; }
+
+// Two groups by lifetime: h1 and the MX activation copy are live across the
+// whole block; qkv, the attention workspace and o (world 1) are dead once the
+// output projection has read o, before g and its MX copy are first written,
+// so the second group starts where the first does.
 BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int32_t n_seg,
                         bool share, int32_t head_count) {
   const int64_t es = (int64_t)esize(c->dtype);
@@ -668,7 +683,15 @@ BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int3
     off += (size_t)round_up(bytes, 256);
     return at;
   };
-  w.h1 = take(n * c->dim * es);
+  w.h1 = take(block_mx_norm(c) ? 0 : n * c->dim * es);
+  if (c->gemm_fp8) {
+    // MX copies of the projection inputs: h1 / o / h2 share one (width max(C, H*D)), g its own
+    w.xkp = round_up(c->dim > hd ? c->dim : hd, 128);
+    w.fkp = round_up(c->ffn_dim, 128);
+    w.xq = take(n * w.xkp);
+    w.xs = take(n * (w.xkp / 32));
+  }
+  const size_t stage = off;
   w.qkv = take(n * 3 * hd * es);
   const int64_t an = share ? n_buf : n;
   const int ah = share ? head_count : c->n_heads;
@@ -676,25 +699,23 @@ BlockWs block_ws_layout(const h3_block_config* c, int64_t n, int64_t n_buf, int3
                             : (int64_t)attn_workspace_bytes(c->dtype == H3_BF16, an, ah,
                                                             c->head_dim, n_seg));
   w.o = take(share ? 0 : n * hd * es);
-  w.g = take(n * (int64_t)c->ffn_dim * es);
+  const size_t attn_end = off;
+  off = stage;
+  w.g = take(block_g_mx_only(c) ? 0 : n * (int64_t)c->ffn_dim * es);
   if (c->gemm_fp8) {
-    // MX copies of the projection inputs: h1 / o / h2 share one (width max(C, H*D)), g its own
-    w.xkp = round_up(c->dim > hd ? c->dim : hd, 128);
-    w.fkp = round_up(c->ffn_dim, 128);
-    w.xq = take(n * w.xkp);
-    w.xs = take(n * (w.xkp / 32));
     w.gq = take(n * w.fkp);
     w.gs = take(n * (w.fkp / 32));
   }
-  w.total = off;
+  w.total = off > attn_end ? off : attn_end;
   return w;
 }
 }  // namespace
 
 size_t h3_dit_block_workspace_size(const h3_block_config* cfg, int64_t n_tok_local,
-                                   int64_t n_buf, int32_t n_seg) {
-  if (!cfg || n_tok_local < 0 || n_buf < 0 || n_seg <= 0) return 0;
-  // the query does not know the mode: cover world 1 and a rank share of any head count
+                                   int64_t n_buf, int32_t n_seg, int32_t head_count) {
+  if (!cfg || n_tok_local < 0 || n_buf < 0 || n_seg <= 0 || head_count < 0) return 0;
+  if (head_count > 0) return block_ws_layout(cfg, n_tok_local, n_buf, n_seg, true, head_count).total;
+  // 0: cover world 1 and a rank share of any head count
   const size_t w1 = block_ws_layout(cfg, n_tok_local, n_tok_local, n_seg, false, cfg->n_heads).total;
   const size_t sh = block_ws_layout(cfg, n_tok_local, n_buf, n_seg, true, cfg->n_heads).total;
   return w1 > sh ? w1 : sh;
@@ -799,7 +820,7 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
 
   // FP8 projections with C % 128 == 0: the modulated norms write the MX operand
   // of h1 / h2 directly (the same bytes as storing bf16 h and quantizing it)
-  const bool mx_norm = f8 && C % 128 == 0;
+  const bool mx_norm = block_mx_norm(cfg);
   // A1 h1 = norm(x)(1 + scale1) + shift1
   if (mx_norm) {
     TRY(hip_status(launch_modulate_mx(io->x, io->ld_x, mslot(0), mslot(1), ldm, wsb + L.xq, L.xkp,
@@ -984,13 +1005,15 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   void* g = wsb + L.g;
   if (f8) {
     if (!mx_norm) TRY(quant_act(h1, C, C));
-    // g's MX operand comes from the up-projection's epilogue when F % 128 == 0
+    // g's MX operand comes from the up-projection's epilogue when F % 128 == 0,
+    // and then only it is written (the down-projection reads nothing else)
     GemmMap gmx;
-    if (F % 128 == 0) {
+    if (block_g_mx_only(cfg)) {
       gmx.mx_q = (uint8_t*)(wsb + L.gq);
       gmx.mx_ld = L.fkp;
       gmx.mx_s = (uint8_t*)(wsb + L.gs);
       gmx.mx_lds = L.fkp / 32;
+      gmx.mx_only = true;
     }
     TRY(hip_status(launch_gemm_mx8(EPI_SWIGLU, xq, wmx(2), wmx(3), g, F, nullptr, 0, n, F, C, s,
                                    gmx),

@@ -160,8 +160,10 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
           continue;
         }
       }
-      if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
-      else for (int e = 0; col + e < N; ++e) po[e] = src[e];
+      if (!(EPI == EPI_SWIGLU && map.mx_only)) {
+        if (col + 8 <= N) *reinterpret_cast<uint4*>(po) = *reinterpret_cast<const uint4*>(src);
+        else for (int e = 0; col + e < N; ++e) po[e] = src[e];
+      }
       if (EPI == EPI_SWIGLU && map.mx_q) {
         // MX e4m3 copy: a 32-column block is the chunks of 4 adjacent lanes (N % 32 == 0,
         // so a quad is active or skipped as a whole)

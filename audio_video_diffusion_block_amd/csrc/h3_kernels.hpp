@@ -44,6 +44,8 @@ struct GemmMap {
   int64_t mx_ld = 0;
   uint8_t* mx_s = nullptr;
   int64_t mx_lds = 0;
+  // with mx_q: only the MX operand is written (C is not touched and may be NULL)
+  bool mx_only = false;
   // EPI_STORE of a QKV projection (N = 3*qk_H*qk_D, qk_D in {64, 128}): the q
   // and k head columns (n < 2*qk_H*qk_D) of rows whose qk_pos kind is video or
   // audio get Q/K RMSNorm (gains qk_gq, qk_gk) and RoPE before they are
@@ -55,7 +57,9 @@ struct GemmMap {
   int qk_H = 0, qk_D = 0;
   float qk_eps = 0.f;
   RopeTab qk_tab{};
-  bool empty() const { return a_kgroup == 0 && peer_hc == 0 && mx_q == nullptr && qk_pos == nullptr; }
+  bool empty() const {
+    return a_kgroup == 0 && peer_hc == 0 && mx_q == nullptr && !mx_only && qk_pos == nullptr;
+  }
 };
 
 // out = A @ B^T with epilogue; for EPI_SWIGLU, B = W1, B3 = W3 and N = features

@@ -415,7 +415,7 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
   // operand maps exist only on the bf16 K % 64 kernel (and a scatter only for plain stores)
   if (!map.empty() && (!bf16 || K < BK || K % BK != 0 || (map.a_kgroup % BK) != 0 ||
                        (map.peer_hc && epi != EPI_STORE) ||
-                       (map.mx_q && (epi != EPI_SWIGLU || N % 32 != 0)) ||
+                       (map.mx_q && (epi != EPI_SWIGLU || N % 32 != 0)) || (map.mx_only && !map.mx_q) ||
                        (map.qk_pos && (epi != EPI_STORE || (map.qk_D != 64 && map.qk_D != 128) ||
                                        N != 3 * map.qk_H * map.qk_D))))
     return hipErrorInvalidValue;

@@ -290,7 +290,7 @@ hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, cons
   if (M == 0 || N == 0) return hipSuccess;
   // only the store epilogue's peer-major scatter applies here (A is an MX operand)
   if (map.a_kgroup != 0 || (map.peer_hc && epi != EPI_STORE) ||
-      (map.mx_q && (epi != EPI_SWIGLU || N % 32 != 0)) ||
+      (map.mx_q && (epi != EPI_SWIGLU || N % 32 != 0)) || (map.mx_only && !map.mx_q) ||
       (map.qk_pos && (epi != EPI_STORE || (map.qk_D != 64 && map.qk_D != 128) ||
                       N != 3 * map.qk_H * map.qk_D)))
     return hipErrorInvalidValue;

@@ -13,8 +13,14 @@ around each C entry point on the stream it is launched on.  The CPU baseline
 is the float64 oracle, timed on this host on a bounded row sample and
 extrapolated by row count.
 
-  python bench.py [--steps K] [--warmup W] [--config share10s|share5s|tiny]
-                  [--no-cpu-baseline] [--only attn|attn_fp8|copy|block]
+The default run then frees the 10 s share and adds the other configurations
+of the request sweep as extra keys: the 8k varlen attention case (bf16 and
+FP8), one block on the 5 s share, and the four-forward 15 s student loop
+(bf16, then FP8 with only the MX weights resident, with peak device bytes of
+both).
+
+  python bench.py [--steps K] [--warmup W] [--config share10s|share5s|loop15s|tiny]
+                  [--no-cpu-baseline] [--no-extra] [--only attn|attn_fp8|copy|block]
 """
 from __future__ import annotations
 
@@ -46,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", choices=["", "attn", "attn_fp8", "copy", "block"])
     ap.add_argument("--op-reps", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other configs (8k varlen attention, 5 s block, 15 s loop)")
     return ap.parse_args()
 
 
@@ -200,21 +208,29 @@ def cpu_baseline(wl, w, bi, work, attn_rows=2048, local_rows=4096):
 
 # ------------------------------------------------------------ student loop
 
-def run_loop_bench(args, h3, torch, W):
+def loop_measure(h3, torch, W, seed, steps, warmup):
     """Four-forward student loop on the 15 s share: 8 blocks with their own weights,
-    modulation regenerated per sigma from the timestep embedding, Euler update."""
-    import numpy as np
-    wl = W.PRESETS[args.config]
+    modulation regenerated per sigma from the timestep embedding, Euler update.
+    Timed in bf16, then with FP8 attention and FP8 projections with only the MX
+    weights resident (the bf16 copies freed first).  Peak device bytes are the
+    caching allocator's high-water mark over each run, counted from what was
+    allocated when it started (inputs, weights, workspaces and activations of
+    the loop itself)."""
+    wl = W.LOOP_15S
     bf = torch.bfloat16
     timer = EventTimer(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
     t0 = time.time()
     blocks = []
     for b in range(wl.n_blocks):
-        w = W.block_weights(wl, args.seed, "bf16", block=b)
+        w = W.block_weights(wl, seed, "bf16", block=b)
         blocks.append({k: to_dev(getattr(w, k), bf) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")})
         del w
-    tw = W.timestep_weights(wl, args.seed, "bf16")
-    bi = W.block_inputs(wl, args.seed, "bf16")
+    tw = W.timestep_weights(wl, seed, "bf16")
+    bi = W.block_inputs(wl, seed, "bf16")
     log(f"generated and uploaded loop inputs in {time.time() - t0:.1f}s")
     H, D, C = wl.n_heads, wl.head_dim, wl.dim
     hc = wl.head_count
@@ -225,17 +241,18 @@ def run_loop_bench(args, h3, torch, W):
     mods = torch.empty((wl.n_blocks, 6, C), dtype=bf, device="cuda")
     pos, cu, vl = to_dev(bi.pos), to_dev(bi.cu_slots), to_dev(bi.valid_len)
     max_len = int(bi.valid_len.max())
-    cfg = h3.block_config(C, H, D, wl.ffn_dim, wl.sections, wl.theta, wl.eps_qk, wl.eps_mod, 0, bf)
     share = dict(qkv_attn=to_dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), bf),
                  o_attn=torch.zeros((wl.n_pad_total, hc * D), dtype=bf, device="cuda"),
                  o_local=to_dev(bi.o_local.reshape(wl.n_loc, -1), bf), tok_begin=wl.tok_begin,
                  head_begin=wl.head_begin, head_count=hc)
-    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, wl.n_pad_total, 1), dtype=torch.uint8, device="cuda")
+    del bi
     tws = torch.empty(max(h3.timestep_workspace_size(C), 16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()  # the upload's fp32 staging copies are not the loop's
     sig = W.STUDENT_SIGMAS
     fwd_ms = []
 
-    def loop(record=False):
+    def run(cfg, weights, ws, record=False):
         z.copy_(z0)
         x.copy_(z0)
         for k in range(len(sig) - 1):
@@ -244,59 +261,128 @@ def run_loop_bench(args, h3, torch, W):
             e0.record()
             h3.h3_timestep_modulation(sig[k], t1, t2, tab, mods, ws=tws)
             for b in range(wl.n_blocks):
-                h3.h3_dit_block_forward(cfg, blocks[b], x, mods[b:b + 1], pos, cu, vl, max_len, ws=ws, **share)
+                h3.h3_dit_block_forward(cfg, weights[b], x, mods[b:b + 1], pos, cu, vl, max_len, ws=ws, **share)
             h3.h3_euler_update(z, x, x, sig[k], sig[k + 1])
             e1.record()
             if record:
                 fwd_ms.append((e0, e1))
 
-    for _ in range(args.warmup):
-        loop()
+    cfg = h3.block_config(C, H, D, wl.ffn_dim, wl.sections, wl.theta, wl.eps_qk, wl.eps_mod, 0, bf)
+    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, wl.n_pad_total, 1, hc), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        run(cfg, blocks, ws)
     torch.cuda.synchronize()
-    steps = max(args.steps, 1)
-    t_start = time.perf_counter()
-    loop_ms = timer.time(lambda: loop(record=True), steps)
-    wall = (time.perf_counter() - t_start) * 1e3 / steps
-    per_fwd = [a.elapsed_time(b) for a, b in fwd_ms]
-    # the same loop with FP8 attention and FP8 projections (MX weights quantized once, untimed)
+    loop_ms = timer.time(lambda: run(cfg, blocks, ws, record=True), steps)
+    per_fwd = [a.elapsed_time(b) for a, b in fwd_ms[-(len(sig) - 1):]]
+    peak_bf16 = torch.cuda.max_memory_allocated() - base
+    # FP8: MX weights quantized once (untimed), the bf16 projection weights freed
+    blocks8 = []
+    for bw in blocks:
+        blocks8.append({"mx": h3.block_weights_mx(bw), "g_q": bw["g_q"], "g_k": bw["g_k"]})
+        for key in ("w_qkv", "w_o", "w1", "w3", "w2"):
+            del bw[key]
+    del blocks, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
     cfg8 = h3.block_config(C, H, D, wl.ffn_dim, wl.sections, wl.theta, wl.eps_qk, wl.eps_mod, 0, bf,
                            attn_fp8=True, gemm_fp8=True)
-    ws8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, wl.n_pad_total, 1), dtype=torch.uint8,
+    ws8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, wl.n_pad_total, 1, hc), dtype=torch.uint8,
                       device="cuda")
-    blocks8 = [{"mx": h3.block_weights_mx(bw), "g_q": bw["g_q"], "g_k": bw["g_k"]} for bw in blocks]
-
-    def loop8():
-        z.copy_(z0)
-        x.copy_(z0)
-        for k in range(len(sig) - 1):
-            h3.h3_timestep_modulation(sig[k], t1, t2, tab, mods, ws=tws)
-            for b in range(wl.n_blocks):
-                h3.h3_dit_block_forward(cfg8, blocks8[b], x, mods[b:b + 1], pos, cu, vl, max_len, ws=ws8, **share)
-            h3.h3_euler_update(z, x, x, sig[k], sig[k + 1])
-
-    loop8()
+    for _ in range(warmup):
+        run(cfg8, blocks8, ws8)
     torch.cuda.synchronize()
-    loop8_ms = timer.time(loop8, steps)
-    del blocks8, ws8
+    loop8_ms = timer.time(lambda: run(cfg8, blocks8, ws8), steps)
+    peak_fp8 = torch.cuda.max_memory_allocated() - base
+    del blocks8, ws8, share, z, x, z0, mods, tws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     work = algorithmic_work(wl)
     blk_flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
     total_flop = blk_flop * wl.n_blocks * (len(sig) - 1)
-    value = total_flop / loop_ms / 1e9
+    return {"loop_ms": loop_ms, "ms_per_forward": per_fwd,
+            "ms_per_block": loop_ms / (wl.n_blocks * (len(sig) - 1)), "TFLOP/s": total_flop / loop_ms / 1e9,
+            "fp8_loop_ms": loop8_ms, "fp8_ms_per_forward": loop8_ms / (len(sig) - 1),
+            "fp8_speedup": loop_ms / loop8_ms,
+            "peak_device_bytes_bf16": peak_bf16, "peak_device_bytes_fp8": peak_fp8,
+            "peak_fp8_vs_bf16": peak_fp8 / peak_bf16,
+            "workload": f"{wl.name}: {wl.n_blocks} DiT blocks x {len(sig) - 1} forwards, rank {wl.rank} of "
+                        f"{wl.sp_degree} share (n_loc={wl.n_loc}; attention over N={wl.n_valid}, {hc} of {H} "
+                        f"heads x {D})",
+            "fp8_note": "FP8 attention and FP8 projections (MX e4m3 operands), only the MX weights resident; "
+                        "parity at these shapes: tests/test_gpu_fp8_attn.py, tests/test_gpu_fp8_gemm.py"}
+
+
+def run_loop_bench(args, h3, torch, W):
+    """--config loop15s: the student loop alone, as the bench line."""
+    wl = W.LOOP_15S
+    steps = max(args.steps, 1)
+    r = loop_measure(h3, torch, W, args.seed, steps, args.warmup)
     out = {
-        "metric": "four-forward student loop, 15 s share: loop ms and ms per forward", "value": value,
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": loop_ms,
+        "metric": "four-forward student loop, 15 s share: loop ms and ms per forward", "value": r["TFLOP/s"],
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": r["loop_ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: {wl.n_blocks} DiT blocks x {len(sig) - 1} forwards, rank {wl.rank} "
-                               f"of {wl.sp_degree} share (n_loc={wl.n_loc}; attention over N={wl.n_valid}, "
-                               f"{hc} of {H} heads x {D})", "n_valid": wl.n_valid, "n_loc": wl.n_loc,
-                   "blocks": wl.n_blocks, "forwards": len(sig) - 1, "parallelism": "1 GPU (rank-share stand-in)"},
-        "loop_ms": loop_ms, "wall_ms": wall, "ms_per_forward": per_fwd[-(len(sig) - 1):],
-        "ms_per_block": loop_ms / (wl.n_blocks * (len(sig) - 1)),
-        "fp8_loop_ms": loop8_ms, "fp8_speedup": loop_ms / loop8_ms,
-        "fp8_note": "the same loop with FP8 attention and FP8 projections (MX e4m3 operands)",
+        "config": {"workload": r["workload"], "n_valid": wl.n_valid, "n_loc": wl.n_loc,
+                   "blocks": wl.n_blocks, "forwards": len(W.STUDENT_SIGMAS) - 1,
+                   "parallelism": "1 GPU (rank-share stand-in)"},
     }
+    out.update({k: v for k, v in r.items() if k != "workload"})
     print(json.dumps(out))
+
+
+def varlen8k_measure(h3, torch, W, timer, reps=20):
+    """The 8k varlen attention case: 8 heads x 128, segments 4032/1500/17 with random
+    suffix pads in an 8192-row buffer; bf16 and FP8 kernels."""
+    c = W.varlen_case(seed=0, dtype="bf16")
+    bf = torch.bfloat16
+    H, D = c.n_heads, c.head_dim
+    q, k, v = (to_dev(a.reshape(c.n_buf, H * D), bf) for a in (c.q, c.k, c.v))
+    o = torch.empty_like(q)
+    cu, vl = to_dev(c.cu_slots), to_dev(c.valid_len)
+    ml = int(c.valid_len.max())
+    flop = 4.0 * D * H * float(sum(int(n) ** 2 for n in c.valid_len))
+    ws = torch.empty(max(h3.varlen_attn_workspace_size(c.n_buf, H, D, len(c.valid_len), bf), 16),
+                     dtype=torch.uint8, device="cuda")
+    ms = timer.time(lambda: h3.h3_varlen_attn(q, k, v, o, H, D, cu, vl, ml, ws=ws), reps, warm=2)
+    ws8 = torch.empty(max(h3.varlen_attn_fp8_workspace_size(c.n_buf, H, D, len(c.valid_len)), 16),
+                      dtype=torch.uint8, device="cuda")
+    ms8 = timer.time(lambda: h3.h3_varlen_attn_fp8(q, k, v, o, H, D, cu, vl, ml, ws=ws8), reps, warm=2)
+    return {"ms": ms, "TFLOP/s": flop / ms / 1e9, "frac_peak": flop / ms / 1e9 / BF16_PEAK_TFLOPS,
+            "fp8_ms": ms8, "fp8_TFLOP/s": flop / ms8 / 1e9, "algorithmic_flop": flop,
+            "workload": "8 heads x 128, segments 4032/1500/17 with random suffix pads in 8192 rows"}
+
+
+def share_block_measure(h3, torch, W, timer, wl, seed, reps):
+    """One DiT block on a request share (rank 7 of 8), bf16: ms per block."""
+    bf = torch.bfloat16
+    w = W.block_weights(wl, seed, "bf16")
+    bi = W.block_inputs(wl, seed, "bf16")
+    wd = {k: to_dev(getattr(w, k), bf) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")}
+    x = to_dev(bi.x, bf)
+    mod = to_dev(bi.mod, bf)
+    pos, cu, vl = to_dev(bi.pos), to_dev(bi.cu_slots), to_dev(bi.valid_len)
+    hc, D = wl.head_count, wl.head_dim
+    share = dict(qkv_attn=to_dev(bi.qkv_attn.reshape(wl.n_pad_total, -1), bf),
+                 o_attn=torch.zeros((wl.n_pad_total, hc * D), dtype=bf, device="cuda"),
+                 o_local=to_dev(bi.o_local.reshape(wl.n_loc, -1), bf),
+                 tok_begin=wl.tok_begin, head_begin=wl.head_begin, head_count=hc)
+    cfg = h3.block_config(wl.dim, wl.n_heads, D, wl.ffn_dim, wl.sections, wl.theta, wl.eps_qk,
+                          wl.eps_mod, 0, bf)
+    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, wl.n_pad_total, 1, hc), dtype=torch.uint8,
+                     device="cuda")
+    max_len = int(bi.valid_len.max())
+    ms = timer.time(lambda: h3.h3_dit_block_forward(cfg, wd, x, mod, pos, cu, vl, max_len, ws=ws, **share),
+                    reps, warm=2)
+    work = algorithmic_work(wl)
+    flop = work["attn_flop"] + work["qkv_flop"] + work["out_flop"] + work["w13_flop"] + work["w2_flop"]
+    del wd, x, mod, share, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"ms": ms, "TFLOP/s": flop / ms / 1e9, "attn_TFLOP/s_share_of_block": work["attn_flop"] / flop,
+            "workload": f"{wl.name}: one DiT block, rank {wl.rank} of {wl.sp_degree} share "
+                        f"(n_loc={wl.n_loc}; attention over N={wl.n_valid})"}
+
 
 # ------------------------------------------------------------------- main
 
@@ -354,7 +440,7 @@ def main():
                      o_local=to_dev(bi.o_local.reshape(wl.n_loc, -1), bf),
                      tok_begin=wl.tok_begin, head_begin=wl.head_begin, head_count=hc)
     n_buf = wl.n_pad_total if wl.share_mode else wl.n_loc
-    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, n_buf, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(h3.block_workspace_size(cfg, wl.n_loc, n_buf, 1, hc if wl.share_mode else 0), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     log(f"uploaded in {time.time() - t0:.1f}s; workspace {ws.numel() / 2**30:.2f} GiB")
 
@@ -496,7 +582,7 @@ def main():
                         ("block_fp8", True, True)):
         cfg8 = h3.block_config(wl.dim, wl.n_heads, wl.head_dim, wl.ffn_dim, wl.sections, wl.theta,
                                wl.eps_qk, wl.eps_mod, 0, bf, attn_fp8=a8, gemm_fp8=g8)
-        ws_b8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, n_buf, 1), dtype=torch.uint8,
+        ws_b8 = torch.empty(h3.block_workspace_size(cfg8, wl.n_loc, n_buf, 1, hc if wl.share_mode else 0), dtype=torch.uint8,
                             device="cuda")
         x8 = x0.clone()
         ops[key] = timer.time(lambda: h3.h3_dit_block_forward(
@@ -605,6 +691,23 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, w, bi, work)
+    if not args.no_extra and wl.name == "share10s":
+        # the other configurations of the request sweep, each after the 10 s
+        # share's buffers are freed
+        del w, bi, wd, x, x0, mod, pos, cu, vl, share, ws, attn_ws, h1, qkv, xs, sw_ws
+        del q_v, k_v, v_v, o_v, o_in
+        if wl.share_mode:
+            del qa
+        else:
+            del qkv_t
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log("extra configs: 8k varlen attention")
+        out["varlen8k_attention"] = varlen8k_measure(h3, torch, W, timer)
+        log("extra configs: 5 s share block")
+        out["share5s_block"] = share_block_measure(h3, torch, W, timer, W.SHARE_5S, args.seed, 10)
+        log("extra configs: 15 s four-forward loop (bf16, then FP8 with MX weights only)")
+        out["loop15s"] = loop_measure(h3, torch, W, args.seed, 1, 1)
     print(json.dumps(out))
 
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 6
+#define H3_ABI_VERSION 7
 
 typedef enum {
   H3_OK = 0,
@@ -435,9 +435,17 @@ typedef struct {
  * each bf16 activation (h1, o, h2, g) is quantized to an MX operand in the workspace
  * just before its projection, the weights come from w->mx (the bf16 weight pointers
  * may then be NULL).  Needs dtype H3_BF16 and dim, ffn_dim, H*D multiples of 32.
+ *
+ * h3_dit_block_workspace_size: bytes of the workspace h3_dit_block_forward needs
+ * for this cfg.  head_count > 0: a rank share with that head slice over an
+ * n_buf-row attention buffer; 0: enough for world 1 and for a share of any head
+ * count.  The workspace holds, by lifetime, h1 and the MX activation copy for
+ * the whole block, then qkv, the attention workspace and o (world 1), whose
+ * bytes the SwiGLU's g and its MX copy reuse.  Returns 0 for a NULL cfg or a
+ * negative size.
  */
 size_t h3_dit_block_workspace_size(const h3_block_config* cfg, int64_t n_tok_local,
-                                   int64_t n_buf, int32_t n_seg);
+                                   int64_t n_buf, int32_t n_seg, int32_t head_count);
 h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weights* w,
                                const h3_block_io* io, void* ws, size_t ws_bytes, void* stream);
 

@@ -108,7 +108,7 @@ def test_block_argument_checks():
     import audio_video_diffusion_block_amd as h3
     cfg = h3.block_config(256, 4, 64, 704, (16, 24, 24))
     need = h3.block_workspace_size(cfg, 480, 480, 1)
-    assert need > 480 * (256 + 768 + 704) * 2
+    assert need >= 480 * (256 + 768) * 2  # h1 and qkv at least
     w = h3.BlockWeights(*([FAKE] * 7))
     io = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 480, 0, 0, 4, None, None, None)
     st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), FAKE, need - 256, None)
@@ -241,7 +241,7 @@ def test_block_gemm_fp8_argument_checks():
     io = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 480, 480, 0, 0, 4, None, None, None)
     cfg = h3.block_config(256, 4, 64, 704, (16, 24, 24), gemm_fp8=True)
     need = h3.block_workspace_size(cfg, 480, 480, 1)
-    assert need > h3.block_workspace_size(h3.block_config(256, 4, 64, 704, (16, 24, 24)), 480, 480, 1)
+    assert need != h3.block_workspace_size(h3.block_config(256, 4, 64, 704, (16, 24, 24)), 480, 480, 1)
     st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), FAKE, need, None)
     assert st == h3.H3_ERR_ARG and "weights.mx" in h3.last_error()
     f32 = h3.block_config(256, 4, 64, 704, (16, 24, 24), dtype=torch.float32, gemm_fp8=True)
@@ -356,3 +356,42 @@ def test_noalloc_attention_argument_checks():
     big = h3.NOALLOC_SCRATCH_BYTES // (8 * 128 * 2) + 64
     assert call(n_buf=big) == h3.H3_ERR_WORKSPACE and "scratch" in h3.last_error()
     assert call(n_buf=0) == h3.H3_OK                     # empty call: nothing to do
+
+
+def test_block_workspace_size_by_head_slice():
+    """The size query: a rank share's workspace follows its head slice, 0 covers
+    world 1 and every share, and the forward refuses 256 bytes less than the
+    query for the mode it runs in."""
+    import audio_video_diffusion_block_amd as h3
+    for kw in ({}, dict(attn_fp8=True), dict(gemm_fp8=True), dict(attn_fp8=True, gemm_fp8=True)):
+        cfg = h3.block_config(256, 8, 64, 768, (16, 24, 24), **kw)
+        n, n_buf = 480, 3840
+        sizes = [h3.block_workspace_size(cfg, n, n_buf, 1, hc) for hc in (1, 2, 4, 8)]
+        assert all(a < b for a, b in zip(sizes, sizes[1:])), (kw, sizes)
+        anyc = h3.block_workspace_size(cfg, n, n_buf, 1)
+        assert anyc >= sizes[-1] and anyc >= h3.block_workspace_size(cfg, n, n, 1), kw
+        assert h3.block_workspace_size(cfg, n, n_buf, 1, -1) == 0
+        # a share with 2 of 8 heads: refused 256 bytes short of its own size
+        w = h3.BlockWeights(*([FAKE] * 7))
+        if kw.get("gemm_fp8"):
+            mx = (h3.MxOperand * 5)(h3.MxOperand(FAKE, 256, FAKE, 8), h3.MxOperand(FAKE, 512, FAKE, 16),
+                                    h3.MxOperand(FAKE, 256, FAKE, 8), h3.MxOperand(FAKE, 256, FAKE, 8),
+                                    h3.MxOperand(FAKE, 768, FAKE, 24))
+            w.mx = ctypes.cast(mx, ctypes.POINTER(h3.MxOperand))
+        io = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, n_buf, n, n_buf, 0, 2, 2,
+                        FAKE, FAKE, FAKE)
+        st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), FAKE, sizes[1] - 256, None)
+        assert st == h3.H3_ERR_WORKSPACE, (kw, h3.last_error())
+
+
+def test_block_workspace_stages_share_bytes():
+    """qkv, the attention workspace and o are dead before the SwiGLU writes g:
+    the workspace is the larger stage, not the sum (bf16, world 1)."""
+    import audio_video_diffusion_block_amd as h3
+    C, H, D, F, n = 256, 4, 64, 2048, 1024
+    cfg = h3.block_config(C, H, D, F, (16, 24, 24))
+    need = h3.block_workspace_size(cfg, n, n, 1, 0)
+    h1, qkv, o, g = n * C * 2, n * 3 * H * D * 2, n * H * D * 2, n * F * 2
+    assert g > qkv + o  # the FFN stage is the larger one here
+    assert need < h1 + qkv + o + g
+    assert need >= h1 + g
