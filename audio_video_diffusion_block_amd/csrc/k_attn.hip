@@ -429,6 +429,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   const int v_bytes = (int)(D * vt_cols * 2);
   // staging registers: tile t is loaded one step before it is stored
   uint4 rk[KPT], rv[VPT];
+  // The loads of tile jt+2 are issued one by one inside phase A of step jt
+  // (load_begin, then load_part(i) after every fourth MFMA) instead of in one
+  // burst after the barrier, where all 8 waves of the CU would issue theirs at
+  // once and stall on the address unit.  A load past the last tile re-reads
+  // the last tile (in bounds) and is never stored.
+  __amdgpu_buffer_rsrc_t ld_rk, ld_rv;
+  auto load_begin = [&](int jt) {
+    const int j0 = min(jt, n_tiles - 1) * KT;
+    ld_rk = make_rsrc(kbase + (int64_t)j0 * k_row_bytes, min(len - j0, KT) * k_row_bytes);
+    ld_rv = make_rsrc(vbase + (int64_t)j0 * 2, v_bytes);
+  };
+  auto load_part = [&](int i) {  // i < KPT: K chunk i, else V^T chunk i - KPT
+    if (i < KPT) rk[i] = buf_load16(ld_rk, k_voff[i]);
+    else rv[i - KPT] = buf_load16(ld_rv, v_voff[i - KPT]);
+  };
   auto load_tile = [&](int jt) {
     const int j0 = jt * KT;
     const __amdgpu_buffer_rsrc_t rs_k =
@@ -534,7 +549,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
 
   // A tile step is two phases, hand-ordered so that each keeps both pipes fed:
   //  phase A: S(next) = K(next) Q^T (16 MFMAs), each followed by 1/16 of the
-  //           softmax of S(cur): 2 fma + 2 exp + 1 pack + 1 dot2 (VALU-heavy);
+  //           softmax of S(cur): 2 exp + 1 pack + 1 dot2 (VALU-heavy), and
+  //           every fourth by one load of tile jt+2;
   //  phase B: O^T += V(cur)^T P^T (16 MFMAs), each followed by one step of the
   //           row max of S(next) (MFMA-heavy).
   // LDS fragments are read 4 MFMAs ahead.  sched_barrier(0) keeps the order.
@@ -557,6 +573,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     bf16x8_t kf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[i] = kfrag(sk, i >> 1, i & 1);
+    load_begin(jt + 2);
     // Slot i: one MFMA of S(next), the fma/exp of softmax slice i and the
     // pack/row-sum of slice i-1 (so a pack never waits on the exp it consumes:
     // in-order issue would stall the wave there).
@@ -565,6 +582,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     for (int i = 0; i < NA; ++i) {
       nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1],
                                                           i < 2 ? negm : nxt[i & 1], 0, 0, 0);
+      if (i % 4 == 3 && i / 4 < KPT + VPT) load_part(i / 4);
       if (i + 4 < NA) kf[i & 3] = kfrag(sk, (i + 4) >> 1, (i + 4) & 1);
       else {
         const int pidx = i + 4 - NA;  // first P.V fragments of phase B
@@ -660,7 +678,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
       negm[r] = -m0;
     }
   }
-  if (n_tiles > 2) load_tile(2);
 
   // Phase rotation: the two wave halves of the work-group share each SIMD
   // (waves w and w + NW/2).  The first half runs A(jt) then B(jt) in step jt;
@@ -668,8 +685,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
   // barriers, but at any moment one wave of a SIMD is in its VALU-heavy phase
   // while the other feeds the matrix core.
   // During step jt the ring holds tiles jt-1 (V, second half), jt (V, first
-  // half) and jt+1 (K, both halves); tile jt+2, loaded into registers during
-  // the previous step, goes to the fourth stage, and tile jt+3 is loaded.
+  // half) and jt+1 (K, both halves); tile jt+2 is loaded into registers during
+  // phase A and stored to the fourth stage before the barrier.
   // After the last tile, S(next) reads a stale stage and is discarded.
   const bool lag = __builtin_amdgcn_readfirstlane(wave) >= NW / 2;
   // SKIP flags: sk_cur for the tile whose softmax runs in this step, sk_prev
@@ -684,7 +701,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_pipe_kernel(
     if (!lag) sk_cur = phase_b(jt % NSTAGE, nxt, jt, sk_cur);
     if (jt + 2 < n_tiles) store_tile((jt + 2) % NSTAGE);
     __syncthreads();
-    if (jt + 3 < n_tiles) load_tile(jt + 3);
   };
   for (int jt = 0; jt < n_tiles; jt += 2) {
     step(jt, sa, sb);
