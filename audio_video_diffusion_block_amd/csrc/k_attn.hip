@@ -8,7 +8,7 @@
 //  * One work-group = NW waves = one (segment, head, 32*NW-row query tile).
 //    Each wave owns 32 query rows for the whole key loop; its Q fragments stay
 //    in registers.
-//  * Keys stream in tiles of 64 through LDS, double buffered: K as [64][D]
+//  * Keys stream in tiles of 64 through a 4-stage LDS ring: K as [64][D]
 //    (d contiguous) and V pre-transposed to [D][64] (keys contiguous) by a
 //    separate pass into scratch, so both MFMA operands are plain 16-byte LDS
 //    reads.
@@ -19,10 +19,12 @@
 //    that the accumulator's key order matches, register for register, the
 //    B-operand order of the P.V product; P is converted to bf16 in registers
 //    and feeds O^T += V^T P^T directly (no LDS round trip).
-//  * Online softmax in the log2 domain (scale*log2(e) folded into one FMA).
-//    The running max is raised only when a row max exceeds it by more than 8
-//    (2^8 bound on unnormalised weights), so the O rescale is skipped on most
-//    tiles; the final 1/l uses the same stale max, so the result is exact.
+//  * Online softmax in the log2 domain: Q is scaled once by scale*log2(e) and
+//    every score chain starts from minus the running max, so scores leave the
+//    matrix pipe ready for v_exp_f32.  The running max is raised only when a
+//    row max exceeds it by more than 8 (2^8 bound on unnormalised weights), so
+//    the O rescale is skipped on most tiles; the final 1/l uses the same stale
+//    max, so the result is exact.
 //  * Keys beyond the valid length are zero-filled in LDS (K) / scratch (V^T)
 //    and their scores masked to -inf, so NaN/Inf pad rows never reach a product.
 //  * No atomics, no split over keys: the result is deterministic.
@@ -139,211 +141,13 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) 
 }
 }  // namespace
 
-// LDS layout of one stage: K tile [64 keys][D + 8] then V^T tile [D][64 + 8]
-// (bf16).  The 16-byte row padding puts the 16 rows that one 16-lane group of
-// a ds_read_b128 touches on 16 distinct 4-bank groups, and keeps every
-// fragment read a compile-time offset from one per-lane base address.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(
-    const bf16_t* __restrict__ q, int64_t ld_q, const bf16_t* __restrict__ k, int64_t ld_k,
-    const bf16_t* __restrict__ vt, int64_t vt_cols, bf16_t* __restrict__ o, int64_t ld_o,
-    const int* __restrict__ cu, const int* __restrict__ valid, float scale_log2) {
-  constexpr int BMQ = NW * 32;
-  constexpr int NTH = NW * 64;
-  constexpr int KCH = D / 8;           // 16-byte chunks per K row
-  constexpr int KS = D + 8;            // padded K row, elements
-  constexpr int VS = KT + 8;           // padded V^T row, elements
-  constexpr int K_ELEMS = KT * KS;
-  constexpr int STAGE = K_ELEMS + D * VS;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
-
-  const int s = blockIdx.y;
-  const int head = blockIdx.z;
-  const int seg_lo = cu[s];
-  const int len = seg_valid(cu, valid, s);
-  const int q0 = blockIdx.x * BMQ;
-  if (q0 >= len) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int qi = lane & 31;   // this lane's query row within the wave
-  const int hf = lane >> 5;   // lane half
-  const int qrow = q0 + wave * 32 + qi;
-  const bool q_ok = qrow < len;
-
-  // ---- Q fragments: B operand of S^T = K Q^T, k-block kk covers d = kk*16 + hf*8 .. +8
-  bf16x8_t qf[D / 16];
-  {
-    const bf16_t* qp = q + (int64_t)(seg_lo + (q_ok ? qrow : 0)) * ld_q + head * D + hf * 8;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 val = q_ok ? *reinterpret_cast<const uint4*>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, val);
-    }
-  }
-
-  // ---- tile loaders (buffer loads: per-thread byte offsets fixed, per-tile base in SGPRs)
-  constexpr int KPT = KT * KCH / NTH;  // 16-byte K chunks per thread per tile
-  constexpr int VPT = D * 8 / NTH;     // 16-byte V^T chunks per thread per tile
-  static_assert((KT * KCH) % NTH == 0 && (D * 8) % NTH == 0, "tile split");
-  const char* kbase = reinterpret_cast<const char*>(k + (int64_t)seg_lo * ld_k + head * D);
-  const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)head * D * vt_cols +
-                                                    vt_segment_base(seg_lo, s));
-  const int k_row_bytes = (int)(ld_k * 2);
-  int k_voff[KPT], k_lds[KPT], v_voff[VPT], v_lds[VPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int c = tid + i * NTH, r = c / KCH, ch = c % KCH;
-    k_voff[i] = r * k_row_bytes + ch * 16;
-    k_lds[i] = r * KS + ch * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int c = tid + i * NTH, r = c / 8, ch = c % 8;
-    v_voff[i] = r * (int)(vt_cols * 2) + ch * 16;
-    v_lds[i] = K_ELEMS + r * VS + ch * 8;
-  }
-  const int v_bytes = (int)(D * vt_cols * 2);
-  uint4 rk[KPT], rv[VPT];
-  auto load_tile = [&](int jt) {
-    const int j0 = jt * KT;
-    const __amdgpu_buffer_rsrc_t rs_k =
-        make_rsrc(kbase + (int64_t)j0 * k_row_bytes, min(len - j0, KT) * k_row_bytes);
-    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(vbase + (int64_t)j0 * 2, v_bytes);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) rk[i] = buf_load16(rs_k, k_voff[i]);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) rv[i] = buf_load16(rs_v, v_voff[i]);
-  };
-  auto store_tile = [&](int stage) {
-    bf16_t* st = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(st + k_lds[i]) = rk[i];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(st + v_lds[i]) = rv[i];
-  };
-
-  f32x16_t oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled scores (log2 domain)
-  float l_run = 0.f;        // this lane's partial row sum
-
-  const int n_tiles = (len + KT - 1) / KT;
-  const int k_frag = sigma_row(qi) * KS + hf * 8;  // per-lane K fragment base (elements)
-  const int v_frag = K_ELEMS + qi * VS + hf * 8;   // per-lane V^T fragment base
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const bf16_t* st = smem + (jt & 1) * STAGE;
-    if (jt + 1 < n_tiles) load_tile(jt + 1);
-
-    // S^T for keys [0,32) and [32,64) of the tile, the two chains interleaved
-    f32x16_t sc[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(st + k_frag + kk * 16);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(st + k_frag + 32 * KS + kk * 16);
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], sc[0], 0, 0, 0);
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], sc[1], 0, 0, 0);
-    }
-    // mask keys >= len (only the last tile can hold them)
-    if ((jt + 1) * KT > len) {
-      const int base = jt * KT;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = base + kb * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
-          if (key >= len) sc[kb][r] = -INFINITY;
-        }
-    }
-    // row max over the tile: lane-local, then with the partner lane (same query)
-    float mx = sc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-    }
-    const float mx_s = mx * scale_log2;
-    // raise the running max only when it is exceeded by more than 8 (log2 units)
-    const bool raise = mx_s > m_run + 8.0f;
-    if (__any(raise)) {
-      const float m_new = raise ? mx_s : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exp2(-inf) = 0 on the first tile
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    // P = exp2(s*scale_log2 - m), partial row sums, bf16 B operands
-    bf16x8_t pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + 2 * t], scale_log2, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + 2 * t + 1], scale_log2, -m_run));
-          l_run += p0 + p1;
-          w[t] = cvt_pk_bf16(p0, p1);
-        }
-        pb[kb][half] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-      }
-    }
-    // O^T += V^T P^T : d blocks of 32, keys in 4 blocks of 16
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              st + v_frag + db * 32 * VS + kb * 32 + half * 16);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][half], oacc[db], 0, 0, 0);
-        }
-      }
-    }
-    if (jt + 1 < n_tiles) store_tile((jt + 1) & 1);
-    __syncthreads();
-  }
-
-  // ---- normalise and store: lane holds query qi, d = db*32 + (r/4)*8 + hf*4 + r%4
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!q_ok) return;
-  const float inv = 1.0f / l_tot;
-  bf16_t* op = o + (int64_t)(seg_lo + qrow) * ld_o + head * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + g * 8 + hf * 4;
-      uint2 val;
-      val.x = cvt_pk_bf16(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
-      val.y = cvt_pk_bf16(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d) = val;
-    }
-  }
-}
-
 // ---------------------------------------------- software-pipelined MFMA kernel
 //
-// Same operand layouts as above, restructured so the MFMA and VALU pipes
+// LDS layout of one stage: the K tile [64 keys][D + 8] then the V^T tile
+// [D][64 + 8] (bf16).  The 16-byte row padding puts the 16 rows that one
+// 16-lane group of a ds_read_b128 touches on 16 distinct 4-bank groups, and
+// keeps every fragment read a compile-time offset from one per-lane base
+// address.  The kernel is software-pipelined so the MFMA and VALU pipes
 // overlap: in tile step j a wave issues S(j+1) = K(j+1) Q^T (MFMA,
 // independent) while it runs the softmax of S(j) (VALU), then P(j).V(j).  The
 // two halves of the work-group run these two phases in opposite order, so the
