@@ -143,6 +143,9 @@ h3_status validate_attn(const void* q, int64_t ld_q, const void* k, int64_t ld_k
   CHECK(ld_q > 0 && ld_k > 0 && ld_v > 0 && ld_o > 0, "row strides must be positive");
   // the bf16 kernel addresses a 64-row key tile and the transposed-V scratch with 32-bit byte offsets
   CHECK(ld_k <= (1 << 23) && n_buf <= (1 << 22), "row stride above 2^23 or n_buf above 2^22");
+  // ... and a head's transposed V (D rows of vt_columns keys, 2 bytes each) likewise
+  CHECK((int64_t)D * h3::vt_columns(n_buf, n_seg) * 2 <= (int64_t)INT32_MAX,
+        "n_buf %lld with %d segments: a head's transposed V exceeds 2^31 bytes", (long long)n_buf, n_seg);
   if (ws_from_library) return H3_OK;
   const size_t need = fp8 ? h3::attn_fp8_workspace_bytes(n_buf, H, D, n_seg)
                          : h3::attn_workspace_bytes(dt == H3_BF16, n_buf, H, D, n_seg);

@@ -119,7 +119,10 @@ h3_status h3_qk_norm_rope(void* q, int64_t ld_q, void* k, int64_t ld_k, int64_t 
  *   softmax_scale <= 0 means 1/sqrt(head_dim).  Bidirectional, no cross-segment
  *   attention.  head_dim in {64, 128}.
  *   ws: scratch of h3_varlen_attn_workspace_size(n_buf, n_heads, head_dim,
- *   n_seg, dtype) bytes (a transposed copy of v).
+ *   n_seg, dtype) bytes (a transposed copy of v).  One head of that copy
+ *   (head_dim rows of n_buf rounded up to 64 plus 128 (n_seg + 1) keys, 2 bytes
+ *   each) must stay below 2^31 bytes, since the kernels address it with 32-bit
+ *   offsets: larger calls return H3_ERR_ARG before any launch.
  */
 size_t h3_varlen_attn_workspace_size(int64_t n_buf, int32_t n_heads, int32_t head_dim,
                                      int32_t n_seg, h3_dtype dtype);

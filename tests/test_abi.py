@@ -88,6 +88,16 @@ def test_attention_argument_checks():
     assert call(max_len=9000) == h3.H3_ERR_ARG
     assert call(D=80) == h3.H3_ERR_UNSUPPORTED
     assert call(ws=None) == h3.H3_ERR_ARG
+    # the largest buffer with many segments: a head's transposed V (D rows of
+    # round_up(n_buf, 64) + 128 (n_seg + 1) keys) would pass 2^31 bytes, which
+    # the kernels address with 32-bit offsets; refused before any launch
+    # (only refused calls here: these pointers must never reach a launch)
+    big = 1 << 22
+    limit = (2 ** 31 - 1) // (128 * 2)  # keys per transposed-V row at D = 128
+    first_bad = -(-(limit + 1 - big) // 128) - 1  # smallest n_seg with 128 (n_seg + 1) > limit - n_buf
+    for n_seg in (first_bad, 40000, 65535):
+        st = call(n_buf=big, n_seg=n_seg, max_len=16, ws_bytes=1 << 40)
+        assert st == h3.H3_ERR_ARG and "transposed V" in h3.last_error(), (n_seg, st)
 
 
 def test_modres_and_linear_argument_checks():
