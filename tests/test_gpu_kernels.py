@@ -213,3 +213,64 @@ def test_varlen_attention_edge_segments(lib):
     assert_close(got, ref, "bf16", "attn edges")
     assert np.all(got[0:10] == 0)
     assert np.allclose(got[10], v[10], atol=0)  # one-row segment: o = v exactly (p = 1)
+
+
+def _ramp_case(n, H, D, dtype, slope, noise, seed):
+    """One segment whose scores follow a ramp along the keys: every query is
+    sqrt(D) u (u a unit vector per head) and key j is slope * j * u plus
+    N(0, noise^2), so score(i, j) ~ slope * j.  With slope >= 0.1 the largest
+    score of each 64-key tile exceeds the one before by more than 8 in log2
+    units (a raise of the running max on every tile); a negative slope puts
+    the max in the first tile and lets later tiles underflow."""
+    r = np.random.default_rng(seed)
+    u = r.standard_normal((H, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    q = np.broadcast_to(u[None] * np.sqrt(D), (n, H, D)) + noise * r.standard_normal((n, H, D))
+    k = u[None] * (slope * np.arange(n, dtype=np.float64)[:, None, None]) + noise * r.standard_normal((n, H, D))
+    v = r.standard_normal((n, H, D))
+    q, k, v = (W.as_dtype_values(a.astype(np.float32), dtype) for a in (q, k, v))
+    return W.VarlenCase(n, H, D, np.array([0, n], np.int32), np.array([n], np.int32), q, k, v)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["rising", "falling", "wide"])
+def test_varlen_attention_running_max_paths(lib, dtype, D, kind):
+    """The running max raised on every tile (O and the row sums rescaled each
+    time), never raised while later tiles underflow, and raised at random
+    positions (q and k of standard deviation 1.6: scores of standard deviation
+    ~3.7 log2 units, a raise in ~1% of the rows; much wider scores exceed the
+    bf16 bar through the bf16 rounding of the prescaled Q)."""
+    n, H = 700, 2
+    if kind == "wide":
+        c = W.varlen_case(seed=41, lengths=(n,), n_buf=n, n_heads=H, head_dim=D, dtype=dtype)
+        c = W.VarlenCase(n, H, D, c.cu_slots, c.valid_len, W.as_dtype_values(c.q * 1.6, dtype),
+                         W.as_dtype_values(c.k * 1.6, dtype), c.v)
+    else:
+        c = _ramp_case(n, H, D, dtype, 0.1 if kind == "rising" else -0.1, 0.05, seed=42)
+    got = _attn_gpu(lib, c, dtype)
+    ref = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    assert_close(got, ref, dtype, f"attn running max {kind} D{D}")
+
+
+def test_varlen_attention_many_segments_strided(lib):
+    """Fifteen segments with lengths around the 64-key and 256-query tile edges
+    (0 and 1 included) and NaN/Inf suffix pads; q, k, v read as column windows
+    of one [n_buf, 3 H D] buffer, o written into a window of a wider buffer whose
+    other columns must stay untouched."""
+    lengths = (64, 63, 65, 1, 0, 255, 256, 257, 128, 2, 511, 17, 700, 129, 33)
+    H, D = 3, 128
+    hd = H * D
+    n_buf = sum(lengths) + 300
+    c = W.varlen_case(seed=7, lengths=lengths, n_buf=n_buf, n_heads=H, head_dim=D, dtype="bf16",
+                      pad_fill="nan")
+    qkv = torch.cat([dev(a.reshape(n_buf, hd), "bf16") for a in (c.q, c.k, c.v)], dim=1)
+    o_big = torch.full((n_buf, hd + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o = o_big[:, 32:32 + hd]
+    lib.h3_varlen_attn(qkv[:, :hd], qkv[:, hd:2 * hd], qkv[:, 2 * hd:], o, H, D, dev_i32(c.cu_slots),
+                       dev_i32(c.valid_len), max(lengths))
+    torch.cuda.synchronize()
+    assert torch.isnan(o_big[:, :32].float()).all() and torch.isnan(o_big[:, 32 + hd:].float()).all()
+    got = host(o).reshape(n_buf, H, D)
+    ref = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    assert_close(got, ref, "bf16", "attn many segments strided")
