@@ -10,10 +10,13 @@
 // to the token's position: video tokens use the position on the pair's axis
 // (sections [t | h | w] of widths sec_t, sec_h, D - sec_t - sec_h, each an
 // independent 1-D RoPE), audio tokens their audio index over one section of
-// width D.  The per-position rotation of every pair is computed on the host in
-// double and rounded once to float, in revolutions; a lane then needs one
-// fp32 product and the sine and cosine instructions (v_sin_f32/v_cos_f32,
-// which take revolutions) per pair and token.
+// width D.  The per-position rotation of every pair, in revolutions, is
+// computed on the host in double and kept as a 32-bit fixed-point fraction.
+// A lane multiplies it by the position in 32-bit integers, which wraps
+// exactly to the fractional turn (positions of any size keep the full
+// precision and the sine/cosine inputs stay in [0, 1) turns), converts that
+// to fp32 and applies the sine and cosine instructions (v_sin_f32/v_cos_f32,
+// which take revolutions).
 #pragma once
 
 #include <cmath>
@@ -23,7 +26,9 @@
 namespace h3 {
 
 struct RopeTab {
-  float rev[2][64];  // [0] video (within the pair's section), [1] audio; D <= 128
+  // turns per unit of position, times 2^32 ([0] video, within the pair's
+  // section; [1] audio); D <= 128.  Every rate is below 1/(2 pi) turn.
+  uint32_t rev[2][64];
   int sec_t = 0, sec_h = 0;
 };
 
@@ -33,6 +38,7 @@ inline RopeTab make_rope_tab(int D, int sec_t, int sec_h, float theta) {
   t.sec_h = sec_h;
   const double l2t = std::log2((double)theta);
   const double inv2pi = 1.0 / (2.0 * 3.14159265358979323846);
+  auto fixed = [](double turns) { return (uint32_t)std::llround(std::ldexp(turns, 32)); };
   for (int p = 0; p < D / 2 && p < 64; ++p) {
     int jj, width;
     if (p < sec_t / 2) {
@@ -42,15 +48,15 @@ inline RopeTab make_rope_tab(int D, int sec_t, int sec_h, float theta) {
     } else {
       jj = p - (sec_t + sec_h) / 2; width = D - sec_t - sec_h;
     }
-    t.rev[0][p] = (float)(std::exp2(-2.0 * jj / width * l2t) * inv2pi);
-    t.rev[1][p] = (float)(std::exp2(-2.0 * p / D * l2t) * inv2pi);
+    t.rev[0][p] = fixed(std::exp2(-2.0 * jj / width * l2t) * inv2pi);
+    t.rev[1][p] = fixed(std::exp2(-2.0 * p / D * l2t) * inv2pi);
   }
   return t;
 }
 
 // the 4 pairs 4*lane8 .. 4*lane8+3 of a lane holding dims 8*lane8 .. 8*lane8+7
 struct RopeLane {
-  float rv[4], ra[4];
+  uint32_t rv[4], ra[4];
   int axis[4];
 };
 
@@ -72,7 +78,9 @@ __device__ __forceinline__ void rope_cos_sin(const RopeLane& r, int4 ps, float (
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int pv = r.axis[j] == 0 ? ps.y : (r.axis[j] == 1 ? ps.z : ps.w);
-    const float turns = ps.x == 1 ? (float)ps.y * r.ra[j] : (float)pv * r.rv[j];
+    // the fractional turn, exact modulo 2^32 (negative positions wrap too)
+    const uint32_t ph = ps.x == 1 ? (uint32_t)ps.y * r.ra[j] : (uint32_t)pv * r.rv[j];
+    const float turns = (float)ph * 0x1p-32f;
     s[j] = __builtin_amdgcn_sinf(turns);
     c[j] = __builtin_amdgcn_cosf(turns);
   }

@@ -70,6 +70,39 @@ def test_qk_norm_rope_parity(lib, dtype, shape):
     assert np.array_equal(got[pad], qkv[pad].astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_qk_norm_rope_large_positions(lib, dtype):
+    """Positions far beyond the test workloads' (video t < 3000, h < 500, w < 800;
+    audio index < 20000, i.e. a rotation of up to ~3200 turns of the first pair).
+    The QKV projection's store epilogue runs the same rotation code; its bit
+    equality with this pass is checked in the block tests."""
+    H, D, n = 3, 128, 640
+    sections, theta, eps = W.SHARE_10S.sections, W.SHARE_10S.theta, W.SHARE_10S.eps_qk
+    r = np.random.default_rng(17)
+    pos = np.zeros((n, 4), np.int32)
+    pos[:320, 0] = W.POS_VIDEO
+    pos[:320, 1] = r.integers(0, 3000, 320)
+    pos[:320, 2] = r.integers(0, 500, 320)
+    pos[:320, 3] = r.integers(0, 800, 320)
+    pos[320:, 0] = W.POS_AUDIO
+    pos[320:, 1] = r.integers(0, 20000, 320)
+    pos[-8:, 1] = [0, 1, 1608, 1609, 1610, 9999, 19998, 19999]
+    hd = H * D
+    qkv = W.as_dtype_values(W.normal(12, "qkv_rows_far", (n, 3 * hd)) * 1.7, dtype)
+    gq = W.as_dtype_values(W.normal(12, "gq", (D,), std=0.02, mean=1.0), dtype)
+    gk = W.as_dtype_values(W.normal(12, "gk", (D,), std=0.02, mean=1.0), dtype)
+    t = dev(qkv, dtype)
+    lib.h3_qk_norm_rope(t[:, :hd], t[:, hd:2 * hd], H, D, dev(gq, dtype), dev(gk, dtype), dev_i32(pos),
+                        sections, theta, eps)
+    torch.cuda.synchronize()
+    got = host(t)
+    q = qkv[:, :hd].reshape(n, H, D)
+    k = qkv[:, hd:2 * hd].reshape(n, H, D)
+    rq, rk = O.qk_norm_rope(q, k, pos, gq, gk, sections, theta, eps)
+    assert_close(got[:, :hd], rq.reshape(n, hd), dtype, "q far positions")
+    assert_close(got[:, hd:2 * hd], rk.reshape(n, hd), dtype, "k far positions")
+
+
 # ----------------------------------------------------------- modulate/residual
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
