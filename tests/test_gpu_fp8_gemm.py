@@ -219,7 +219,14 @@ def test_fp8_projections_share_shapes_sampled(lib, n):
 
 
 @pytest.mark.parametrize("rows,dim,per_token,norm_kind", [(333, 256, True, 0), (70, 384, False, 0),
-                                                         (129, 5120, True, 0), (65, 1024, True, 1)])
+                                                         (129, 5120, True, 0), (65, 1024, True, 1),
+                                                         # every other launch tier, whole and partial
+                                                         # (16, 144, 272, 512, 528, 656, 1040 and 2048
+                                                         # chunks of 8)
+                                                         (9, 128, True, 0), (17, 1152, True, 1),
+                                                         (17, 2176, True, 0), (9, 4096, False, 0),
+                                                         (9, 4224, True, 1), (9, 5248, True, 0),
+                                                         (5, 8320, True, 1), (5, 16384, True, 0)])
 def test_modulate_mx_equals_norm_then_quantize(lib, rows, dim, per_token, norm_kind):
     """The fused modulated norm -> MX operand gives the bytes of the two passes it
     replaces: the bf16 modulated norm, then the MX quantizer (each pinned to the

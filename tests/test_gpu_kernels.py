@@ -107,7 +107,12 @@ def test_qk_norm_rope_large_positions(lib, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dim,n,mode", [(256, 480, "per_token"), (5120, 777, "per_token"),
-                                        (5120, 300, "broadcast"), (1024, 65, "rms")])
+                                        (5120, 300, "broadcast"), (1024, 65, "rms"),
+                                        # every launch tier (threads x chunks per thread), whole and
+                                        # partial, and the limits: 1, 129, 257, 512, 641, 1025, 2048 chunks
+                                        (8, 33, "per_token"), (1032, 17, "per_token"), (2056, 17, "rms"),
+                                        (4096, 9, "broadcast"), (5128, 9, "per_token"),
+                                        (8200, 5, "per_token"), (16384, 5, "rms")])
 def test_modulate_residual_parity(lib, dtype, dim, n, mode):
     seed = 3
     x = W.as_dtype_values(W.normal(seed, "x", (n, dim)) * 1.3 + 0.2, dtype)
