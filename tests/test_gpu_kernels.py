@@ -169,6 +169,40 @@ def test_linear_parity(lib, dtype, m, n, k):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m,n,k", [(300, 100, 64), (300, 100, 136), (77, 36, 40), (1, 1, 8),
+                                   (5, 260, 1024), (257, 9, 64)])
+def test_linear_ragged_widths(lib, dtype, m, n, k):
+    """Output widths that are not a multiple of 8 (the epilogues' element-wise tail),
+    K a multiple of 64 (the tiled kernel) or only of 8, single rows; a, w, out and
+    the gate are column windows of wider buffers, and the output's columns past n
+    stay untouched."""
+    seed = 6
+    a = W.as_dtype_values(W.normal(seed, "a", (m, k)), dtype)
+    w = W.as_dtype_values(W.normal(seed, "w", (n, k), std=k ** -0.5), dtype)
+    x = W.as_dtype_values(W.normal(seed, "x", (m, n)), dtype)
+    g = W.as_dtype_values(W.normal(seed, "g", (m, n), std=0.1), dtype)
+    wide = lambda arr, extra: torch.cat([dev(arr, dtype), dev(np.zeros((arr.shape[0], extra), np.float32), dtype)],
+                                        dim=1)
+    n8 = -(-n // 8) * 8 + 8
+    at, wt = wide(a, 8)[:, :k], wide(w, 16)[:, :k]
+    ref = O.linear(a, w)
+    for gated in (False, True):
+        buf = torch.full((m, n8), float("nan"), dtype=at.dtype, device="cuda")
+        out = buf[:, :n]
+        if gated:
+            out.copy_(dev(x, dtype))
+            lib.h3_linear(at, wt, out, gate=wide(g, n8 + 8 - n)[:, :n])
+        else:
+            lib.h3_linear(at, wt, out)
+        torch.cuda.synchronize()
+        want = O.gated_residual(x, g, ref) if gated else ref
+        # (a mean over a handful of elements is one rounding, not an average: the max bar then)
+        few = {"mean_abs": 2e-2} if dtype == "bf16" and m * n < 64 else {}
+        assert_close(host(out), want, dtype, f"linear {m}x{n}x{k} gated={gated}", **few)
+        assert torch.isnan(buf[:, n:].float()).all(), "columns past n were written"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816)])
 def test_swiglu_parity(lib, dtype, n, c, f):
     seed = 9
