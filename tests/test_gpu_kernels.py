@@ -203,7 +203,10 @@ def test_linear_ragged_widths(lib, dtype, m, n, k):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816)])
+@pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816),
+                                   # ffn_dim off the 32-row W1/W3 interleave and the 128-wide
+                                   # output tile; dim off the 64-deep K step
+                                   (65, 136, 712), (33, 64, 200)])
 def test_swiglu_parity(lib, dtype, n, c, f):
     seed = 9
     h = W.as_dtype_values(W.normal(seed, "h", (n, c)), dtype)
