@@ -180,7 +180,7 @@ def test_block_fp8_attention(lib, case):
     assert not np.array_equal(got, exact_path)  # the FP8 path really ran
 
 
-@pytest.mark.parametrize("case", ["world1", "share_r2", "peer_r3", "peer_r0_attn_fp8"])
+@pytest.mark.parametrize("case", ["world1", "share_r2", "peer_r3", "peer_r0_attn_fp8", "world1_c320_f896"])
 def test_block_fp8_projections(lib, case):
     """Block with the four projections on MX-e4m3 operands (and, in one case, the
     FP8 attention too), update-dominant inputs.
@@ -195,9 +195,13 @@ def test_block_fp8_projections(lib, case):
     exact one (10.1% / 8.1% with FP8 attention as well).  Bounds: update
     relative L2 < 12% against the quantized-operand oracle, < 15% against the
     exact oracle -- a wiring mistake (wrong weight, buffer or layout) moves it
-    by O(100%)."""
-    rank = {"world1": None, "share_r2": 2, "peer_r3": 3, "peer_r0_attn_fp8": 0}[case]
+    by O(100%).  world1_c320_f896 takes the other two operand paths: a hidden
+    width off the 128 grid (h1 and h2 written in bf16, then quantized by their
+    own pass) and an inner width on it (g written only as its MX operand)."""
+    rank = {"world1": None, "world1_c320_f896": None, "share_r2": 2, "peer_r3": 3, "peer_r0_attn_fp8": 0}[case]
     wl = W.TINY if rank is None else W.TINY.replace(sp_degree=4, rank=rank)
+    if case == "world1_c320_f896":
+        wl = W.TINY.replace(dim=320, n_heads=5, ffn_dim=896)
     w = W.block_weights(wl, 4, "bf16")
     bi = W.block_inputs(wl, 4, "bf16")
     x, mod = _update_dominant(bi)
