@@ -389,7 +389,7 @@ def share_block_measure(h3, torch, W, timer, wl, seed, reps, warm=1):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the "
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1 (the "
                                    "sequence-parallel sharding across GPUs is a design, not built)"}))
         sys.exit(2)
     import numpy as np
