@@ -734,6 +734,8 @@ h3_status h3_dit_block_forward(const h3_block_config* cfg, const h3_block_weight
   CHECK(C > 0 && C % 8 == 0 && C <= 16384, "dim must be a positive multiple of 8, <= 16384");
   CHECK(H > 0 && F > 0 && F % 8 == 0, "n_heads > 0 and ffn_dim a positive multiple of 8 required");
   TRY(check_head_dim(D));
+  // they are GEMM widths and row strides of the block's buffers
+  CHECK(F <= (1 << 22) && (int64_t)H * D <= (1 << 22), "ffn_dim and n_heads*head_dim must be <= 2^22");
   TRY(check_sections(D, cfg->sec_t, cfg->sec_h, cfg->sec_w));
   CHECK(cfg->norm_kind == 0 || cfg->norm_kind == 1, "norm_kind must be 0 or 1");
   CHECK(cfg->theta > 0.f && cfg->eps_qk >= 0.f && cfg->eps_mod >= 0.f, "theta/eps out of range");

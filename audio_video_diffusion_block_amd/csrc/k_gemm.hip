@@ -204,6 +204,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 constexpr int W4_THREADS = 256;
 constexpr int W4_STAGE = 32768;  // bytes of one 256 x 64 bf16 tile
+constexpr int64_t W4_MAX_LD = (int64_t)1 << 22;  // 255 rows * 2^23 bytes < 2^31
 }  // namespace
 
 template <int EPI>
@@ -423,8 +424,13 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
     const int tiles_m = (int)ceil_div(M, BM);
     const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
+    // the K % 64 kernel keeps a lane's load offsets (up to 255 rows of A or B)
+    // in 32 bits: row strides up to 2^22 elements; beyond that the general
+    // kernel (64-bit addressing) runs, which has no operand maps
+    const bool narrow = lda <= W4_MAX_LD && ldb <= W4_MAX_LD;
+    if (!map.empty() && !narrow) return hipErrorInvalidValue;
 #define H3_G(E)                                                                                 \
-  if (K >= BK && K % BK == 0)                                                                   \
+  if (K >= BK && K % BK == 0 && narrow)                                                         \
     hipLaunchKernelGGL((gemm_bf16_w4_kernel<E>), grid, dim3(W4_THREADS), 0, s, (const bf16_t*)A, \
                        lda, (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,           \
                        (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n, map);       \

@@ -352,10 +352,10 @@ h3_status h3_swiglu_fp8(const h3_mx_operand* h, const h3_mx_operand* w1,
 /* ------------------------------------------------------------ whole block */
 
 typedef struct {
-  int32_t dim;        /* C */
-  int32_t n_heads;    /* H */
+  int32_t dim;        /* C, a multiple of 8, at most 16384 */
+  int32_t n_heads;    /* H; H * D at most 2^22 */
   int32_t head_dim;   /* D, 64 or 128 */
-  int32_t ffn_dim;    /* F */
+  int32_t ffn_dim;    /* F, a multiple of 8, at most 2^22 */
   int32_t sec_t, sec_h, sec_w;  /* RoPE sections of a head row (video) */
   float theta;        /* RoPE base */
   float eps_qk;       /* Q/K RMSNorm epsilon */

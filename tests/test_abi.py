@@ -141,6 +141,11 @@ def test_block_argument_checks():
     io3 = h3.BlockIO(FAKE, 256, FAKE, 6 * 256, FAKE, FAKE, None, 1, 480, 120, 480, 400, 3, 1, FAKE, FAKE, FAKE)
     st = h3._c_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io3), FAKE, need, None)
     assert st == h3.H3_ERR_ARG and "local rows" in h3.last_error()
+    # ffn_dim and n_heads*head_dim become GEMM widths and row strides: at most 2^22
+    for big in (h3.block_config(256, 4, 64, (1 << 22) + 8, (16, 24, 24)),
+                h3.block_config(256, (1 << 22) // 64 + 1, 64, 704, (16, 24, 24))):
+        st = h3._c_block(ctypes.byref(big), ctypes.byref(w), ctypes.byref(io), FAKE, 1 << 40, None)
+        assert st == h3.H3_ERR_ARG and "2^22" in h3.last_error()
 
 
 def test_frames_argument_checks():

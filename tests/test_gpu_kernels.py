@@ -202,6 +202,39 @@ def test_linear_ragged_widths(lib, dtype, m, n, k):
         assert torch.isnan(buf[:, n:].float()).all(), "columns past n were written"
 
 
+@pytest.mark.parametrize("which", ["a", "w"])
+def test_linear_wide_row_strides(lib, which):
+    """Row strides above 2^22 elements: K a multiple of 64, yet the call must not
+    take the tiled kernel, whose per-lane load offsets are 32-bit (it runs on the
+    general kernel); plain and gated residual epilogues."""
+    seed, k, ld = 7, 128, (1 << 22) + 64
+    m, n = (70, 296) if which == "a" else (300, 40)
+    a = W.as_dtype_values(W.normal(seed, "a", (m, k)), "bf16")
+    w = W.as_dtype_values(W.normal(seed, "w", (n, k), std=k ** -0.5), "bf16")
+    x = W.as_dtype_values(W.normal(seed, "x", (m, n)), "bf16")
+    g = W.as_dtype_values(W.normal(seed, "g", (m, n), std=0.1), "bf16")
+
+    def strided(arr):
+        buf = torch.empty((arr.shape[0], ld), dtype=torch.bfloat16, device="cuda")
+        buf[:, :k] = dev(arr, "bf16")
+        return buf[:, :k]
+
+    at = strided(a) if which == "a" else dev(a, "bf16")
+    wt = strided(w) if which == "w" else dev(w, "bf16")
+    assert (at.stride(0) if which == "a" else wt.stride(0)) == ld
+    ref = O.linear(a, w)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    lib.h3_linear(at, wt, out)
+    torch.cuda.synchronize()
+    assert_close(host(out), ref, "bf16", f"linear wide {which} stride")
+    xt = dev(x, "bf16")
+    lib.h3_linear(at, wt, xt, gate=dev(g, "bf16"))
+    torch.cuda.synchronize()
+    assert_close(host(xt), O.gated_residual(x, g, ref), "bf16", f"linear+residual wide {which} stride")
+    del at, wt
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816),
                                    # ffn_dim off the 32-row W1/W3 interleave and the 128-wide
