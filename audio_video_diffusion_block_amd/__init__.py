@@ -187,6 +187,75 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+# Tensor metadata checks.  The C ABI sees pointers and sizes only, so the
+# binding checks that every tensor holds what the call will touch: the call's
+# dtype, at least the rows and columns it addresses (views of larger buffers
+# are fine), contiguous columns.  They raise before any pointer is taken (the
+# device check comes with the pointer).
+_TDT = {H3_BF16: torch.bfloat16, H3_F32: torch.float32}
+
+
+def _mat(t, name: str, rows: int, cols: int, dtype: torch.dtype):
+    """t: 2-D view of at least rows x cols elements of dtype, columns contiguous."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} is {t.dtype}; this call needs {dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; the call addresses ({rows}, {cols})")
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: columns must be contiguous")
+
+
+def _dense(t, name: str, shape: tuple, dtype: torch.dtype):
+    """t: a contiguous tensor of exactly `shape` (passed to the library as a bare pointer)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} is {t.dtype}; this call needs {dtype}")
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}{'' if t.is_contiguous() else ' (strided)'}")
+
+
+def _ints(t, name: str, n: int):
+    """t: contiguous int32 tensor of at least n elements."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous int32 tensor of >= {n} elements, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _gate_rows(gate, ld_gate, m: int) -> int:
+    """Rows a gate view must hold: 1 when broadcast (ld_gate 0), else m."""
+    if ld_gate not in (0, None) and ld_gate != _ld(gate):
+        raise ValueError("ld_gate must be 0 (broadcast) or the gate's own row stride")
+    return 1 if (ld_gate == 0 or (ld_gate is None and gate.shape[0] == 1)) else m
+
+
+def _segments(cu_slots, valid_len) -> int:
+    """n_seg from cu_slots [n_seg + 1]; checks both are int32 device metadata."""
+    if cu_slots is None or cu_slots.dim() != 1 or cu_slots.numel() < 2:
+        raise ValueError("cu_slots must be a 1-D int32 tensor of n_seg + 1 >= 2 entries")
+    n_seg = cu_slots.shape[0] - 1
+    _ints(cu_slots, "cu_slots", n_seg + 1)
+    if valid_len is not None:
+        _ints(valid_len, "valid_len", n_seg)
+    return n_seg
+
+
+def _attn_operands(q, k, v, o, n_heads: int, head_dim: int, dtype=None) -> int:
+    """q, k, v, o: [n_buf, >= n_heads*head_dim] views of one dtype; returns n_buf."""
+    n_buf, width = q.shape[0], n_heads * head_dim
+    dtype = dtype or q.dtype
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _mat(t, name, n_buf, width, dtype)
+    return n_buf
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -203,6 +272,12 @@ def h3_qk_norm_rope(q: torch.Tensor, k: torch.Tensor, n_heads: int, head_dim: in
                     g_q: torch.Tensor, g_k: torch.Tensor, pos: torch.Tensor,
                     sections: Sequence[int], theta: float = 1e4, eps: float = 1e-6, stream=None):
     """In place on q, k (views [n_tok, >= H*D] with row strides)."""
+    n = q.shape[0]
+    _mat(q, "q", n, n_heads * head_dim, q.dtype)
+    _mat(k, "k", n, n_heads * head_dim, q.dtype)
+    _dense(g_q, "g_q", (head_dim,), q.dtype)
+    _dense(g_k, "g_k", (head_dim,), q.dtype)
+    _ints(pos, "pos", 4 * n)
     _check(_c_qk(_ptr(q), _ld(q), _ptr(k), _ld(k), q.shape[0], n_heads, head_dim, _ptr(g_q),
                  _ptr(g_k), _ptr(pos), sections[0], sections[1], sections[2], theta, eps, _dt(q),
                  _stream(stream)))
@@ -215,8 +290,8 @@ def varlen_attn_workspace_size(n_buf: int, n_heads: int, head_dim: int, n_seg: i
 def h3_varlen_attn(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.Tensor,
                    valid_len: Optional[torch.Tensor], max_valid_len: int,
                    softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None, stream=None):
-    n_buf = q.shape[0]
-    n_seg = cu_slots.shape[0] - 1
+    n_buf = _attn_operands(q, k, v, o, n_heads, head_dim)
+    n_seg = _segments(cu_slots, valid_len)
     need = varlen_attn_workspace_size(n_buf, n_heads, head_dim, n_seg, q.dtype)
     if ws is None:
         ws = _bytes_ws(need, q.device)
@@ -231,8 +306,8 @@ def h3_varlen_attn_noalloc(q, k, v, o, n_heads: int, head_dim: int, cu_slots: to
                            softmax_scale: float = 0.0, stream=None):
     """h3_varlen_attn with the library's own fixed scratch (no workspace, no
     allocation; NOALLOC_SCRATCH_BYTES per device, shared by every call)."""
-    n_buf = q.shape[0]
-    n_seg = cu_slots.shape[0] - 1
+    n_buf = _attn_operands(q, k, v, o, n_heads, head_dim)
+    n_seg = _segments(cu_slots, valid_len)
     _check(_c_attn_na(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
                       n_heads, head_dim, _ptr(cu_slots), _ptr(valid_len), n_seg, max_valid_len,
                       softmax_scale, _dt(q), _stream(stream)))
@@ -247,8 +322,8 @@ def h3_varlen_attn_skip(q, k, v, o, n_heads: int, head_dim: int, cu_slots, valid
     """bf16 attention with Skip-Softmax: key blocks of 64 whose scores are all
     more than |skip_log2| (log2 units) below a query group's running max are
     skipped (workspace as h3_varlen_attn)."""
-    n_buf = q.shape[0]
-    n_seg = cu_slots.shape[0] - 1
+    n_buf = _attn_operands(q, k, v, o, n_heads, head_dim)
+    n_seg = _segments(cu_slots, valid_len)
     if ws is None:
         ws = _bytes_ws(varlen_attn_workspace_size(n_buf, n_heads, head_dim, n_seg, q.dtype), q.device)
     _check(_c_attn_skip(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
@@ -265,8 +340,8 @@ def h3_varlen_attn_fp8(q, k, v, o, n_heads: int, head_dim: int, cu_slots: torch.
                        valid_len: Optional[torch.Tensor], max_valid_len: int,
                        softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None, stream=None):
     """h3_varlen_attn with MX-scaled e4m3 operands (bf16 in, bf16 out)."""
-    n_buf = q.shape[0]
-    n_seg = cu_slots.shape[0] - 1
+    n_buf = _attn_operands(q, k, v, o, n_heads, head_dim, torch.bfloat16)
+    n_seg = _segments(cu_slots, valid_len)
     need = varlen_attn_fp8_workspace_size(n_buf, n_heads, head_dim, n_seg)
     if ws is None:
         ws = _bytes_ws(need, q.device)
@@ -280,8 +355,8 @@ def h3_varlen_attn_fp8_skip(q, k, v, o, n_heads: int, head_dim: int, cu_slots, v
                             max_valid_len: int, skip_log2: float, softmax_scale: float = 0.0,
                             ws: Optional[torch.Tensor] = None, stream=None):
     """h3_varlen_attn_fp8 with the Skip-Softmax rule of h3_varlen_attn_skip."""
-    n_buf = q.shape[0]
-    n_seg = cu_slots.shape[0] - 1
+    n_buf = _attn_operands(q, k, v, o, n_heads, head_dim, torch.bfloat16)
+    n_seg = _segments(cu_slots, valid_len)
     if ws is None:
         ws = _bytes_ws(varlen_attn_fp8_workspace_size(n_buf, n_heads, head_dim, n_seg), q.device)
     _check(_c_attn8_skip(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o), n_buf,
@@ -297,6 +372,18 @@ def h3_modulate_residual(x, y=None, gate=None, shift=None, scale=None, h_out=Non
     mod_ref = next((t for t in (gate, shift, scale) if t is not None), None)
     if ld_mod is None:
         ld_mod = 0 if mod_ref is None or mod_ref.shape[0] == 1 else _ld(mod_ref)
+    n, c = x.shape
+    _mat(x, "x", n, c, x.dtype)
+    if y is not None:
+        _mat(y, "y", n, c, x.dtype)
+    if h_out is not None:
+        _mat(h_out, "h_out", n, c, x.dtype)
+    for t, name in ((gate, "gate"), (shift, "shift"), (scale, "scale")):
+        if t is not None:
+            # the three share one row stride in the call
+            _mat(t, name, 1 if ld_mod == 0 else n, c, x.dtype)
+            if ld_mod != 0 and _ld(t) != ld_mod:
+                raise ValueError("gate, shift and scale must share one row stride (ld_mod)")
     _check(_c_modres(_ptr(x), _ld(x), _ptr(y), _ld(y) if y is not None else 0, _ptr(gate),
                      _ptr(shift), _ptr(scale), ld_mod, _ptr(h_out),
                      _ld(h_out) if h_out is not None else 0, x.shape[0], x.shape[1], norm_kind, eps,
@@ -305,8 +392,15 @@ def h3_modulate_residual(x, y=None, gate=None, shift=None, scale=None, h_out=Non
 
 def h3_linear(a, w, out, gate=None, ld_gate: Optional[int] = None, stream=None):
     """out = a @ w^T, or out += gate * (a @ w^T) if gate is given."""
-    if gate is not None and ld_gate is None:
-        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    m, k = a.shape
+    n = w.shape[0]
+    _mat(a, "a", m, k, a.dtype)
+    _mat(w, "w", n, k, a.dtype)
+    _mat(out, "out", m, n, a.dtype)
+    if gate is not None:
+        _mat(gate, "gate", _gate_rows(gate, ld_gate, m), n, a.dtype)
+        if ld_gate is None:
+            ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
     _check(_c_linear(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(out), _ld(out), a.shape[0],
                      w.shape[0], a.shape[1], _ptr(gate), ld_gate or 0, _dt(a), _stream(stream)))
 
@@ -319,8 +413,15 @@ def h3_swiglu(h, w1, w3, w2, out, gate=None, ld_gate: Optional[int] = None,
               ws: Optional[torch.Tensor] = None, stream=None):
     n, c = h.shape
     f = w1.shape[0]
-    if gate is not None and ld_gate is None:
-        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    _mat(h, "h", n, c, h.dtype)
+    _dense(w1, "w1", (f, c), h.dtype)
+    _dense(w3, "w3", (f, c), h.dtype)
+    _dense(w2, "w2", (c, f), h.dtype)
+    _mat(out, "out", n, c, h.dtype)
+    if gate is not None:
+        _mat(gate, "gate", _gate_rows(gate, ld_gate, n), c, h.dtype)
+        if ld_gate is None:
+            ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
     if ws is None:
         ws = _bytes_ws(swiglu_workspace_size(n, f, h.dtype), h.device)
     _check(_c_swiglu(_ptr(h), _ld(h), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out), _ld(out),
@@ -342,6 +443,15 @@ class MxTensor:
         return MxTensor(torch.empty((rows, kp), dtype=torch.uint8, device=device),
                         torch.empty((rows, kp // 32), dtype=torch.uint8, device=device), k)
 
+    def check(self, name: str, rows: int, k: Optional[int] = None):
+        """Holds rows x round_up(k, 128) e4m3 bytes and their scale bytes."""
+        k = self.k if k is None else k
+        if self.k != k:
+            raise ValueError(f"{name} holds k = {self.k} columns; the call needs {k}")
+        kp = -(-k // 128) * 128
+        _mat(self.q, f"{name}.q", rows, kp, torch.uint8)
+        _mat(self.s, f"{name}.s", rows, kp // 32, torch.uint8)
+
     def c(self) -> MxOperand:
         return MxOperand(_ptr(self.q), _ld(self.q), _ptr(self.s), _ld(self.s))
 
@@ -349,8 +459,10 @@ class MxTensor:
 def h3_mx_quantize(x, out: Optional[MxTensor] = None, stream=None) -> MxTensor:
     """bf16 x [rows, cols] -> MxTensor (allocated when out is None)."""
     rows, cols = x.shape
+    _mat(x, "x", rows, cols, torch.bfloat16)
     if out is None:
         out = MxTensor.empty(rows, cols, x.device)
+    out.check("out", rows, cols)
     _check(_c_mxq(_ptr(x), _ld(x), rows, cols, _ptr(out.q), _ld(out.q), _ptr(out.s), _ld(out.s),
                   _dt(x), _stream(stream)))
     return out
@@ -361,10 +473,16 @@ def h3_modulate_mx(x, shift, scale, out: Optional[MxTensor] = None, ld_mod: Opti
     """Modulated norm of bf16 x [n, C] written as an MxTensor (C % 128 == 0); the
     same bytes as h3_mx_quantize of h3_modulate_residual's bf16 h."""
     n, c = x.shape
+    _mat(x, "x", n, c, torch.bfloat16)
     if out is None:
         out = MxTensor.empty(n, c, x.device)
+    out.check("out", n, c)
     if ld_mod is None:
         ld_mod = 0 if shift.shape[0] == 1 else _ld(shift)
+    for t, name in ((shift, "shift"), (scale, "scale")):
+        _mat(t, name, 1 if ld_mod == 0 else n, c, torch.bfloat16)
+        if ld_mod != 0 and _ld(t) != ld_mod:
+            raise ValueError("shift and scale must share one row stride (ld_mod)")
     _check(_c_modmx(_ptr(x), _ld(x), _ptr(shift), _ptr(scale), ld_mod, _ptr(out.q), _ld(out.q),
                     _ptr(out.s), _ld(out.s), n, c, norm_kind, eps, _stream(stream)))
     return out
@@ -373,8 +491,14 @@ def h3_modulate_mx(x, shift, scale, out: Optional[MxTensor] = None, ld_mod: Opti
 def h3_linear_fp8(a: MxTensor, w: MxTensor, out, gate=None, ld_gate: Optional[int] = None,
                   stream=None):
     """out = a @ w^T over MX operands, or out += gate * (a @ w^T)."""
-    if gate is not None and ld_gate is None:
-        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    m, n = a.q.shape[0], w.q.shape[0]
+    a.check("a", m)
+    w.check("w", n, a.k)
+    _mat(out, "out", m, n, torch.bfloat16)
+    if gate is not None:
+        _mat(gate, "gate", _gate_rows(gate, ld_gate, m), n, torch.bfloat16)
+        if ld_gate is None:
+            ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
     ca, cw = a.c(), w.c()
     _check(_c_lin8(ctypes.byref(ca), ctypes.byref(cw), _ptr(out), _ld(out), a.q.shape[0],
                    w.q.shape[0], a.k, _ptr(gate), ld_gate or 0, _stream(stream)))
@@ -387,8 +511,15 @@ def swiglu_fp8_workspace_size(n_tok: int, ffn_dim: int) -> int:
 def h3_swiglu_fp8(h: MxTensor, w1: MxTensor, w3: MxTensor, w2: MxTensor, out, gate=None,
                   ld_gate: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None):
     n, c, f = h.q.shape[0], h.k, w1.q.shape[0]
-    if gate is not None and ld_gate is None:
-        ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
+    h.check("h", n)
+    w1.check("w1", f, c)
+    w3.check("w3", f, c)
+    w2.check("w2", c, f)
+    _mat(out, "out", n, c, torch.bfloat16)
+    if gate is not None:
+        _mat(gate, "gate", _gate_rows(gate, ld_gate, n), c, torch.bfloat16)
+        if ld_gate is None:
+            ld_gate = 0 if gate.shape[0] == 1 else _ld(gate)
     if ws is None:
         ws = _bytes_ws(swiglu_fp8_workspace_size(n, f), h.q.device)
     ops = [x.c() for x in (h, w1, w3, w2)]
@@ -430,10 +561,38 @@ def h3_dit_block_forward(cfg: BlockConfig, weights: dict, x, mod, pos, cu_slots,
     n = x.shape[0]
     share = qkv_attn is not None
     n_buf = n_buf if n_buf is not None else (qkv_attn.shape[0] if share else n)
-    n_seg = cu_slots.shape[0] - 1
+    n_seg = _segments(cu_slots, valid_len)
+    C, H, D, F = cfg.dim, cfg.n_heads, cfg.head_dim, cfg.ffn_dim
+    dt = _TDT.get(cfg.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype code {cfg.dtype}")
+    _mat(x, "x", n, C, dt)
+    if mod.dim() != 3 or mod.shape[1:] != (6, C) or mod.dtype != dt or mod.shape[0] not in (1, n) \
+            or mod.stride(2) != 1 or mod.stride(1) != C:
+        raise ValueError(f"mod must be [n_tok or 1, 6, {C}] of {dt} with contiguous [6, C] rows, "
+                         f"got {mod.dtype} {tuple(mod.shape)}")
+    _ints(pos, "pos", 4 * n)
+    for key, shape in (("w_qkv", (3 * H * D, C)), ("w_o", (C, H * D)), ("w1", (F, C)),
+                       ("w3", (F, C)), ("w2", (C, F)), ("g_q", (D,)), ("g_k", (D,))):
+        if key in ("g_q", "g_k") or not cfg.gemm_fp8 or weights.get(key) is not None:
+            _dense(weights.get(key), key, shape, dt)
+    hc = head_count if head_count is not None else H
+    for t, name, shape in ((qkv_attn, "qkv_attn", (n_buf, 3 * hc * D)), (o_attn, "o_attn", (n_buf, hc * D)),
+                           (o_local, "o_local", (n, H * D))):
+        if t is not None:
+            if t.numel() < shape[0] * shape[1] or not t.is_contiguous() or t.dtype != dt:
+                raise ValueError(f"{name} must be a contiguous {dt} buffer of {shape[0]} x {shape[1]} elements")
+    P = H // hc if hc else 0
+    for t, name, per in ((qkv_send, "qkv_send", 3 * hc * D), (o_recv, "o_recv", hc * D)):
+        if t is not None:
+            if t.numel() < P * n * per or not t.is_contiguous() or t.dtype != dt:
+                raise ValueError(f"{name} must be a contiguous {dt} buffer of {P} x {n} x {per} elements")
     mx = None
     if weights.get("mx") is not None:
         # MX copies of w_qkv, w_o, w1, w3, w2 (MxTensor each) for cfg.gemm_fp8
+        shapes = ((3 * H * D, C), (C, H * D), (F, C), (F, C), (C, F))
+        for name, m, (rows, k) in zip(("w_qkv", "w_o", "w1", "w3", "w2"), weights["mx"], shapes):
+            m.check(f"mx[{name}]", rows, k)
         mx = (MxOperand * 5)(*[m.c() for m in weights["mx"]])
     w = BlockWeights(*(_ptr(weights.get(k)) for k in ("w_qkv", "w_o", "w1", "w3", "w2", "g_q", "g_k")),
                      ctypes.cast(mx, ctypes.POINTER(MxOperand)) if mx is not None else None)
@@ -455,6 +614,13 @@ def timestep_workspace_size(dim: int) -> int:
 
 def h3_timestep_modulation(sigma: float, w_t1, w_t2, table, mod_out, ws=None, stream=None):
     nb, six, c = table.shape
+    if six != 6:
+        raise ValueError("table must be [n_blocks, 6, C]")
+    e = w_t1.shape[1] if w_t1.dim() == 2 else -1
+    _dense(table, "table", (nb, 6, c), table.dtype)
+    _dense(mod_out, "mod_out", (nb, 6, c), table.dtype)
+    _dense(w_t1, "w_t1", (c, e), table.dtype)
+    _dense(w_t2, "w_t2", (6 * c, c), table.dtype)
     if ws is None:
         ws = _bytes_ws(timestep_workspace_size(c), table.device)
     _check(_c_temb(sigma, _ptr(w_t1), _ptr(w_t2), _ptr(table), _ptr(mod_out), nb, c,
@@ -464,6 +630,10 @@ def h3_timestep_modulation(sigma: float, w_t1, w_t2, table, mod_out, ws=None, st
 
 def h3_euler_update(z, u, x_next=None, sigma_from: float = 0.0, sigma_to: float = 0.0,
                     stream=None):
+    """z <- z + (sigma_to - sigma_from) * u over every element; x_next <- z."""
+    for t, name in ((z, "z"), (u, "u"), (x_next, "x_next")):
+        if t is not None and (t.dtype != z.dtype or t.numel() != z.numel() or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous with z's dtype and element count")
     _check(_c_euler(_ptr(z), _ptr(u), _ptr(x_next), z.numel(), sigma_from, sigma_to, _dt(z),
                     _stream(stream)))
 
