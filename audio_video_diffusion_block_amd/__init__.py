@@ -8,7 +8,12 @@ passes raw pointers, strides and sizes to the C ABI declared in
 is no CPU fallback: if the library is missing, importing the binding raises.
 
 Names mirror the C entry points (``h3_qk_norm_rope`` ...); tensors' row
-strides are taken from the tensors themselves.
+strides are taken from the tensors themselves.  Since the C ABI sees only
+pointers and sizes, each entry first checks every tensor against the call:
+its dtype, that it holds at least the rows and columns the call addresses,
+contiguous columns (dense layout for operands passed as bare pointers), int32
+segment and position metadata; a mismatch raises ValueError or TypeError
+before anything reaches the library.
 """
 from __future__ import annotations
 
