@@ -14,7 +14,8 @@
 // waves as 2 (M) x 4 (N), each wave 128x64 from 4x2 v_mfma_f32_32x32x16_bf16
 // tiles, A and B staged through registers into LDS with the 16-byte chunk
 // index XOR-swizzled by the row) and the K % 64 == 0 one (every shape of the
-// block), described where it is defined.
+// block), described where it is defined.  The general kernel addresses in 64
+// bits and also takes K % 64 == 0 calls whose row strides exceed 2^22 elements.
 // The next K tile is fetched into registers while the current one is
 // multiplied.  Work-group ids are remapped so that the tiles one XCD runs at
 // a time form a compact 4 (M) x 8 (N) patch: their A and B panels are then
