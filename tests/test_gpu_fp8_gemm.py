@@ -67,7 +67,7 @@ def test_mx_quantize_matches_oracle(lib, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 200, 256), (513, 520, 768), (64, 96, 704), (1, 8, 128),
-                                   (1000, 264, 5120)])
+                                   (1000, 264, 5120), (77, 40, 224), (5, 24, 32)])
 @pytest.mark.parametrize("residual", [False, True])
 def test_linear_fp8_parity(lib, M, N, K, residual):
     a = _bf16(2, f"a{M}", (M, K))
