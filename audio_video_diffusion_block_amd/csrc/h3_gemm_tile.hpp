@@ -61,6 +61,49 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
               ef[(mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3)) * FS + wn * 128 + ni * 32 + fr] = acc[mi][ni][r];
       }
       __syncthreads();
+      if (m0 + half * 128 + 128 <= M && tn * BN + BN <= N && ldc <= (int64_t)1 << 22 &&
+          ld_gate <= (int64_t)1 << 22) {
+        // every chunk of this pass is inside the output: straight-line code
+        // whose loads of x and gate for G chunks are all in flight before the
+        // first is used.  Buffer accesses: a 32-bit lane offset plus a scalar
+        // offset per chunk (chunk i of a thread is 8 i rows below its first),
+        // so the addresses take no registers.
+        constexpr int G = 4;
+        const int64_t row0 = m0 + half * 128;
+        const auto rc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(C + row0 * ldc + tn * BN), 0, 0x7FFFFFF0, 0x00020000);
+        const auto rg = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(gate + row0 * ld_gate + tn * BN)), 0,
+            0x7FFFFFF0, 0x00020000);
+        const int voc = (tid >> 5) * (int)(ldc * 2) + (tid & 31) * 16;
+        const int vog = (tid >> 5) * (int)(ld_gate * 2) + (tid & 31) * 16;
+        const int stc = 8 * (int)(ldc * 2), stg = 8 * (int)(ld_gate * 2);
+#pragma unroll
+        for (int i0 = 0; i0 < 16; i0 += G) {
+          uint4 xv[G], gv[G];
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            xv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, voc, (i0 + u) * stc, 0));
+            gv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, vog, (i0 + u) * stg, 0));
+          }
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            const int chunk = tid + (i0 + u) * W4_THREADS;
+            const float* src = ef + (chunk >> 5) * FS + (chunk & 31) * 8;
+            const float4 y0 = *reinterpret_cast<const float4*>(src);
+            const float4 y1 = *reinterpret_cast<const float4*>(src + 4);
+            const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            bf16_t* xe = reinterpret_cast<bf16_t*>(&xv[u]);
+            const bf16_t* ge = reinterpret_cast<const bf16_t*>(&gv[u]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xe[e] = f2bf(bf2f(xe[e]) + bf2f(ge[e]) * yv[e]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, xv[u]),
+                                                   rc, voc, (i0 + u) * stc, 0);
+          }
+        }
+        __syncthreads();
+        continue;
+      }
 #pragma unroll 4
       for (int i = 0; i < 16; ++i) {
         const int chunk = tid + i * W4_THREADS;  // 128 rows x 32 chunks of 8
