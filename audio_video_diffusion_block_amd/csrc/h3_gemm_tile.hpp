@@ -164,6 +164,56 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
       Vec8<bf16_t>::load(map.qk_gk + cd, qk_gk);
       qk_rl = rope_lane(map.qk_tab, cd / 8);
     }
+    if (EPI == EPI_STORE && map.qk_pos && !map.peer_hc && m0 + 256 <= M && tn * BN + BN <= N &&
+        tn * BN + BN <= 2 * qk_hd && ldc <= ((int64_t)1 << 22)) {
+      // A tile of q and k head columns wholly inside the output: straight-line
+      // code that requests the positions of G chunks' rows (one 16-byte entry
+      // per row) together instead of waiting on each; buffer accesses, a lane
+      // offset plus a scalar offset per chunk (chunk i of a thread is 8 i rows
+      // below its first).  Same arithmetic as the general path below.
+      constexpr int G = 4;
+      const auto rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<int4*>(map.qk_pos + m0), 0,
+                                                        0x7FFFFFF0, 0x00020000);
+      const auto rc = __builtin_amdgcn_make_buffer_rsrc(C + (int64_t)m0 * ldc + tn * BN, 0,
+                                                        0x7FFFFFF0, 0x00020000);
+      const int r0 = tid / CPR, c8 = (tid % CPR) * 8;
+      const int vop = r0 * 16, voc = r0 * (int)(ldc * 2) + c8 * 2;
+      const int stc = (W4_THREADS / CPR) * (int)(ldc * 2);
+      const float* gain = tn * BN + c8 < qk_hd ? qk_gq : qk_gk;
+#pragma unroll
+      for (int i0 = 0; i0 < 256 * CPR / W4_THREADS; i0 += G) {
+        int4 ps[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+          ps[u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rp, vop, (i0 + u) * (W4_THREADS / CPR) * 16, 0));
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(eb + (r0 + (i0 + u) * (W4_THREADS / CPR)) * ES + c8);
+          uint4 out = raw;
+          if (ps[u].x == 0 || ps[u].x == 1) {
+            float v[8], cs[4], sn[4];
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[2 * e] = __uint_as_float(w[e] << 16);
+              v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+            rope_cos_sin(qk_rl, ps[u], cs, sn);
+            if (map.qk_D == 128) qk_norm_rope_lane<16>(v, gain, cs, sn, map.qk_eps);
+            else qk_norm_rope_lane<8>(v, gain, cs, sn, map.qk_eps);
+            out.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            out.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            out.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+            out.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, out), rc, voc,
+              (i0 + u) * stc, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll 4
     for (int i = 0; i < 256 * CPR / W4_THREADS; ++i) {
       const int chunk = tid + i * W4_THREADS;
