@@ -28,16 +28,19 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in_group / gsize;
 }
 
-// Epilogue of a 256-row output tile held by 4 waves as 2 (M) x 2 (N), each
-// 128 x 128 in 4 x 4 32x32 accumulator blocks (acc[mi][ni], 256 threads).
-// smem must hold 135168 bytes and be free (the caller's K loop is done).
-template <int EPI>
-__device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16_t* C, int64_t ldc,
-                                         const bf16_t* gate, int64_t ld_gate, int M, int N,
-                                         int m0, int tn, int wm, int wn, int fr, int fh,
+// Epilogue of a 64 MI-row output tile (MI = 4: 256 rows; MI = 2: 128) held by
+// 4 waves as 2 (M) x 2 (N), each 32 MI x 128 in MI x 4 32x32 accumulator
+// blocks (acc[mi][ni], 256 threads).  smem must hold 135168 bytes and be free
+// (the caller's K loop is done).
+template <int EPI, int MI = 4>
+__device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[MI][4], bf16_t* C,
+                                         int64_t ldc, const bf16_t* gate, int64_t ld_gate, int M,
+                                         int N, int m0, int tn, int wm, int wn, int fr, int fh,
                                          const GemmMap& map) {
   constexpr int W4_THREADS = 256;
   constexpr int BN = 256;
+  constexpr int RW = 32 * MI;  // rows per wave row
+  constexpr int TR = 2 * RW;   // rows of the tile
   // Through LDS.  A lane holds column lane%32 and rows
   // (r/4)*8 + (lane/32)*4 + r%4 of each 32x32 block; the tile is written to LDS
   // in that layout and read back as row-contiguous 16-byte chunks, so every
@@ -46,19 +49,21 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
   __syncthreads();  // every wave is done with the last tile's fragments
   const int tid = threadIdx.x;
   if constexpr (EPI == EPI_RESIDUAL) {
-    // out = out + gate * acc with acc in fp32: two passes of 128 rows
+    // out = out + gate * acc with acc in fp32: passes of 128 rows (two for a
+    // 256-row tile, each written by one wave row; one for a 128-row tile)
     constexpr int FS = 264;  // floats per LDS row
     float* ef = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wm == half) {
+    for (int half = 0; half < TR / 128; ++half) {
+      if ((wm * RW) / 128 == half) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              ef[(mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3)) * FS + wn * 128 + ni * 32 + fr] = acc[mi][ni][r];
+              ef[(wm * RW - half * 128 + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3)) * FS + wn * 128 +
+                 ni * 32 + fr] = acc[mi][ni][r];
       }
       __syncthreads();
       if (m0 + half * 128 + 128 <= M && tn * BN + BN <= N && ldc <= (int64_t)1 << 22 &&
@@ -136,10 +141,10 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
     constexpr int ES = OC + 8;  // bf16 per LDS row
     bf16_t* eb = reinterpret_cast<bf16_t*>(smem);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 128 + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3);
+        const int rl = wm * RW + mi * 32 + (r >> 2) * 8 + fh * 4 + (r & 3);
         if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
@@ -164,7 +169,7 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
       Vec8<bf16_t>::load(map.qk_gk + cd, qk_gk);
       qk_rl = rope_lane(map.qk_tab, cd / 8);
     }
-    if (EPI == EPI_STORE && map.qk_pos && !map.peer_hc && m0 + 256 <= M && tn * BN + BN <= N &&
+    if (EPI == EPI_STORE && map.qk_pos && !map.peer_hc && m0 + TR <= M && tn * BN + BN <= N &&
         tn * BN + BN <= 2 * qk_hd && ldc <= ((int64_t)1 << 22)) {
       // A tile of q and k head columns wholly inside the output: straight-line
       // code that requests the positions of G chunks' rows (one 16-byte entry
@@ -181,7 +186,7 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
       const int stc = (W4_THREADS / CPR) * (int)(ldc * 2);
       const float* gain = tn * BN + c8 < qk_hd ? qk_gq : qk_gk;
 #pragma unroll
-      for (int i0 = 0; i0 < 256 * CPR / W4_THREADS; i0 += G) {
+      for (int i0 = 0; i0 < TR * CPR / W4_THREADS; i0 += G) {
         int4 ps[G];
 #pragma unroll
         for (int u = 0; u < G; ++u)
@@ -215,7 +220,7 @@ __device__ __forceinline__ void epilogue(char* smem, f32x16_t (&acc)[4][4], bf16
       return;
     }
 #pragma unroll 4
-    for (int i = 0; i < 256 * CPR / W4_THREADS; ++i) {
+    for (int i = 0; i < TR * CPR / W4_THREADS; ++i) {
       const int chunk = tid + i * W4_THREADS;
       const int rl = chunk / CPR, c8 = (chunk % CPR) * 8;
       const int row = m0 + rl, col = (EPI == EPI_SWIGLU ? tn * 128 : tn * BN) + c8;

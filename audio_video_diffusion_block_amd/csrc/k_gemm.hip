@@ -208,19 +208,21 @@ constexpr int W4_STAGE = 32768;  // bytes of one 256 x 64 bf16 tile
 constexpr int64_t W4_MAX_LD = (int64_t)1 << 22;  // 255 rows * 2^23 bytes < 2^31
 }  // namespace
 
-template <int EPI>
-__global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
-    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+// One output tile of 64 MI rows (MI = 4: 256 rows, the usual tile; MI = 2:
+// 128 rows, for the rows of a last partial round) starting at row m0, in
+// tile column tn.  Each wave computes MI x 4 MFMA tiles; the k-order of every
+// output element's MFMAs is the same for both heights.
+template <int EPI, int MI>
+__device__ __forceinline__ void w4_tile(
+    char* smem, const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
     const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
-    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
-    int tiles_n, GemmMap map) {
-  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
-  // (256 x 264 bf16 or 128 x 264 fp32 = 135168 bytes)
-  __shared__ __attribute__((aligned(1024))) char smem[135168];
-
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM;
+    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int m0, int tn,
+    const GemmMap& map) {
+  static_assert(MI == 4 || MI == 2, "tile of 256 or 128 rows");
+  constexpr int RA = 16 * MI;  // A rows each wave loads into LDS
+  constexpr int NAI = 2 * MI;  // ... in NAI instructions of 8 rows
+  constexpr int NI = NAI + 8;  // load instructions per K tile (B: 8 per wave)
+  constexpr int NF = 4 + MI;   // fragments per 16-wide k-slice
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -239,12 +241,17 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
     b_row0 = tn * BN;
   }
   b_base = reinterpret_cast<const char*>(B + (int64_t)b_row0 * ldb);
-  int a_off[8], b_off[8];
+  int a_off[NAI], b_off[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + j * 8 + (lane >> 3);  // LDS row
+  for (int j = 0; j < NAI; ++j) {
+    const int r = wave * RA + j * 8 + (lane >> 3);  // LDS row of the A tile
     const int c = (lane & 7) ^ ((r >> 1) & 7);       // global chunk for this slot
     a_off[j] = (min(m0 + r, M - 1) - m0) * row_a + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + j * 8 + (lane >> 3);  // LDS row of the B tile
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     int br;
     if constexpr (EPI == EPI_SWIGLU) {
       // tile rows 64 w .. 64 w + 31 are W1 rows, the next 32 the W3 rows of
@@ -276,10 +283,10 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
   };
   auto issue_dma = [&](int kt, int stage, int t) {
     const int koff = kt * BK * 2;
-    if (t < 8) {
-      dma16(a_base + a_koff(kt), a_off[t], lds0 + stage * W4_STAGE + wave * 8192 + t * 1024);
+    if (t < NAI) {
+      dma16(a_base + a_koff(kt), a_off[t], lds0 + stage * W4_STAGE + wave * (RA * 128) + t * 1024);
     } else {
-      const int j = t - 8;
+      const int j = t - NAI;
       const char* src = (EPI == EPI_SWIGLU && j >= 4) ? b3_base : b_base;
       dma16(src + koff, b_off[j], lds0 + (2 + stage) * W4_STAGE + wave * 8192 + j * 1024);
     }
@@ -292,13 +299,13 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int cs = ((kk * 2 + fh) ^ swz) * 16;
-    fa[kk] = (wm * 128 + fr) * 128 + cs;
+    fa[kk] = (wm * 32 * MI + fr) * 128 + cs;
     fb[kk] = 2 * W4_STAGE + (wn * 128 + fr) * 128 + cs;
   }
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[MI][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
 
   const int nk = K / BK;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) issue_dma(0, 0, t);
+  for (int t = 0; t < NI; ++t) issue_dma(0, 0, t);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // one K step; MORE: tile kt+1 exists and is fetched during slice 0 (the
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
   auto k_step = [&](int kt, auto more_tag) {
     constexpr bool MORE = decltype(more_tag)::value;
     const int so = (kt & 1) * W4_STAGE;
-    bf16x8_t af[2][4], bfr[2][4];
+    bf16x8_t af[2][MI], bfr[2][4];
     // fragment j of slice kk: A0, B0..B3, A1..A3 (the order the MFMAs use them)
     auto read_frag = [&](int kk, int j) {
       const int c = kk & 1;
@@ -323,23 +330,24 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
       else af[c][j - 4] = *reinterpret_cast<const bf16x8_t*>(smem + fa[kk] + so + (j - 4) * 4096);
     };
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NF; ++j) {
       read_frag(0, j);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slice kk: 16 MFMAs (mi-major).  The 8 fragments of slice kk+1 are
-    // requested after the first 8 of them (so they land before slice kk+1
-    // starts); in slices 0 and 1 every second MFMA is followed by one DMA of
-    // tile kt+1.
+    // slice kk: 4 MI MFMAs (mi-major).  The NF fragments of slice kk+1 are
+    // requested after the first NF of them (so they land before slice kk+1
+    // starts); every second MFMA of the step is followed by one load of tile
+    // kt+1 until its NI loads are issued (slices 0-1 at MI = 4, 0-2 at MI = 2).
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk & 1;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 4 * MI; ++t) {
         const int mi = t >> 2, ni = t & 3;
+        const int slot = kk * 4 * MI + t;
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][mi], bfr[c][ni], acc[mi][ni], 0, 0, 0);
-        if (MORE && kk < 2 && (t & 1)) issue_dma(kt + 1, (kt + 1) & 1, kk * 8 + (t >> 1));
-        if (kk + 1 < 4 && t < 8) read_frag(kk + 1, t);
+        if (MORE && (slot & 1) && (slot >> 1) < NI) issue_dma(kt + 1, (kt + 1) & 1, slot >> 1);
+        if (kk + 1 < 4 && t < NF) read_frag(kk + 1, t);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -353,7 +361,32 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
   k_step(nk - 1, std::false_type{});
 
   // ---- epilogue through LDS (shared with the FP8 kernel)
-  gemm_tile::epilogue<EPI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh, map);
+  gemm_tile::epilogue<EPI, MI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh, map);
+}
+
+// Work-groups [0, n_big) take 256-row tiles of rows [0, tiles_m * 256) in the
+// XCD-aware order; the rest take 128-row tiles of rows [m_split, M) (the rows
+// of what would be a last partial round of 256-row tiles, now packed into
+// half-height tiles: launch_gemm chooses the split).
+template <int EPI>
+__global__ __launch_bounds__(W4_THREADS, 1) void gemm_bf16_w4_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+    const bf16_t* __restrict__ B3, int64_t ldb, bf16_t* C, int64_t ldc,
+    const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int tiles_m,
+    int tiles_n, int n_big, int m_split, GemmMap map) {
+  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
+  // (256 x 264 bf16 or 128 x 264 fp32 = 135168 bytes)
+  __shared__ __attribute__((aligned(1024))) char smem[135168];
+  int tm, tn;
+  if ((int)blockIdx.x < n_big) {
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    w4_tile<EPI, 4>(smem, A, lda, B, B3, ldb, C, ldc, gate, ld_gate, M, N, K, tm * BM, tn, map);
+  } else {
+    const int small_m = (M - m_split + 127) / 128;
+    tile_of(blockIdx.x - n_big, small_m, tiles_n, tm, tn);
+    w4_tile<EPI, 2>(smem, A, lda, B, B3, ldb, C, ldc, gate, ld_gate, M, N, K, m_split + tm * 128, tn,
+                    map);
+  }
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -409,6 +442,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     }
 }
 
+namespace {
+constexpr int W4_CUS = 256;  // compute units that run one tile at a time each
+
+// Split of the K % 64 kernel's rows: the first `big` tile rows as 256-row
+// tiles, the rest as 128-row tiles.  The makespan of in-order dispatch onto
+// W4_CUS units is estimated in units of one 256-row tile, a 128-row tile
+// costing 0.8 of one (it has the same B tile and most of the per-step work;
+// measured: a split predicted from half the cost made the QKV projection 1%
+// slower), for splits near the last full round; a split is taken when it
+// saves at least 1.5%.
+struct W4Split { int big, small_m; };
+W4Split w4_split(int64_t M, int tiles_m, int tiles_n) {
+  constexpr double CS = 0.8;
+  auto makespan = [&](int b, int small_m) {
+    const int64_t nb = (int64_t)b * tiles_n, ns = (int64_t)small_m * tiles_n;
+    const int64_t full = nb / W4_CUS, rem = nb % W4_CUS;
+    if (rem == 0) return (double)full + CS * (double)ceil_div(ns, W4_CUS);
+    // the last 256-row tiles run beside 128-row ones on the other units
+    const int64_t beside = (int64_t)((W4_CUS - rem) / CS);
+    const int64_t left = ns > beside ? ns - beside : 0;
+    return (double)full + 1.0 + CS * (double)ceil_div(left, W4_CUS);
+  };
+  const double t0 = (double)ceil_div((int64_t)tiles_m * tiles_n, W4_CUS);
+  W4Split best{tiles_m, 0};
+  double best_t = t0;
+  for (int b = tiles_m - 1; b >= 0 && b >= tiles_m - 16; --b) {
+    const int small_m = (int)ceil_div(M - (int64_t)b * BM, 128);
+    const double t = makespan(b, small_m);
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = {b, small_m};
+    }
+  }
+  if (best_t > 0.985 * t0) return {tiles_m, 0};
+  return best;
+}
+}  // namespace
+
 hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B,
                        const void* B3, int64_t ldb, void* C, int64_t ldc, const void* gate,
                        int64_t ld_gate, int64_t M, int N, int K, hipStream_t s,
@@ -430,11 +501,18 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
     // kernel (64-bit addressing) runs, which has no operand maps
     const bool narrow = lda <= W4_MAX_LD && ldb <= W4_MAX_LD;
     if (!map.empty() && !narrow) return hipErrorInvalidValue;
+    // 256-row tiles, and 128-row tiles for the rows of a last partial round
+    // (appended to the same grid, so they fill the units the last 256-row
+    // tiles leave idle)
+    const W4Split sp = w4_split(M, tiles_m, tiles_n);
+    const dim3 grid_w4((unsigned)((sp.big + sp.small_m) * tiles_n));
+    const int n_big = sp.big * tiles_n, m_split = sp.big * BM;
 #define H3_G(E)                                                                                 \
   if (K >= BK && K % BK == 0 && narrow)                                                         \
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<E>), grid, dim3(W4_THREADS), 0, s, (const bf16_t*)A, \
-                       lda, (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,           \
-                       (const bf16_t*)gate, ld_gate, (int)M, N, K, tiles_m, tiles_n, map);       \
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<E>), grid_w4, dim3(W4_THREADS), 0, s,               \
+                       (const bf16_t*)A, lda, (const bf16_t*)B, (const bf16_t*)B3, ldb,         \
+                       (bf16_t*)C, ldc, (const bf16_t*)gate, ld_gate, (int)M, N, K, sp.big,     \
+                       tiles_n, n_big, m_split, map);                                            \
   else                                                                                           \
     hipLaunchKernelGGL((gemm_bf16_kernel<E>), grid, dim3(NTHREADS), 0, s, (const bf16_t*)A, lda, \
                        (const bf16_t*)B, (const bf16_t*)B3, ldb, (bf16_t*)C, ldc,                \

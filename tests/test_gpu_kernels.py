@@ -143,10 +143,11 @@ def test_modulate_residual_parity(lib, dtype, dim, n, mode):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("m,n,k", [(480, 768, 256), (1000, 1408, 704), (257, 304, 136),
-                                   (513, 5120, 1024)])
+                                   (513, 5120, 1024), (4000, 5120, 128)])
 def test_linear_parity(lib, dtype, m, n, k):
     """Unit-scale operands (weights std 1/sqrt(k)) so outputs are O(1), like the block's;
-    ragged M, N and K tiles."""
+    ragged M, N and K tiles.  At 4000 x 5120 the 320 tiles of 256 rows would leave a
+    last round of 256 CUs mostly idle: its rows run as 128-row tiles."""
     seed = 5
     a = W.as_dtype_values(W.normal(seed, "a", (m, k)), dtype)
     w = W.as_dtype_values(W.normal(seed, "w", (n, k), std=k ** -0.5), dtype)
@@ -236,7 +237,7 @@ def test_linear_wide_row_strides(lib, which):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816),
+@pytest.mark.parametrize("n,c,f", [(480, 256, 704), (300, 512, 1408), (129, 1024, 2816), (4000, 256, 2816),
                                    # ffn_dim off the 32-row W1/W3 interleave and the 128-wide
                                    # output tile; dim off the 64-deep K step
                                    (65, 136, 712), (33, 64, 200)])
