@@ -13,6 +13,42 @@ constexpr int GROUP_M = 4;
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
 
+// Host side: split of a tiled GEMM's rows into `big` rows of 256-row tiles
+// followed by 128-row tiles for the rest.  The makespan of in-order dispatch
+// onto 256 units (one tile at a time each) is estimated in units of one
+// 256-row tile, a 128-row tile costing 0.8 of one (it has the same B tile and
+// most of the per-step work; measured: a split predicted from half the cost
+// made the QKV projection 1% slower), for splits near the last full round; a
+// split is taken when it saves at least 1.5%.
+struct RowSplit { int big, small_m; };
+inline RowSplit split_rows(int64_t M, int tiles_m, int tiles_n) {
+  constexpr int CUS = 256;
+  constexpr double CS = 0.8;
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  auto makespan = [&](int b, int small_m) {
+    const int64_t nb = (int64_t)b * tiles_n, ns = (int64_t)small_m * tiles_n;
+    const int64_t full = nb / CUS, rem = nb % CUS;
+    if (rem == 0) return (double)full + CS * (double)cdiv(ns, CUS);
+    // the last 256-row tiles run beside 128-row ones on the other units
+    const int64_t beside = (int64_t)((CUS - rem) / CS);
+    const int64_t left = ns > beside ? ns - beside : 0;
+    return (double)full + 1.0 + CS * (double)cdiv(left, CUS);
+  };
+  const double t0 = (double)cdiv((int64_t)tiles_m * tiles_n, CUS);
+  RowSplit best{tiles_m, 0};
+  double best_t = t0;
+  for (int b = tiles_m - 1; b >= 0 && b >= tiles_m - 16; --b) {
+    const int small_m = (int)cdiv(M - (int64_t)b * 256, 128);
+    const double t = makespan(b, small_m);
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = {b, small_m};
+    }
+  }
+  if (best_t > 0.985 * t0) return {tiles_m, 0};
+  return best;
+}
+
 // XCD-aware mapping of a linear work-group id to (tile_m, tile_n).
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;

@@ -442,44 +442,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     }
 }
 
-namespace {
-constexpr int W4_CUS = 256;  // compute units that run one tile at a time each
-
-// Split of the K % 64 kernel's rows: the first `big` tile rows as 256-row
-// tiles, the rest as 128-row tiles.  The makespan of in-order dispatch onto
-// W4_CUS units is estimated in units of one 256-row tile, a 128-row tile
-// costing 0.8 of one (it has the same B tile and most of the per-step work;
-// measured: a split predicted from half the cost made the QKV projection 1%
-// slower), for splits near the last full round; a split is taken when it
-// saves at least 1.5%.
-struct W4Split { int big, small_m; };
-W4Split w4_split(int64_t M, int tiles_m, int tiles_n) {
-  constexpr double CS = 0.8;
-  auto makespan = [&](int b, int small_m) {
-    const int64_t nb = (int64_t)b * tiles_n, ns = (int64_t)small_m * tiles_n;
-    const int64_t full = nb / W4_CUS, rem = nb % W4_CUS;
-    if (rem == 0) return (double)full + CS * (double)ceil_div(ns, W4_CUS);
-    // the last 256-row tiles run beside 128-row ones on the other units
-    const int64_t beside = (int64_t)((W4_CUS - rem) / CS);
-    const int64_t left = ns > beside ? ns - beside : 0;
-    return (double)full + 1.0 + CS * (double)ceil_div(left, W4_CUS);
-  };
-  const double t0 = (double)ceil_div((int64_t)tiles_m * tiles_n, W4_CUS);
-  W4Split best{tiles_m, 0};
-  double best_t = t0;
-  for (int b = tiles_m - 1; b >= 0 && b >= tiles_m - 16; --b) {
-    const int small_m = (int)ceil_div(M - (int64_t)b * BM, 128);
-    const double t = makespan(b, small_m);
-    if (t < best_t - 1e-9) {
-      best_t = t;
-      best = {b, small_m};
-    }
-  }
-  if (best_t > 0.985 * t0) return {tiles_m, 0};
-  return best;
-}
-}  // namespace
-
 hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B,
                        const void* B3, int64_t ldb, void* C, int64_t ldc, const void* gate,
                        int64_t ld_gate, int64_t M, int N, int K, hipStream_t s,
@@ -504,7 +466,7 @@ hipError_t launch_gemm(bool bf16, int epi, const void* A, int64_t lda, const voi
     // 256-row tiles, and 128-row tiles for the rows of a last partial round
     // (appended to the same grid, so they fill the units the last 256-row
     // tiles leave idle)
-    const W4Split sp = w4_split(M, tiles_m, tiles_n);
+    const gemm_tile::RowSplit sp = gemm_tile::split_rows(M, tiles_m, tiles_n);
     const dim3 grid_w4((unsigned)((sp.big + sp.small_m) * tiles_n));
     const int n_big = sp.big * tiles_n, m_split = sp.big * BM;
 #define H3_G(E)                                                                                 \

@@ -92,19 +92,20 @@ constexpr int F8_THREADS = 256;
 constexpr int F8_STAGE = 32768;  // bytes of one 256 x 128 e4m3 tile
 }  // namespace
 
-template <int EPI>
-__global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
-    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ As, int64_t ld_as,
-    const uint8_t* __restrict__ B, const uint8_t* __restrict__ B3, int64_t ldb,
+// One output tile of 64 MI rows (MI = 4: 256; MI = 2: 128, for the rows of a
+// last partial round) starting at row m0, in tile column tn.
+template <int EPI, int MI>
+__device__ __forceinline__ void f8_tile(
+    char* smem, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ As,
+    int64_t ld_as, const uint8_t* __restrict__ B, const uint8_t* __restrict__ B3, int64_t ldb,
     const uint8_t* __restrict__ Bs, const uint8_t* __restrict__ B3s, int64_t ld_bs, bf16_t* C,
-    int64_t ldc, const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K,
-    int tiles_m, int tiles_n, GemmMap map) {
-  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
-  __shared__ __attribute__((aligned(1024))) char smem[135168];
-
-  int tm, tn;
-  gemm_tile::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * F8_BM;
+    int64_t ldc, const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K, int m0,
+    int tn, const GemmMap& map) {
+  static_assert(MI == 4 || MI == 2, "tile of 256 or 128 rows");
+  constexpr int RA = 16 * MI;   // A rows each wave loads into LDS
+  constexpr int NAI = 2 * MI;   // ... in NAI instructions of 8 rows
+  constexpr int NI = NAI + 8;   // load instructions per K tile (B: 8 per wave)
+  constexpr int NR = 2 * (4 + MI);  // 16-byte fragment reads per 64-deep step
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -122,12 +123,17 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
     b_row0 = tn * F8_BN;
   }
   const char* b_base = reinterpret_cast<const char*>(B + (int64_t)b_row0 * ldb);
-  int a_off[8], b_off[8];
+  int a_off[NAI], b_off[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + j * 8 + (lane >> 3);
+  for (int j = 0; j < NAI; ++j) {
+    const int r = wave * RA + j * 8 + (lane >> 3);  // LDS row of the A tile
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     a_off[j] = (min(m0 + r, M - 1) - m0) * row_a + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + j * 8 + (lane >> 3);  // LDS row of the B tile
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     int br;
     if constexpr (EPI == EPI_SWIGLU) {
       br = b_row0 + wave * 32 + ((j * 8 + (lane >> 3)) & 31);
@@ -144,10 +150,10 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
   };
   auto issue_dma = [&](int kt, int stage, int t) {
     const int koff = kt * F8_BK;
-    if (t < 8) {
-      dma16(a_base + koff, a_off[t], lds0 + stage * F8_STAGE + wave * 8192 + t * 1024);
+    if (t < NAI) {
+      dma16(a_base + koff, a_off[t], lds0 + stage * F8_STAGE + wave * (RA * 128) + t * 1024);
     } else {
-      const int j = t - 8;
+      const int j = t - NAI;
       const char* src = (EPI == EPI_SWIGLU && j >= 4) ? b3_base : b_base;
       dma16(src + koff, b_off[j], lds0 + (2 + stage) * F8_STAGE + wave * 8192 + j * 1024);
     }
@@ -163,16 +169,18 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int cs = ((4 * s + 2 * p + fh) ^ swz) * 16;
-      fa[s][p] = (wm * 128 + fr) * 128 + cs;
+      fa[s][p] = (wm * 32 * MI + fr) * 128 + cs;
       fb[s][p] = 2 * F8_STAGE + (wn * 128 + fr) * 128 + cs;
     }
 
   // ---- scale rows of this lane (clamped like the data rows)
-  const uint8_t* sa_row[4];
+  const uint8_t* sa_row[MI];
   const uint8_t* sb_row[4];
 #pragma unroll
+  for (int i = 0; i < MI; ++i)
+    sa_row[i] = As + (int64_t)min(m0 + wm * 32 * MI + i * 32 + fr, M - 1) * ld_as;
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sa_row[i] = As + (int64_t)min(m0 + wm * 128 + i * 32 + fr, M - 1) * ld_as;
     if constexpr (EPI == EPI_SWIGLU) {
       // B tile rows 64 w' .. +31 are W1 features b_row0 + 32 w' + (0..31), the
       // next 32 the W3 rows of the same features; wave column wn reads tile
@@ -183,18 +191,17 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
       sb_row[i] = Bs + (int64_t)min(b_row0 + wn * 128 + i * 32 + fr, N - 1) * ld_bs;
     }
   }
-  uint32_t sa_cur[4], sb_cur[4];
-  auto load_scales = [&](int kt, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+  uint32_t sa_cur[MI], sb_cur[4];
+  auto load_scales = [&](int kt, uint32_t (&sa)[MI], uint32_t (&sb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = *reinterpret_cast<const uint32_t*>(sa_row[i] + kt * 4);
-      sb[i] = *reinterpret_cast<const uint32_t*>(sb_row[i] + kt * 4);
-    }
+    for (int i = 0; i < MI; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(sa_row[i] + kt * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sb[i] = *reinterpret_cast<const uint32_t*>(sb_row[i] + kt * 4);
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[MI][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -203,21 +210,20 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
   const int nk = K / F8_BK;
   load_scales(0, sa_cur, sb_cur);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) issue_dma(0, 0, t);
+  for (int t = 0; t < NI; ++t) issue_dma(0, 0, t);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   auto k_step = [&](int kt, auto more_tag) {
     constexpr bool MORE = decltype(more_tag)::value;
     const int so = (kt & 1) * F8_STAGE;
-    uint32_t sa[4], sb[4], sa_nxt[4], sb_nxt[4];
+    uint32_t sa[MI], sb[4], sa_nxt[MI], sb_nxt[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = sa_cur[i] >> (8 * fh);
-      sb[i] = sb_cur[i] >> (8 * fh);
-    }
+    for (int i = 0; i < MI; ++i) sa[i] = sa_cur[i] >> (8 * fh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sb[i] = sb_cur[i] >> (8 * fh);
     if (MORE) load_scales(kt + 1, sa_nxt, sb_nxt);
-    i32x8_t af[2][4], bf[2][4];
+    i32x8_t af[2][MI], bf[2][4];
     // read j of step s: 0-1 A0, 2-9 B0..B3, 10-15 A1..A3 (two halves each)
     auto read = [&](int s, int j) {
       const int f = j >> 1, p = j & 1;
@@ -233,21 +239,28 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
       dst[4 * p + 3] = (int)u.w;
     };
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NR; ++j) {
       read(0, j);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // 4 MI MFMAs per 64-deep step; during step 0 the NR reads of step 1 follow
+    // its MFMAs (one or two each), and the NI loads of tile kt+1 one per MFMA
+    // slot of the K tile until all are issued
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 4 * MI; ++t) {
         const int mi = t >> 2, ni = t & 3;
+        const int slot = s * 4 * MI + t;
         if (s == 0)
           acc[mi][ni] = mfma_e4m3<0>(af[0][mi], bf[0][ni], acc[mi][ni], sa[mi], sb[ni]);
         else
           acc[mi][ni] = mfma_e4m3<2>(af[1][mi], bf[1][ni], acc[mi][ni], sa[mi], sb[ni]);
-        if (MORE && s == 0) issue_dma(kt + 1, (kt + 1) & 1, t);
-        if (s == 0) read(1, t);
+        if (MORE && slot < NI) issue_dma(kt + 1, (kt + 1) & 1, slot);
+        if (s == 0) {
+          read(1, t);
+          if (t + 4 * MI < NR) read(1, t + 4 * MI);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -255,10 +268,9 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa_cur[i] = sa_nxt[i];
-        sb_cur[i] = sb_nxt[i];
-      }
+      for (int i = 0; i < MI; ++i) sa_cur[i] = sa_nxt[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sb_cur[i] = sb_nxt[i];
     }
   };
   for (int kt = 0; kt + 1 < nk; ++kt) k_step(kt, std::true_type{});
@@ -266,7 +278,31 @@ __global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
   // the epilogue reads every accumulator: let the last scaled MFMAs finish
   scaled_mfma_drain();
 
-  gemm_tile::epilogue<EPI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh, map);
+  gemm_tile::epilogue<EPI, MI>(smem, acc, C, ldc, gate, ld_gate, M, N, m0, tn, wm, wn, fr, fh, map);
+}
+
+// Work-groups [0, n_big) take 256-row tiles of rows [0, tiles_m * 256) in the
+// XCD-aware order, the rest 128-row tiles of rows [m_split, M) (the split is
+// chosen by launch_gemm_mx8).
+template <int EPI>
+__global__ __launch_bounds__(F8_THREADS, 1) void gemm_mx8_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ As, int64_t ld_as,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ B3, int64_t ldb,
+    const uint8_t* __restrict__ Bs, const uint8_t* __restrict__ B3s, int64_t ld_bs, bf16_t* C,
+    int64_t ldc, const bf16_t* __restrict__ gate, int64_t ld_gate, int M, int N, int K,
+    int tiles_m, int tiles_n, int n_big, int m_split, GemmMap map) {
+  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]; the epilogue reuses it
+  __shared__ __attribute__((aligned(1024))) char smem[135168];
+  int tm, tn;
+  if ((int)blockIdx.x < n_big) {
+    gemm_tile::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    f8_tile<EPI, 4>(smem, A, lda, As, ld_as, B, B3, ldb, Bs, B3s, ld_bs, C, ldc, gate, ld_gate, M, N,
+                    K, tm * F8_BM, tn, map);
+  } else {
+    gemm_tile::tile_of(blockIdx.x - n_big, (M - m_split + 127) / 128, tiles_n, tm, tn);
+    f8_tile<EPI, 2>(smem, A, lda, As, ld_as, B, B3, ldb, Bs, B3s, ld_bs, C, ldc, gate, ld_gate, M, N,
+                    K, m_split + tm * 128, tn, map);
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -297,13 +333,18 @@ hipError_t launch_gemm_mx8(int epi, const MxOperand& a, const MxOperand& b, cons
   const int kp = (int)round_up((int64_t)K, 128);
   const int tiles_m = (int)ceil_div(M, F8_BM);
   const int tiles_n = (int)ceil_div(N, epi == EPI_SWIGLU ? 128 : F8_BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  // 256-row tiles, and 128-row tiles for the rows of a last partial round
+  // (appended to the same grid; the split model of the bf16 kernel)
+  const gemm_tile::RowSplit sp = gemm_tile::split_rows(M, tiles_m, tiles_n);
+  const dim3 grid((unsigned)((sp.big + sp.small_m) * tiles_n));
+  const int n_big = sp.big * tiles_n, m_split = sp.big * F8_BM;
 #define H3_G(E)                                                                              \
   hipLaunchKernelGGL((gemm_mx8_kernel<E>), grid, dim3(F8_THREADS), 0, s,                       \
                      (const uint8_t*)a.data, a.ld, (const uint8_t*)a.scale, a.ld_scale,        \
                      (const uint8_t*)b.data, (const uint8_t*)b3.data, b.ld,                    \
                      (const uint8_t*)b.scale, (const uint8_t*)b3.scale, b.ld_scale, (bf16_t*)C, \
-                     ldc, (const bf16_t*)gate, ld_gate, (int)M, N, kp, tiles_m, tiles_n, map)
+                     ldc, (const bf16_t*)gate, ld_gate, (int)M, N, kp, sp.big, tiles_n, n_big,  \
+                     m_split, map)
   if (epi == EPI_SWIGLU) H3_G(EPI_SWIGLU);
   else if (epi == EPI_RESIDUAL) H3_G(EPI_RESIDUAL);
   else H3_G(EPI_STORE);

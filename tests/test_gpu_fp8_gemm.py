@@ -67,7 +67,7 @@ def test_mx_quantize_matches_oracle(lib, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 200, 256), (513, 520, 768), (64, 96, 704), (1, 8, 128),
-                                   (1000, 264, 5120), (77, 40, 224), (5, 24, 32)])
+                                   (1000, 264, 5120), (77, 40, 224), (5, 24, 32), (4000, 5120, 128)])
 @pytest.mark.parametrize("residual", [False, True])
 def test_linear_fp8_parity(lib, M, N, K, residual):
     a = _bf16(2, f"a{M}", (M, K))
@@ -118,7 +118,7 @@ def _swiglu_ref(h, w1, w3, w2, rows=None):
     return O.linear_fp8_operands(g, w2)
 
 
-@pytest.mark.parametrize("n,C,F", [(480, 256, 704), (300, 512, 1408)])
+@pytest.mark.parametrize("n,C,F", [(480, 256, 704), (300, 512, 1408), (4000, 256, 2816)])
 def test_swiglu_fp8_parity(lib, n, C, F):
     h = _bf16(5, "h", (n, C))
     w1 = _bf16(5, "w1", (F, C), std=C ** -0.5)
