@@ -307,6 +307,45 @@ def test_varlen_attention_8k_three_segments(lib):
         assert np.array_equal(alone, got[lo:lo + n])
 
 
+def _attn_noalloc(lib, c):
+    q, k, v = (dev(t.reshape(c.n_buf, -1), "bf16") for t in (c.q, c.k, c.v))
+    o = torch.full_like(q, float("nan"))
+    lib.h3_varlen_attn_noalloc(q, k, v, o, c.n_heads, c.head_dim, dev_i32(c.cu_slots),
+                               dev_i32(c.valid_len), int(c.valid_len.max()))
+    torch.cuda.synchronize()
+    return host(o).reshape(c.n_buf, c.n_heads, c.head_dim)
+
+
+@pytest.mark.parametrize("kind", ["packed", "rising", "falling"])
+def test_varlen_attention_long_segments(lib, kind):
+    """Segments of 1025 (one key past 16 tiles), 4096 and 6400 keys beside 17-
+    and 1024-key ones, with NaN/Inf pads; and one 6400-key segment whose running
+    max rises on every tile or sits in the first tile (later weights underflow).
+    Parity with the oracle, pad rows 0, reruns byte-identical, the no-allocation
+    entry point byte-identical, a segment alone equal to its packed run."""
+    if kind == "packed":
+        c = W.varlen_case(seed=11, lengths=(1025, 17, 4096, 1024, 6400), n_buf=13000, n_heads=2,
+                          head_dim=128, dtype="bf16", pad_fill="nan")
+    else:
+        c = _ramp_case(6400, 1, 64, "bf16", 0.1 if kind == "rising" else -0.1, 0.05, seed=43)
+    print(f"long segments case {kind}: n_buf={c.n_buf} H={c.n_heads} D={c.head_dim}", flush=True)
+    got = _attn_gpu(lib, c, "bf16")
+    ref = O.varlen_attention(c.q, c.k, c.v, c.cu_slots, c.valid_len)
+    assert_close(got, ref, "bf16", f"attn long segments {kind}")
+    assert np.array_equal(_attn_noalloc(lib, c), got)
+    valid = np.zeros(c.n_buf, bool)
+    for s in range(len(c.valid_len)):
+        valid[c.cu_slots[s]:c.cu_slots[s] + c.valid_len[s]] = True
+    assert np.all(got[~valid] == 0)
+    assert np.array_equal(_attn_gpu(lib, c, "bf16"), got)
+    if kind == "packed":
+        s = 2
+        lo, n = int(c.cu_slots[s]), int(c.valid_len[s])
+        one = W.VarlenCase(n, 2, 128, np.array([0, n], np.int32), np.array([n], np.int32),
+                           c.q[lo:lo + n], c.k[lo:lo + n], c.v[lo:lo + n])
+        assert np.array_equal(_attn_gpu(lib, one, "bf16"), got[lo:lo + n])
+
+
 def test_varlen_attention_edge_segments(lib):
     """Zero-length and one-row segments, a segment ending exactly at the buffer end,
     a grid bound above the true maximum."""
