@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--config", default="share10s")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", choices=["", "attn", "attn_fp8", "copy", "block"])
+    ap.add_argument("--only", default="", choices=["", "attn", "attn_fp8", "attn8k", "copy", "block"])
     ap.add_argument("--op-reps", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other configs (8k varlen attention, 5 s block, 15 s loop)")
@@ -404,6 +404,12 @@ def main():
     bf = torch.bfloat16
     stream = torch.cuda.current_stream()
     timer = EventTimer(stream)
+
+    if args.only == "attn8k":
+        # the 8k varlen attention case alone (for its kernel trace)
+        r = varlen8k_measure(h3, torch, W, timer, reps=max(args.steps, 1))
+        print(json.dumps({"kernel": "attn8k", **{k: r[k] for k in ("ms", "TFLOP/s", "fp8_ms")}}))
+        return
 
     if args.only == "copy":
         # plain copy of known size: calibration of the HBM byte counters
